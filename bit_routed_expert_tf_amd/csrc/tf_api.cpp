@@ -1,0 +1,338 @@
+// C ABI of the q4 MoE-layer hot path (declared in include/tf.h).
+//
+// This file validates arguments, lays out workspaces and enqueues the
+// kernels; it never allocates device memory on the hot path and never
+// throws across the ABI.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "tf_internal.h"
+#include "tf_slot.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+tf_status fail(tf_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+tf_status hip_fail(hipError_t e, const char *what) {
+    return fail(TF_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+inline size_t up256(size_t n) { return (n + 255) & ~size_t(255); }
+inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool dim_ok(int32_t v) { return v >= 64 && v <= 4096 && v % 64 == 0; }
+
+tf_status check_qmat(const tf_qmat *m, int bits, int n, int k, const char *what) {
+    if (!m || !m->q || !m->scale || !m->bias) return fail(TF_E_ARG, "%s: NULL matrix", what);
+    if (m->bits != bits || m->group != 64) return fail(TF_E_SHAPE, "%s: need %d-bit, group 64", what, bits);
+    if (m->n != n || m->k != k) return fail(TF_E_SHAPE, "%s: shape [%d][%d], want [%d][%d]", what, m->n, m->k, n, k);
+    if (!aligned(m->q, 16)) return fail(TF_E_ALIGN, "%s: q not 16-byte aligned", what);
+    if (!aligned(m->scale, 2) || !aligned(m->bias, 2)) return fail(TF_E_ALIGN, "%s: scale/bias misaligned", what);
+    return TF_OK;
+}
+
+tf_status check_layer(const tf_moe_layer *L) {
+    if (!L) return fail(TF_E_ARG, "layer is NULL");
+    if (!dim_ok(L->d_model) || !dim_ok(L->d_ff) || !dim_ok(L->d_ff_shared))
+        return fail(TF_E_SHAPE, "d_model/d_ff/d_ff_shared must be multiples of 64 in [64, 4096]");
+    if (L->top_k < 1 || L->top_k > 16) return fail(TF_E_SHAPE, "top_k must be in [1, 16]");
+    if (L->n_experts < L->top_k || L->n_experts > 1024)
+        return fail(TF_E_SHAPE, "n_experts must be in [top_k, 1024]");
+    if (L->act != TF_GELU_ERF && L->act != TF_GELU_TANH) return fail(TF_E_ARG, "unknown activation");
+    tf_status st = check_qmat(&L->router, 8, L->n_experts, L->d_model, "router");
+    if (st) return st;
+    if (!L->shared_blob || !L->pool) return fail(TF_E_ARG, "shared_blob/pool is NULL");
+    if (!aligned(L->shared_blob, 256) || !aligned(L->pool, 256))
+        return fail(TF_E_ALIGN, "blobs must be 256-byte aligned");
+    if (L->blob_stride < tf_expert_blob_bytes(L->d_model, L->d_ff) || L->blob_stride % 256)
+        return fail(TF_E_ALIGN, "blob_stride must be >= the blob size and a multiple of 256");
+    return TF_OK;
+}
+
+// Decode workspace layout (offsets in bytes).
+struct WsLayout {
+    size_t hdr, logits, items, pairs, hs, ys, hr, total;
+};
+
+WsLayout decode_layout(int d, int f, int fs, int E, int k, int T) {
+    WsLayout w{};
+    size_t o = 0;
+    w.hdr = o; o += 256;
+    w.logits = o; o += up256((size_t)8 * T * E);
+    w.items = o; o += up256((size_t)16 * T * k);
+    w.pairs = o; o += up256((size_t)4 * T * k);
+    w.hs = o; o += up256((size_t)4 * T * fs);
+    w.ys = o; o += up256((size_t)4 * T * d);
+    w.hr = o; o += up256((size_t)4 * T * k * f);
+    w.total = o;
+    return w;
+}
+
+template <typename T> T *at(void *ws, size_t off) {
+    return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
+}
+
+void fill_common(DecodeArgs &a, const tf_moe_layer *L, int T) {
+    memset(&a, 0, sizeof a);
+    a.d = L->d_model; a.f = L->d_ff; a.fs = L->d_ff_shared;
+    a.E = L->n_experts; a.k = L->top_k; a.T = T; a.act = L->act;
+    a.rq = L->router.q; a.rs = L->router.scale; a.rb = L->router.bias;
+    a.shared_blob = L->shared_blob; a.pool = L->pool; a.stride = L->blob_stride;
+    a.tbx = T < MAX_TB ? T : MAX_TB;
+    a.tbh = T < 2 ? T : 2;
+    a.kcb = KC_BATCH;
+    a.topk = 1;
+}
+
+int kc_batch(int f) {
+    const int per = (4 * f + 4 * (f >> 5) + 15) & ~15;
+    int b = 65536 / per;
+    return b < 1 ? 1 : (b > KC_BATCH ? KC_BATCH : b);
+}
+
+}  // namespace
+
+void tf_set_error(const char *msg) { g_err = msg; }
+
+extern "C" {
+
+const char *tf_last_error(void) { return g_err.c_str(); }
+const char *tf_version(void) { return "tf-moe-mi355x 0.1 (gfx950)"; }
+
+size_t tf_expert_blob_bytes(int32_t d_model, int32_t d_ff) {
+    if (d_model <= 0 || d_ff <= 0 || d_model % 64 || d_ff % 64) return 0;
+    const size_t mq = (size_t)d_model * d_ff / 2, ms = (size_t)d_model * d_ff / 64 * 2;
+    return 3 * (mq + 2 * ms);
+}
+
+tf_status tf_expert_view(const uint8_t *blob, int32_t d_model, int32_t d_ff, tf_qmat *gate,
+                         tf_qmat *up, tf_qmat *down) {
+    if (!blob || !gate || !up || !down) return fail(TF_E_ARG, "NULL argument");
+    if (d_model <= 0 || d_ff <= 0 || d_model % 64 || d_ff % 64)
+        return fail(TF_E_SHAPE, "d_model and d_ff must be positive multiples of 64");
+    const size_t mq = (size_t)d_model * d_ff / 2, ms = (size_t)d_model * d_ff / 64 * 2;
+    const uint8_t *p = blob;
+    tf_qmat *m[3] = {gate, up, down};
+    for (int i = 0; i < 3; ++i) {
+        m[i]->q = p; p += mq;
+        m[i]->scale = reinterpret_cast<const uint16_t *>(p); p += ms;
+        m[i]->bias = reinterpret_cast<const uint16_t *>(p); p += ms;
+        m[i]->n = i < 2 ? d_ff : d_model;
+        m[i]->k = i < 2 ? d_model : d_ff;
+        m[i]->bits = 4;
+        m[i]->group = 64;
+    }
+    return TF_OK;
+}
+
+tf_status tf_workspace_zero(void *ws, size_t ws_bytes, hipStream_t s) {
+    if (!ws || ws_bytes % 4) return fail(TF_E_ARG, "workspace NULL or size not a multiple of 4");
+    hipError_t e = tf_launch_zero(ws, ws_bytes, s);
+    return e == hipSuccess ? TF_OK : hip_fail(e, "zero kernel");
+}
+
+tf_status tf_workspace_flags(void *ws, int32_t *flags_host, hipStream_t s) {
+    if (!ws || !flags_host) return fail(TF_E_ARG, "NULL argument");
+    uint32_t v = 0;
+    hipError_t e = hipMemcpyAsync(&v, ws, 4, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "reading workspace flags");
+    *flags_host = (int32_t)v;
+    e = tf_launch_zero(ws, 4, s);
+    return e == hipSuccess ? TF_OK : hip_fail(e, "clearing workspace flags");
+}
+
+static size_t router_hdr_bytes(int32_t T) { return up256((size_t)4 * (T + 3)); }
+
+size_t tf_router_workspace_bytes(int32_t n_experts, int32_t T) {
+    if (n_experts <= 0 || T <= 0) return 256;
+    return router_hdr_bytes(T) + up256((size_t)8 * T * n_experts);
+}
+
+tf_status tf_router_topk(const tf_qmat *router, const uint16_t *x, int32_t T, int32_t top_k,
+                         const int32_t *forced_ids, int32_t *ids, float *weights, double *logits,
+                         void *ws, size_t ws_bytes, hipStream_t s) {
+    if (T < 0 || T > 4096) return fail(TF_E_ARG, "T must be in [0, 4096]");
+    if (T == 0) return TF_OK;
+    if (!router) return fail(TF_E_ARG, "router is NULL");
+    const int E = router->n, d = router->k;
+    if (!dim_ok(d)) return fail(TF_E_SHAPE, "d_model must be a multiple of 64 in [64, 4096]");
+    if (top_k < 1 || top_k > 16 || E < top_k || E > 1024)
+        return fail(TF_E_SHAPE, "need 1 <= top_k <= 16 and top_k <= n_experts <= 1024");
+    tf_status st = check_qmat(router, 8, E, d, "router");
+    if (st) return st;
+    if (!x || !ids || !weights || !ws) return fail(TF_E_ARG, "NULL x/ids/weights/ws");
+    if (!aligned(x, 16) || !aligned(ws, 256)) return fail(TF_E_ALIGN, "x 16-byte / ws 256-byte alignment");
+    if (ws_bytes < tf_router_workspace_bytes(E, T)) return fail(TF_E_NOMEM, "workspace too small");
+    DecodeArgs a;
+    memset(&a, 0, sizeof a);
+    a.d = d; a.E = E; a.k = top_k; a.T = T;
+    a.x = x; a.rq = router->q; a.rs = router->scale; a.rb = router->bias;
+    a.forced = forced_ids; a.ids = ids; a.weights = weights;
+    a.hdr = at<uint32_t>(ws, 0);
+    a.logits = logits ? logits : at<double>(ws, router_hdr_bytes(T));
+    a.a_router_waves = E * T;
+    a.topk = 1;
+    a.do_group = 0;
+    a.f = a.fs = 64;
+    hipError_t e = tf_launch_decode(a, STAGE_A, s);
+    return e == hipSuccess ? TF_OK : hip_fail(e, "router launch");
+}
+
+size_t tf_gemv_workspace_bytes(int32_t d_ff, int32_t P) {
+    if (d_ff <= 0 || P <= 0) return 256;
+    return 256 + up256((size_t)4 * P * d_ff);
+}
+
+tf_status tf_expert_q4_gemv(const uint8_t *pool, size_t blob_stride, int32_t d_model,
+                            int32_t d_ff, const int32_t *slot, const int32_t *token,
+                            const float *coef, int32_t P, const uint16_t *x, int32_t T,
+                            float *y32, tf_act act, void *ws, size_t ws_bytes, hipStream_t s) {
+    if (P < 0 || P > 256 || T < 0 || T > 256) return fail(TF_E_ARG, "P and T must be in [0, 256]");
+    if (P == 0 || T == 0) return TF_OK;
+    if (!dim_ok(d_model) || !dim_ok(d_ff)) return fail(TF_E_SHAPE, "d_model/d_ff: multiples of 64 in [64, 4096]");
+    if (!pool || !slot || !x || !y32 || !ws) return fail(TF_E_ARG, "NULL pool/slot/x/y32/ws");
+    if (!token && T != P) return fail(TF_E_ARG, "token == NULL requires T == P");
+    if (act != TF_GELU_ERF && act != TF_GELU_TANH) return fail(TF_E_ARG, "unknown activation");
+    if (!aligned(pool, 256) || blob_stride % 256 || blob_stride < tf_expert_blob_bytes(d_model, d_ff))
+        return fail(TF_E_ALIGN, "pool 256-byte aligned, stride a multiple of 256 >= blob size");
+    if (!aligned(x, 16) || !aligned(y32, 16) || !aligned(ws, 256)) return fail(TF_E_ALIGN, "x/y32/ws alignment");
+    if (ws_bytes < tf_gemv_workspace_bytes(d_ff, P)) return fail(TF_E_NOMEM, "workspace too small");
+    DecodeArgs a;
+    memset(&a, 0, sizeof a);
+    a.d = d_model; a.f = d_ff; a.fs = 64; a.E = 1; a.k = 1; a.T = T; a.act = act;
+    a.x = x; a.pool = pool; a.stride = blob_stride;
+    a.y32 = y32;
+    a.hdr = at<uint32_t>(ws, 0);
+    a.h_r = at<float>(ws, 256);
+    a.gemv_slot = slot; a.gemv_token = token; a.gemv_coef = coef; a.P = P;
+    a.tbx = 1; a.tbh = 1; a.kcb = kc_batch(d_ff);
+    a.b_routed_waves = P * (d_ff / 8);
+    hipError_t e = tf_launch_decode(a, STAGE_B | STAGE_C, s);
+    return e == hipSuccess ? TF_OK : hip_fail(e, "gemv launch");
+}
+
+size_t tf_moe_workspace_bytes(const tf_moe_layer *L, int32_t T) {
+    if (!L || T <= 0) return 0;
+    return decode_layout(L->d_model, L->d_ff, L->d_ff_shared, L->n_experts, L->top_k, T).total;
+}
+
+tf_status tf_moe_layer_fwd(const tf_moe_layer *L, const uint16_t *x, int32_t T,
+                           const int32_t *forced_ids, uint16_t *y, float *y32, int32_t *ids,
+                           float *weights, tf_slot_cache *cache, int32_t layer,
+                           hipStream_t compute, hipStream_t copy, void *ws, size_t ws_bytes) {
+    if (T < 0 || T > MAX_DECODE_T) return fail(TF_E_ARG, "T must be in [0, %d]", MAX_DECODE_T);
+    if (T == 0) return TF_OK;
+    tf_status st = check_layer(L);
+    if (st) return st;
+    if (!x || !y || !ids || !weights || !ws) return fail(TF_E_ARG, "NULL x/y/ids/weights/ws");
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, 256) || (y32 && !aligned(y32, 16)))
+        return fail(TF_E_ALIGN, "x/y/y32 16-byte, ws 256-byte alignment");
+    const WsLayout w = decode_layout(L->d_model, L->d_ff, L->d_ff_shared, L->n_experts, L->top_k, T);
+    if (ws_bytes < w.total) return fail(TF_E_NOMEM, "workspace too small (%zu < %zu)", ws_bytes, w.total);
+    if (cache) {
+        if (T != 1) return fail(TF_E_ARG, "the slot-cache path takes one token per call");
+        st = tf_slot_check_layer(cache, L, layer);
+        if (st) return st;
+    }
+
+    DecodeArgs a;
+    fill_common(a, L, T);
+    a.kcb = kc_batch(L->d_ff);
+    a.x = x; a.forced = forced_ids; a.ids = ids; a.weights = weights; a.y = y; a.y32 = y32;
+    a.hdr = at<uint32_t>(ws, w.hdr);
+    a.logits = at<double>(ws, w.logits);
+    a.items = at<int32_t>(ws, w.items);
+    a.pairs = at<int32_t>(ws, w.pairs);
+    a.h_s = at<float>(ws, w.hs);
+    a.y_s = at<float>(ws, w.ys);
+    a.h_r = at<float>(ws, w.hr);
+    a.do_group = 1;
+    const int n_router = a.E * T;
+    const int n_shared_a = (a.fs / 8) * ((T + a.tbx - 1) / a.tbx);
+    const int n_routed_b = (a.f / 8) * (T * a.k);
+    const int n_shared_b = (a.d / 8) * ((T + a.tbh - 1) / a.tbh);
+    hipError_t e;
+
+    if (!cache) {
+        a.a_router_waves = n_router;
+        a.a_shared_waves = n_shared_a;
+        a.b_routed_waves = n_routed_b;
+        a.b_shared_waves = n_shared_b;
+        e = tf_launch_decode(a, STAGE_A | STAGE_B | STAGE_C, compute);
+        return e == hipSuccess ? TF_OK : hip_fail(e, "decode launch");
+    }
+
+    // Slot-cache path: router -> lookup -> shared branch (runs while the host
+    // waits for the miss list and the copies run) -> routed experts.
+    a.a_router_waves = n_router;
+    e = tf_launch_decode(a, STAGE_A, compute);
+    if (e != hipSuccess) return hip_fail(e, "router launch");
+    st = tf_slot_cache_lookup(cache, layer, ids, L->top_k, nullptr, compute);
+    if (st) return st;
+    a.a_router_waves = 0;
+    a.a_shared_waves = n_shared_a;
+    a.b_routed_waves = 0;
+    a.b_shared_waves = n_shared_b;
+    e = tf_launch_decode(a, STAGE_A | STAGE_B, compute);
+    if (e != hipSuccess) return hip_fail(e, "shared-branch launch");
+    hipEvent_t filled = tf_slot_fill_event(cache);
+    int32_t nmiss = 0;
+    st = tf_slot_cache_fill(cache, layer, copy, filled, &nmiss);
+    if (st) return st;
+    e = hipStreamWaitEvent(compute, filled, 0);
+    if (e != hipSuccess) return hip_fail(e, "waiting for the fill");
+    a.slot_map = tf_slot_map(cache, layer);
+    a.pool = tf_slot_pool(cache, layer);
+    a.b_routed_waves = n_routed_b;
+    a.b_shared_waves = 0;
+    e = tf_launch_decode(a, STAGE_B | STAGE_C, compute);
+    return e == hipSuccess ? TF_OK : hip_fail(e, "routed launch");
+}
+
+}  // extern "C"
+
+extern "C" {
+
+size_t tf_prefill_workspace_bytes(const tf_moe_layer *L, int32_t T) {
+    if (!L || T <= 0) return 0;
+    const int Tb = T < MAX_DECODE_T ? T : MAX_DECODE_T;
+    return decode_layout(L->d_model, L->d_ff, L->d_ff_shared, L->n_experts, L->top_k, Tb).total;
+}
+
+// Chunked prefill: the chunk runs as decode steps of up to 16 tokens each;
+// inside a step the (token, rank) pairs are grouped by expert.
+tf_status tf_moe_prefill_chunk(const tf_moe_layer *L, const uint16_t *x, int32_t T, uint16_t *y,
+                               float *y32, int32_t *ids, float *weights, hipStream_t s, void *ws,
+                               size_t ws_bytes) {
+    if (T < 0 || T > 128) return fail(TF_E_ARG, "T must be in [0, 128]");
+    if (T == 0) return TF_OK;
+    tf_status st = check_layer(L);
+    if (st) return st;
+    if (!x || !y || !ids || !weights || !ws) return fail(TF_E_ARG, "NULL x/y/ids/weights/ws");
+    if (ws_bytes < tf_prefill_workspace_bytes(L, T)) return fail(TF_E_NOMEM, "workspace too small");
+    const size_t d = L->d_model, k = L->top_k;
+    for (int t0 = 0; t0 < T; t0 += MAX_DECODE_T) {
+        const int n = T - t0 < MAX_DECODE_T ? T - t0 : MAX_DECODE_T;
+        st = tf_moe_layer_fwd(L, x + t0 * d, n, nullptr, y + t0 * d, y32 ? y32 + t0 * d : nullptr,
+                              ids + t0 * k, weights + t0 * k, nullptr, 0, s, s, ws, ws_bytes);
+        if (st) return st;
+    }
+    return TF_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,214 @@
+/*
+ * tf.h -- C ABI of the MI355X (gfx950) q4 MoE-layer hot path.
+ *
+ * One token of a Mixture-of-Experts decoder layer, as the TurboFieldfare
+ * pages describe it (blog.hypho.cn review, "它省的不是模型大小": 128 routed
+ * experts per layer, the router picks 8 per token, a dense shared expert
+ * always runs; shilu.ai README translation, "概览" table: MLX affine 4-bit
+ * weights with group 64 for the shared and routed experts, 8-bit router;
+ * "推理引擎的工作原理": router first, then a 16-slot LFU expert cache per
+ * layer whose misses are filled while the shared branch runs, then the shared
+ * and routed outputs are combined; prefill in chunks of at most 128 tokens).
+ *
+ * Layer definition (per token t):
+ *     l   = W_router x_t                      (8-bit affine, fp64 accumulate)
+ *     ids = top-k of l by (logit desc, id asc), in rank order
+ *     p   = softmax(l[ids])                   (over the k selected logits)
+ *     y_t = shared(x_t) + sum_r p_r * expert_{ids_r}(x_t)
+ *     expert(x) = W_down (gelu(W_gate x) (.) (W_up x)),  gelu(z) = z Phi(z)
+ *
+ * Conventions
+ * -----------
+ * - Pointers are DEVICE pointers unless the name ends in _host.  Every call
+ *   is stream-ordered and asynchronous unless marked [SYNC].
+ * - Quantised matrix W[n][k] (affine, group 64): q uint8 [n][k*bits/8]; for
+ *   4 bits element j of a row is byte j/2, low nibble when j is even; scale
+ *   and bias are IEEE fp16 [n][k/64] (passed as uint16_t); w = scale*q + bias.
+ * - Expert blob: gate.q | gate.scale | gate.bias | up.q | up.scale | up.bias |
+ *   down.q | down.scale | down.bias, back to back; gate/up are
+ *   [d_ff][d_model], down is [d_model][d_ff].  3,345,408 bytes at
+ *   d_model=2816, d_ff=704.  Blobs must start 256-byte aligned.
+ * - x and y are fp16 (uint16_t) row-major [T][d_model]; y is rounded to
+ *   nearest even from an fp32 accumulation (|y| >= 65520 becomes +-inf).
+ * - Shapes: d_model, d_ff, d_ff_shared multiples of 64 and <= 4096;
+ *   1 <= top_k <= 16; top_k <= n_experts <= 1024.
+ * - Argument errors are detected before anything is enqueued and leave no
+ *   side effects.  HIP failures return TF_E_HIP.  Asynchronous faults surface
+ *   on a later call.  Nothing aborts; no C++ exception crosses the ABI.
+ * - T = 0 returns TF_OK with no launches.
+ * - Handles and workspaces are not thread-safe: one host thread and one
+ *   stream sequence per workspace.  Calls never allocate device memory,
+ *   except tf_slot_cache_create.
+ * - Workspaces must be zero-filled before first use (tf_workspace_zero);
+ *   the library leaves its counters at zero after every completed call.
+ */
+#ifndef TF_H
+#define TF_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TF_OK = 0,
+    TF_E_ARG = 1,     /* NULL pointer, bad count or flag                          */
+    TF_E_SHAPE = 2,   /* dimension not supported (see Conventions)                */
+    TF_E_ALIGN = 3,   /* pointer misaligned (q rows 16 B, blobs 256 B, ws 256 B)  */
+    TF_E_HIP = 4,     /* a HIP runtime call failed; see tf_last_error()           */
+    TF_E_NOMEM = 5,   /* workspace too small / allocation failed                  */
+    TF_E_STATE = 6    /* handle used out of order (e.g. fill before lookup)       */
+} tf_status;
+
+typedef enum { TF_GELU_ERF = 0, TF_GELU_TANH = 1 } tf_act;
+
+/* Device-side error flags a call can record in its workspace (read with
+ * tf_workspace_flags).  Kernels clamp the offending ids so that every memory
+ * access stays in bounds; outputs of the affected token are unspecified. */
+enum { TF_FLAG_ID_RANGE = 1, TF_FLAG_ID_REPEAT = 2 };
+
+/* Thread-local text of the last non-OK return. */
+const char *tf_last_error(void);
+const char *tf_version(void);
+
+/* Non-owning view of an affine-quantised W[n][k]. */
+typedef struct {
+    const uint8_t *q;
+    const uint16_t *scale;
+    const uint16_t *bias;
+    int32_t n, k, bits, group;   /* bits 4 or 8, group 64, k % 64 == 0 */
+} tf_qmat;
+
+/* Size in bytes of one expert blob (host-only arithmetic). */
+size_t tf_expert_blob_bytes(int32_t d_model, int32_t d_ff);
+
+/* Split a blob into its three matrix views (host-only pointer arithmetic). */
+tf_status tf_expert_view(const uint8_t *blob, int32_t d_model, int32_t d_ff,
+                         tf_qmat *gate, tf_qmat *up, tf_qmat *down);
+
+/* Zero a workspace with a fill kernel (safe to record in a HIP graph). */
+tf_status tf_workspace_zero(void *ws, size_t ws_bytes, hipStream_t s);
+
+/* [SYNC] Read and clear the device-side error flags of a workspace. */
+tf_status tf_workspace_flags(void *ws, int32_t *flags_host, hipStream_t s);
+
+/* ---------------------------------------------------------------- router */
+/* Router matvec (8-bit affine, products exact in fp32, sums in fp64), then
+ * top-k by (logit desc, id asc) and softmax over the k selected logits.
+ *   router     : 8-bit tf_qmat [n_experts][d_model]
+ *   x          : fp16 [T][d_model]
+ *   forced_ids : NULL, or int32 [T][top_k] ids to use instead of the top-k
+ *                (p is then the softmax of the router logits at those ids,
+ *                in the given order); ids must be distinct and in range --
+ *                violations set TF_FLAG_ID_* in the workspace.
+ *   ids        : int32 [T][top_k] out, rank order
+ *   weights    : fp32 [T][top_k] out
+ *   logits     : NULL or fp64 [T][n_experts] out
+ *   ws         : workspace of tf_router_workspace_bytes(n_experts, T) bytes */
+size_t tf_router_workspace_bytes(int32_t n_experts, int32_t T);
+tf_status tf_router_topk(const tf_qmat *router, const uint16_t *x, int32_t T,
+                         int32_t top_k, const int32_t *forced_ids, int32_t *ids,
+                         float *weights, double *logits, void *ws, size_t ws_bytes,
+                         hipStream_t s);
+
+/* ------------------------------------------------------ expert q4 GEMV */
+/* For each pair p (0 <= p < P):
+ *     y32[token[p]] += coef[p] * expert(pool + slot[p]*blob_stride)(x[token[p]])
+ * token[] must be non-decreasing (pairs grouped by token); each token's pairs
+ * are summed in pair order, so the result is deterministic.  token == NULL
+ * means token[p] = p (then T must equal P); coef == NULL means 1.
+ * y32 is fp32 [T][d_model], read and written.  P <= 256, T <= 256.
+ * ws: tf_gemv_workspace_bytes(d_ff, P) bytes. */
+size_t tf_gemv_workspace_bytes(int32_t d_ff, int32_t P);
+tf_status tf_expert_q4_gemv(const uint8_t *pool, size_t blob_stride, int32_t d_model,
+                            int32_t d_ff, const int32_t *slot, const int32_t *token,
+                            const float *coef, int32_t P, const uint16_t *x, int32_t T,
+                            float *y32, tf_act act, void *ws, size_t ws_bytes,
+                            hipStream_t s);
+
+/* ------------------------------------------------------------ MoE layer */
+typedef struct tf_slot_cache tf_slot_cache;   /* opaque, see below */
+
+typedef struct {
+    tf_qmat router;              /* 8-bit [n_experts][d_model]               */
+    const uint8_t *shared_blob;  /* shared expert, blob layout, d_ff_shared  */
+    const uint8_t *pool;         /* n_experts blobs (all-resident) or the
+                                    slot pool of a tf_slot_cache             */
+    size_t blob_stride;          /* bytes between consecutive blobs          */
+    int32_t d_model, d_ff, d_ff_shared, n_experts, top_k;
+    int32_t act;                 /* tf_act                                   */
+} tf_moe_layer;
+
+/* Workspace for tf_moe_layer_fwd with up to T tokens. */
+size_t tf_moe_workspace_bytes(const tf_moe_layer *L, int32_t T);
+
+/* Decode step: T (1..16) independent tokens through one layer.
+ *   x [T][d_model] fp16 in; y [T][d_model] fp16 out; y32 NULL or fp32 out.
+ *   ids/weights [T][top_k] out (rank order).
+ *   forced_ids NULL or [T][top_k] (see tf_router_topk).
+ *   cache NULL: blob of expert e is pool + e*blob_stride (all resident).
+ *   cache non-NULL (T must be 1): the layer's routed experts are looked up in
+ *     the slot cache; misses are copied from the pinned host pool on `copy`
+ *     while the shared branch runs on `compute`.  [SYNC: waits once for the
+ *     lookup result to issue the copies.]
+ * Kernels: router+shared gate/up | (lookup) | routed gate/up + shared down |
+ * routed down + combine. */
+tf_status tf_moe_layer_fwd(const tf_moe_layer *L, const uint16_t *x, int32_t T,
+                           const int32_t *forced_ids, uint16_t *y, float *y32,
+                           int32_t *ids, float *weights, tf_slot_cache *cache,
+                           int32_t layer, hipStream_t compute, hipStream_t copy,
+                           void *ws, size_t ws_bytes);
+
+/* Prefill: one chunk of T (1..128) tokens through one layer, all experts
+ * resident.  Tokens are grouped by expert so that each expert's weights are
+ * read once per chunk.  Same outputs as T single-token calls (ids bitwise,
+ * y within fp32 rounding). */
+size_t tf_prefill_workspace_bytes(const tf_moe_layer *L, int32_t T);
+tf_status tf_moe_prefill_chunk(const tf_moe_layer *L, const uint16_t *x, int32_t T,
+                               uint16_t *y, float *y32, int32_t *ids, float *weights,
+                               hipStream_t s, void *ws, size_t ws_bytes);
+
+/* ------------------------------------------------------------ slot cache */
+/* Per-layer LFU expert cache in HBM (shilu.ai README translation,
+ * "推理引擎的工作原理"; sh.edu-sjtu.cn, "三件事").  Policy: a slot's count is
+ * 1 on fill and +1 per hit; the token's own ids are pinned; misses are
+ * handled in rank order; the victim is the lowest empty slot, else the
+ * unpinned slot with the smallest (count, last-use token, slot index); every
+ * layer starts empty.
+ *   slot_pool        : device [n_layers][n_slots][blob_stride] bytes (caller-owned)
+ *   host_pool_pinned : pinned host [n_layers][n_experts][blob_stride] bytes
+ *                      (caller-owned, hipHostMalloc)
+ *   trace_cap        : tokens per layer recorded in the hit/slot trace (0 = off)
+ * The handle owns only its small device tables, a mapped pinned miss list,
+ * the trace and two events. */
+tf_status tf_slot_cache_create(int32_t n_layers, int32_t n_experts, int32_t n_slots,
+                               int32_t top_k, size_t blob_stride, uint8_t *slot_pool,
+                               const uint8_t *host_pool_pinned, int64_t trace_cap,
+                               tf_slot_cache **out);
+void tf_slot_cache_destroy(tf_slot_cache *c);
+/* Look up one token's ids (device int32 [n]) in `layer`'s cache: updates
+ * the LFU state, writes slots (device int32 [n]) and the miss list, records
+ * the lookup event.  Asynchronous. */
+tf_status tf_slot_cache_lookup(tf_slot_cache *c, int32_t layer, const int32_t *ids,
+                               int32_t n, int32_t *slots, hipStream_t compute);
+/* [SYNC] Wait for the last lookup of `layer`, copy each missed blob from the
+ * host pool into its slot on `copy` (one hipMemcpyAsync per miss), then
+ * record `filled` (may be NULL) on `copy`.  *n_miss_host receives the count. */
+tf_status tf_slot_cache_fill(tf_slot_cache *c, int32_t layer, hipStream_t copy,
+                             hipEvent_t filled, int32_t *n_miss_host);
+/* [SYNC] Copy `layer`'s trace (hit flag, slot per token and rank) to the host.
+ * hit_host / slot_host hold cap entries; *len receives the entries written. */
+tf_status tf_slot_cache_trace(tf_slot_cache *c, int32_t layer, int8_t *hit_host,
+                              int16_t *slot_host, int64_t cap, int64_t *len);
+/* [SYNC] Empty every layer and clear the traces. */
+tf_status tf_slot_cache_reset(tf_slot_cache *c);
+/* Total bytes copied host->device by fills since create/reset. */
+int64_t tf_slot_cache_bytes_filled(const tf_slot_cache *c);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TF_H */

@@ -19,6 +19,7 @@ STATUS_NAMES = {0: "TF_OK", 1: "TF_E_ARG", 2: "TF_E_SHAPE", 3: "TF_E_ALIGN", 4: 
                 5: "TF_E_NOMEM", 6: "TF_E_STATE"}
 TF_GELU_ERF, TF_GELU_TANH = 0, 1
 TF_FLAG_ID_RANGE, TF_FLAG_ID_REPEAT = 1, 2
+TF_KERNEL_ROUTER_SHARED_GATEUP, TF_KERNEL_ROUTED_GATEUP_SHARED_DOWN, TF_KERNEL_DOWN_COMBINE = 1, 2, 4
 
 c_void_p, c_int32, c_int64, c_size_t = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 
@@ -65,6 +66,7 @@ _SIGS = {
     "tf_moe_prefill_chunk": (c_int32, [ctypes.POINTER(tf_moe_layer), c_void_p, c_int32,
                                        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                        c_void_p, c_size_t]),
+    "tf_profile_kernel": (c_int32, [c_int32, c_void_p, c_void_p]),
     "tf_slot_cache_create": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_size_t, c_void_p,
                                        c_void_p, c_int64, ctypes.POINTER(c_void_p)]),
     "tf_slot_cache_destroy": (None, [c_void_p]),

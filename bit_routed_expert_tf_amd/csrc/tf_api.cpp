@@ -75,9 +75,9 @@ WsLayout decode_layout(int d, int f, int fs, int E, int k, int T) {
     w.logits = o; o += up256((size_t)8 * T * E);
     w.items = o; o += up256((size_t)16 * T * k);
     w.pairs = o; o += up256((size_t)4 * T * k);
-    w.hs = o; o += up256((size_t)4 * T * fs);
+    w.hs = o; o += up256(h_row_bytes(fs) * T);
     w.ys = o; o += up256((size_t)4 * T * d);
-    w.hr = o; o += up256((size_t)4 * T * k * f);
+    w.hr = o; o += up256(h_row_bytes(f) * T * k);
     w.total = o;
     return w;
 }
@@ -93,15 +93,8 @@ void fill_common(DecodeArgs &a, const tf_moe_layer *L, int T) {
     a.rq = L->router.q; a.rs = L->router.scale; a.rb = L->router.bias;
     a.shared_blob = L->shared_blob; a.pool = L->pool; a.stride = L->blob_stride;
     a.tbx = T < MAX_TB ? T : MAX_TB;
-    a.tbh = T < 2 ? T : 2;
-    a.kcb = KC_BATCH;
+    a.tbh = 1;
     a.topk = 1;
-}
-
-int kc_batch(int f) {
-    const int per = (4 * f + 4 * (f >> 5) + 15) & ~15;
-    int b = 65536 / per;
-    return b < 1 ? 1 : (b > KC_BATCH ? KC_BATCH : b);
 }
 
 }  // namespace
@@ -185,7 +178,7 @@ tf_status tf_router_topk(const tf_qmat *router, const uint16_t *x, int32_t T, in
     a.forced = forced_ids; a.ids = ids; a.weights = weights;
     a.hdr = at<uint32_t>(ws, 0);
     a.logits = logits ? logits : at<double>(ws, router_hdr_bytes(T));
-    a.a_router_waves = E * T;
+    a.a_router_blocks = ((E + 3) / 4) * T;
     a.topk = 1;
     a.do_group = 0;
     a.f = a.fs = 64;
@@ -195,7 +188,7 @@ tf_status tf_router_topk(const tf_qmat *router, const uint16_t *x, int32_t T, in
 
 size_t tf_gemv_workspace_bytes(int32_t d_ff, int32_t P) {
     if (d_ff <= 0 || P <= 0) return 256;
-    return 256 + up256((size_t)4 * P * d_ff);
+    return 256 + up256(h_row_bytes(d_ff) * P);
 }
 
 tf_status tf_expert_q4_gemv(const uint8_t *pool, size_t blob_stride, int32_t d_model,
@@ -214,16 +207,23 @@ tf_status tf_expert_q4_gemv(const uint8_t *pool, size_t blob_stride, int32_t d_m
     if (ws_bytes < tf_gemv_workspace_bytes(d_ff, P)) return fail(TF_E_NOMEM, "workspace too small");
     DecodeArgs a;
     memset(&a, 0, sizeof a);
-    a.d = d_model; a.f = d_ff; a.fs = 64; a.E = 1; a.k = 1; a.T = T; a.act = act;
+    a.d = d_model; a.f = d_ff; a.fs = d_model; a.E = 1; a.k = 1; a.T = T; a.act = act;
     a.x = x; a.pool = pool; a.stride = blob_stride;
     a.y32 = y32;
     a.hdr = at<uint32_t>(ws, 0);
-    a.h_r = at<float>(ws, 256);
+    a.h_r = at<uint4>(ws, 256);
     a.gemv_slot = slot; a.gemv_token = token; a.gemv_coef = coef; a.P = P;
-    a.tbx = 1; a.tbh = 1; a.kcb = kc_batch(d_ff);
-    a.b_routed_waves = P * (d_ff / 8);
+    a.tbx = 1; a.tbh = 1;
+    a.b_routed_blocks = P * (d_ff / (2 * (64 / tf_decode_lpr(a))));
     hipError_t e = tf_launch_decode(a, STAGE_B | STAGE_C, s);
     return e == hipSuccess ? TF_OK : hip_fail(e, "gemv launch");
+}
+
+tf_status tf_profile_kernel(int32_t kernel, hipEvent_t start, hipEvent_t stop) {
+    if (kernel != 0 && ((!start || !stop) || (kernel & (kernel - 1)) || kernel > 4096))
+        return fail(TF_E_ARG, "one kernel id and two events, or kernel 0 to disarm");
+    tf_arm_profile(kernel, start, stop);
+    return TF_OK;
 }
 
 size_t tf_moe_workspace_bytes(const tf_moe_layer *L, int32_t T) {
@@ -252,42 +252,44 @@ tf_status tf_moe_layer_fwd(const tf_moe_layer *L, const uint16_t *x, int32_t T,
 
     DecodeArgs a;
     fill_common(a, L, T);
-    a.kcb = kc_batch(L->d_ff);
     a.x = x; a.forced = forced_ids; a.ids = ids; a.weights = weights; a.y = y; a.y32 = y32;
     a.hdr = at<uint32_t>(ws, w.hdr);
     a.logits = at<double>(ws, w.logits);
     a.items = at<int32_t>(ws, w.items);
     a.pairs = at<int32_t>(ws, w.pairs);
-    a.h_s = at<float>(ws, w.hs);
+    a.h_s = at<uint4>(ws, w.hs);
     a.y_s = at<float>(ws, w.ys);
-    a.h_r = at<float>(ws, w.hr);
+    a.h_r = at<uint4>(ws, w.hr);
     a.do_group = 1;
-    const int n_router = a.E * T;
-    const int n_shared_a = (a.fs / 8) * ((T + a.tbx - 1) / a.tbx);
-    const int n_routed_b = (a.f / 8) * (T * a.k);
-    const int n_shared_b = (a.d / 8) * ((T + a.tbh - 1) / a.tbh);
+    const int max_items = T == 1 ? a.k : T * a.k;
+    const int n_router = ((a.E + 3) / 4) * T;
+    // rows per workgroup: gate/up 2*RPW, shared down 4*RPW (RPW = 64 / lanes per row)
+    const int rpw = 64 / tf_decode_lpr(a);
+    const int n_shared_a = (a.fs / (2 * rpw)) * ((T + a.tbx - 1) / a.tbx);
+    const int n_routed_b = (a.f / (2 * rpw)) * max_items;
+    const int n_shared_b = (a.d / (4 * rpw)) * ((T + a.tbh - 1) / a.tbh);
     hipError_t e;
 
     if (!cache) {
-        a.a_router_waves = n_router;
-        a.a_shared_waves = n_shared_a;
-        a.b_routed_waves = n_routed_b;
-        a.b_shared_waves = n_shared_b;
+        a.a_router_blocks = n_router;
+        a.a_shared_blocks = n_shared_a;
+        a.b_routed_blocks = n_routed_b;
+        a.b_shared_blocks = n_shared_b;
         e = tf_launch_decode(a, STAGE_A | STAGE_B | STAGE_C, compute);
         return e == hipSuccess ? TF_OK : hip_fail(e, "decode launch");
     }
 
     // Slot-cache path: router -> lookup -> shared branch (runs while the host
     // waits for the miss list and the copies run) -> routed experts.
-    a.a_router_waves = n_router;
+    a.a_router_blocks = n_router;
     e = tf_launch_decode(a, STAGE_A, compute);
     if (e != hipSuccess) return hip_fail(e, "router launch");
     st = tf_slot_cache_lookup(cache, layer, ids, L->top_k, nullptr, compute);
     if (st) return st;
-    a.a_router_waves = 0;
-    a.a_shared_waves = n_shared_a;
-    a.b_routed_waves = 0;
-    a.b_shared_waves = n_shared_b;
+    a.a_router_blocks = 0;
+    a.a_shared_blocks = n_shared_a;
+    a.b_routed_blocks = 0;
+    a.b_shared_blocks = n_shared_b;
     e = tf_launch_decode(a, STAGE_A | STAGE_B, compute);
     if (e != hipSuccess) return hip_fail(e, "shared-branch launch");
     hipEvent_t filled = tf_slot_fill_event(cache);
@@ -298,8 +300,8 @@ tf_status tf_moe_layer_fwd(const tf_moe_layer *L, const uint16_t *x, int32_t T,
     if (e != hipSuccess) return hip_fail(e, "waiting for the fill");
     a.slot_map = tf_slot_map(cache, layer);
     a.pool = tf_slot_pool(cache, layer);
-    a.b_routed_waves = n_routed_b;
-    a.b_shared_waves = 0;
+    a.b_routed_blocks = n_routed_b;
+    a.b_shared_blocks = 0;
     e = tf_launch_decode(a, STAGE_B | STAGE_C, compute);
     return e == hipSuccess ? TF_OK : hip_fail(e, "routed launch");
 }

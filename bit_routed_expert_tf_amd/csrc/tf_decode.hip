@@ -1,28 +1,38 @@
 // Decode-path kernels of the q4 MoE layer for gfx950 (CDNA4).
 //
 // One decode step of T <= 16 tokens through one layer is three launches on
-// one stream (the shilu.ai README translation, "推理引擎的工作原理", orders
-// the work as router -> shared branch (overlapping the expert fetch) ->
-// routed experts -> combine):
+// one stream, in the order the shilu.ai README translation
+// ("推理引擎的工作原理") gives for the runtime: router, shared branch,
+// routed experts, combine.
 //
-//   A  router rows (8-bit, fp64 sums) + shared gate/up (q4)     depends on x
-//      the last router wave of a token does its top-k + softmax; the last
-//      token's top-k wave groups the (token, rank) pairs by expert
-//   B  routed gate/up (q4, per expert group) + shared down (q4)  needs ids, h_s
-//   C  routed down (q4) summed over the token's ranks + y_s -> fp16 y
+//   A  router rows (8-bit, fp64 sums) + shared gate/up (q4) -> h_s
+//      The last router workgroup of a token runs its top-k and softmax; for
+//      T > 1 the last token's top-k workgroup groups (token, rank) pairs by
+//      expert so that each expert's weights are read once per step.
+//   B  routed gate/up (q4, per expert item) -> h_r = p * gelu(g) * u
+//      + shared down (q4) -> y_s
+//   C  routed down (q4) over the token's pairs + y_s -> fp16 y
 //
-// Every wave owns an 8-row tile: lanes 8r..8r+7 share row r, lane s reads the
-// 16-byte chunks s, s+8, s+16, ... of the row, so each load instruction moves
-// eight full 128-byte lines.  Activations are staged per wave in LDS in the
-// (e0,e4)(e1,e5)(e2,e6)(e3,e7) pairing that the nibble unpack produces (see
-// tf_device.h).  No float atomics: every sum has a fixed order, so repeated
-// runs are bitwise identical.
+// Workgroups are 256 threads (4 waves).  Every wave owns an 8-row tile of one
+// matrix: lanes 8r..8r+7 share row r and lane s reads the 16-byte chunks s,
+// s+8, s+16, ... of that row, so each load instruction moves eight whole
+// 128-byte lines.  Each workgroup issues its activation loads first and its
+// weight loads second, all before any of them is consumed; loads are
+// straight-line (out-of-range chunks read a clamped address and get a zero
+// scale), so the compiler's in-order load counter lets chunk j be consumed
+// as soon as it lands.  Activations live in LDS in the (e0,e4)(e1,e5)(e2,e6)
+// (e3,e7) pairing the nibble unpack produces; the hidden activations h are
+// written by their producers already split into hi/lo fp16 pairs, so the
+// consumers only copy them.  No float atomics: every sum has a fixed order,
+// so repeated runs are bitwise identical.
 #include "tf_device.h"
 #include "tf_internal.h"
 
 using namespace tfk;
 
 namespace {
+
+constexpr int WG = 256;
 
 struct Mat {
     const uint8_t *q;
@@ -47,406 +57,671 @@ __device__ __forceinline__ void blob_mats(const uint8_t *blob, int d, int f, Mat
 }
 
 __device__ __forceinline__ const uint8_t *expert_blob(const DecodeArgs &a, int e) {
-    const int slot = a.slot_map ? (int)a.slot_map[e] : e;
+    const int slot = a.slot_map ? a.slot_map[e] : e;
     return a.pool + (size_t)slot * a.stride;
 }
 
-// Loads of one 8-row tile of a q4 matrix with K columns: chunk j of lane
-// (r, s) is half-group hg = 8j + s of row row0 + r.  Scale and bias of the
-// chunk's group are packed into one word (scale low, bias high).
-template <int J>
-__device__ __forceinline__ void load_tile(const Mat &m, int row0, int K, int lane, uint4 (&q)[J],
-                                          uint32_t (&sb)[J]) {
-    const int H = K >> 5, G = K >> 6;
-    const int r = lane >> 3, s = lane & 7;
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// ----------------------------------------------------------- weight tile
+// RPW = 64/LPR rows of one q4 matrix with K columns per wave: lane (r, s)
+// (r = lane / LPR, s = lane % LPR) reads half-group chunks hg = LPR*j + s of
+// row row0 + r.  Out-of-range chunks read the row's last chunk and are
+// disabled through a zero scale/bias word.
+template <int LPR, int J>
+struct Tile {
+    uint4 q[J];
+    uint4 sv, bv;   // lane l < RPW*G/8: uint4 l of the tile's scales / biases
+};
+
+// Scale/bias loads are issued before the code loads, so that storing them to
+// LDS does not wait for the codes.  The RPW rows' scales are RPW*G contiguous
+// fp16 values (RPW*G/8 uint4; RPW*G is a multiple of 8 by the launch rule).
+template <int LPR, int J>
+__device__ __forceinline__ void tile_load_sb(Tile<LPR, J> &t, const Mat &m, int row0, int K,
+                                             int lane) {
+    constexpr int RPW = WAVE / LPR;
+    const int G = K >> 6, NS = RPW * G / 8;
+    const int l = min(lane, NS - 1);
+    t.sv = reinterpret_cast<const uint4 *>(m.s + (size_t)row0 * G)[l];
+    t.bv = reinterpret_cast<const uint4 *>(m.b + (size_t)row0 * G)[l];
+}
+
+template <int LPR, int J>
+__device__ __forceinline__ void tile_load_q(Tile<LPR, J> &t, const Mat &m, int row0, int K,
+                                            int lane) {
+    const int H = K >> 5;
+    const int r = lane / LPR, s = lane % LPR;
     const uint4 *qrow = reinterpret_cast<const uint4 *>(m.q + (size_t)(row0 + r) * (K >> 1));
-    const uint16_t *srow = m.s + (size_t)(row0 + r) * G;
-    const uint16_t *brow = m.b + (size_t)(row0 + r) * G;
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-        const int hg = 8 * j + s;
-        if (hg < H) {
-            q[j] = qrow[hg];
-            sb[j] = (uint32_t)srow[hg >> 1] | ((uint32_t)brow[hg >> 1] << 16);
-        } else {
-            q[j] = make_uint4(0, 0, 0, 0);
-            sb[j] = 0;
-        }
+    for (int j = 0; j < J; ++j) t.q[j] = qrow[min(LPR * j + s, H - 1)];
+}
+
+// Interleave the tile's scales and biases into LDS words (scale | bias<<16),
+// [RPW][G].
+template <int LPR, int J>
+__device__ __forceinline__ void tile_store_sb(const Tile<LPR, J> &t, uint32_t *lsb, int G,
+                                              int lane) {
+    constexpr int RPW = WAVE / LPR;
+    if (lane < RPW * G / 8) {
+        const uint32_t s4[4] = {t.sv.x, t.sv.y, t.sv.z, t.sv.w};
+        const uint32_t b4[4] = {t.bv.x, t.bv.y, t.bv.z, t.bv.w};
+        uint4 o0, o1;
+        o0.x = (s4[0] & 0xFFFFu) | (b4[0] << 16); o0.y = (s4[0] >> 16) | (b4[0] & 0xFFFF0000u);
+        o0.z = (s4[1] & 0xFFFFu) | (b4[1] << 16); o0.w = (s4[1] >> 16) | (b4[1] & 0xFFFF0000u);
+        o1.x = (s4[2] & 0xFFFFu) | (b4[2] << 16); o1.y = (s4[2] >> 16) | (b4[2] & 0xFFFF0000u);
+        o1.z = (s4[3] & 0xFFFFu) | (b4[3] << 16); o1.w = (s4[3] >> 16) | (b4[3] & 0xFFFF0000u);
+        reinterpret_cast<uint4 *>(lsb)[2 * lane] = o0;
+        reinterpret_cast<uint4 *>(lsb)[2 * lane + 1] = o1;
     }
 }
 
-// Partial dot product of the lane's chunks against a staged fp16 row.
-template <int J>
-__device__ __forceinline__ float tile_dot_x(const uint4 (&q)[J], const uint32_t (&sb)[J],
-                                            const uint4 *xp, const float *xs, int H, int lane) {
-    const int s = lane & 7;
+// Sum over the LPR lanes of a row group; every lane of the group gets it.
+template <int LPR>
+__device__ __forceinline__ float row_sum(float v) {
+    v += dpp_f<DPP_XOR1>(v);
+    v += dpp_f<DPP_XOR2>(v);
+    v += dpp_f<DPP_HALF_MIRROR>(v);
+    if (LPR == 16) v += dpp_f<DPP_MIRROR>(v);
+    return v;
+}
+
+// Partial dot product of the lane's chunks with one staged activation row:
+// P = pair words [4][H] (uint4), S = (X, C) per half-group.  With LO, a
+// second pair row (the low part of a hi/lo split) is added into the same sums.
+// The compiler barrier keeps each chunk's LDS reads next to their use
+// (bounded register use; other waves on the SIMD hide the LDS latency), and
+// each chunk waits only for its own code load.
+template <bool LO>
+struct Act {
+    uint4 x[4], xl[LO ? 4 : 1];
+    float2 xc;
+    uint32_t sbw;
+};
+
+template <bool LO>
+__device__ __forceinline__ void act_read(Act<LO> &A, const uint32_t *lsb, int G, const uint4 *P,
+                                         const uint4 *PL, const float2 *S, int H, int r, int hg0) {
+    const int hg = min(hg0, H - 1);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) A.x[m] = P[m * H + hg];
+    if (LO) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) A.xl[LO ? m : 0] = PL[m * H + hg];
+    }
+    A.xc = S[hg];
+    A.sbw = hg0 < H ? lsb[r * G + (hg >> 1)] : 0u;
+}
+
+template <bool LO>
+__device__ __forceinline__ float act_dot(const Act<LO> &A, uint4 q, float acc) {
+    float de = 0.f, dd = 0.f;
+    q4_chunk(q, A.x[0], A.x[1], A.x[2], A.x[3], de, dd);
+    if (LO) q4_chunk(q, A.xl[0], A.xl[LO ? 1 : 0], A.xl[LO ? 2 : 0], A.xl[LO ? 3 : 0], de, dd);
+    const float sc = h2f((uint16_t)(A.sbw & 0xFFFF)), bi = h2f((uint16_t)(A.sbw >> 16));
+    return fmaf(sc, fmaf(dd, 0.0625f, de - A.xc.y), fmaf(bi, A.xc.x, acc));
+}
+
+template <int LPR, int J, bool LO>
+__device__ __forceinline__ float tile_dot(const Tile<LPR, J> &t, const uint32_t *lsb, int G,
+                                          const uint4 *P, const uint4 *PL, const float2 *S, int H,
+                                          int lane) {
+    const int r = lane / LPR, s = lane % LPR;
     float acc = 0.f;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-        const int hg = 8 * j + s;
-        if (hg < H) {
-            const float D = q4_chunk_dot(q[j], xp + hg, xp + H + hg, xp + 2 * H + hg,
-                                         xp + 3 * H + hg, 0.f);
-            const float sc = h2f((uint16_t)(sb[j] & 0xFFFF)), bi = h2f((uint16_t)(sb[j] >> 16));
-            acc = fmaf(sc, D, fmaf(fmaf(-1024.f, sc, bi), xs[hg], acc));
-        }
+        Act<LO> cur;
+        act_read<LO>(cur, lsb, G, P, PL, S, H, r, LPR * j + s);
+        asm volatile("" ::: "memory");
+        acc = act_dot<LO>(cur, t.q[j], acc);
+        __builtin_amdgcn_sched_barrier(0);
     }
     return acc;
 }
 
-// Same against a staged hi/lo pair of fp16 rows (fp32 activation).
-template <int J>
-__device__ __forceinline__ float tile_dot_hl(const uint4 (&q)[J], const uint32_t (&sb)[J],
-                                             const uint4 *hp, const uint4 *lp, const float *xs,
-                                             int H, int lane) {
-    const int s = lane & 7;
-    float acc = 0.f;
+// LDS stage layouts (bytes): fp16 row  = pairs [4H] uint4 + S [H] float2
+//                            hi/lo row = hi [4H] uint4 + lo [4H] uint4 + S [H] float2
+__host__ __device__ constexpr int xst_bytes(int K) { return 72 * (K >> 5); }
+__host__ __device__ constexpr int hst_bytes(int K) { return 136 * (K >> 5); }
+
+// ------------------------------------------------------- fp16 x staging
+// Up to 4 rows (row i at rp[i]) of K fp16 values, 8-value blocks, thread t
+// takes blocks t, t+256, ...: loads first (xs_load), processing later
+// (xs_store) so that weight loads can be issued in between.
+template <int MAXI>
+struct XStage {
+    uint4 v[MAXI];
+};
+
+__device__ __forceinline__ const uint16_t *pick4(const uint16_t *const (&rp)[4], int row) {
+    return row == 0 ? rp[0] : row == 1 ? rp[1] : row == 2 ? rp[2] : rp[3];
+}
+
+template <int MAXI>
+__device__ __forceinline__ void xs_load(XStage<MAXI> &X, const uint16_t *const (&rp)[4],
+                                        int rows, int K, int tid) {
+    const int NB = K >> 3, NT = rows * NB;
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-        const int hg = 8 * j + s;
-        if (hg < H) {
-            float D = q4_chunk_dot(q[j], hp + hg, hp + H + hg, hp + 2 * H + hg, hp + 3 * H + hg,
-                                   0.f);
-            D = q4_chunk_dot(q[j], lp + hg, lp + H + hg, lp + 2 * H + hg, lp + 3 * H + hg, D);
-            const float sc = h2f((uint16_t)(sb[j] & 0xFFFF)), bi = h2f((uint16_t)(sb[j] >> 16));
-            acc = fmaf(sc, D, fmaf(fmaf(-1024.f, sc, bi), xs[hg], acc));
+    for (int i = 0; i < MAXI; ++i) {
+        const int bb = min(tid + WG * i, NT - 1);
+        const int row = bb / NB, b = bb - row * NB;
+        X.v[i] = reinterpret_cast<const uint4 *>(pick4(rp, row))[b];
+    }
+}
+
+template <int MAXI>
+__device__ __forceinline__ void xs_store(const XStage<MAXI> &X, int rows, int K,
+                                         unsigned char *base, int tid) {
+    const int H = K >> 5, NB = K >> 3, NT = rows * NB, sb = xst_bytes(K);
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+        const int bb = tid + WG * i;
+        if (WG * i < NT) {   // uniform: all lanes run the quad sums
+            const uint32_t w4[4] = {X.v[i].x, X.v[i].y, X.v[i].z, X.v[i].w};
+            float xe = 0.f, xo = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                xe += h2f((uint16_t)(w4[e] & 0xFFFF));
+                xo += h2f((uint16_t)(w4[e] >> 16));
+            }
+            xe += dpp_f<DPP_XOR1>(xe);
+            xe += dpp_f<DPP_XOR2>(xe);
+            xo += dpp_f<DPP_XOR1>(xo);
+            xo += dpp_f<DPP_XOR2>(xo);
+            if (bb < NT) {
+                const int row = bb / NB, b = bb - row * NB, hg = b >> 2, m = b & 3;
+                unsigned char *st = base + (size_t)row * sb;
+                reinterpret_cast<uint4 *>(st)[m * H + hg] = pair_halves(X.v[i]);
+                if (m == 0)
+                    reinterpret_cast<float2 *>(st + 64 * H)[hg] =
+                        make_float2(xe + xo, fmaf(1024.f, xe, 64.f * xo));
+            }
         }
     }
-    return acc;
 }
 
-// LDS footprint of one staged fp16 row / hi-lo row of K values (bytes).
-__host__ __device__ constexpr int x_stage_bytes(int K) { return (2 * K + 4 * (K >> 5) + 15) & ~15; }
-__host__ __device__ constexpr int h_stage_bytes(int K) { return (4 * K + 4 * (K >> 5) + 15) & ~15; }
+// --------------------------------------------------- hi/lo h staging
+// Global hi/lo row (written by producers): 10H uint4 = hi [4H] | lo [4H] |
+// per half-group four partial (X, C) pairs, one per 8-value block.  The
+// consumer copies the pair words and adds the four partials in order.
+template <int MAXI, int MAXS>
+struct HStage {
+    uint4 v[MAXI];
+    uint4 s0[MAXS], s1[MAXS];
+};
 
-__device__ __forceinline__ void x_stage_ptrs(unsigned char *base, int K, int i, uint4 *&xp,
-                                             float *&xs) {
-    unsigned char *p = base + (size_t)i * x_stage_bytes(K);
-    xp = reinterpret_cast<uint4 *>(p);
-    xs = reinterpret_cast<float *>(p + 2 * K);
+template <int MAXI, int MAXS>
+__device__ __forceinline__ void hs_load(HStage<MAXI, MAXS> &Hs, const uint4 *src, int rows, int K,
+                                        int tid) {
+    const int H = K >> 5, NC = rows * 8 * H, NS = rows * H;
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+        const int c = min(tid + WG * i, NC - 1);
+        const int row = c / (8 * H), o = c - row * 8 * H;
+        Hs.v[i] = src[(size_t)row * 10 * H + o];
+    }
+#pragma unroll
+    for (int i = 0; i < MAXS; ++i) {
+        const int c = min(tid + WG * i, NS - 1);
+        const int row = c / H, hg = c - row * H;
+        const uint4 *p = src + (size_t)row * 10 * H + 8 * H + 2 * hg;
+        Hs.s0[i] = p[0];
+        Hs.s1[i] = p[1];
+    }
 }
 
-__device__ __forceinline__ void h_stage_ptrs(unsigned char *base, int K, int i, uint4 *&hp,
-                                             uint4 *&lp, float *&xs) {
-    unsigned char *p = base + (size_t)i * h_stage_bytes(K);
-    hp = reinterpret_cast<uint4 *>(p);
-    lp = reinterpret_cast<uint4 *>(p + 2 * K);
-    xs = reinterpret_cast<float *>(p + 4 * K);
+template <int MAXI, int MAXS>
+__device__ __forceinline__ void hs_store(const HStage<MAXI, MAXS> &Hs, int rows, int K,
+                                         unsigned char *base, int tid) {
+    const int H = K >> 5, NC = rows * 8 * H, NS = rows * H, sb = hst_bytes(K);
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+        const int c = tid + WG * i;
+        if (c < NC) {
+            const int row = c / (8 * H), o = c - row * 8 * H;
+            reinterpret_cast<uint4 *>(base + (size_t)row * sb)[o] = Hs.v[i];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < MAXS; ++i) {
+        const int c = tid + WG * i;
+        if (c < NS) {
+            const int row = c / H, hg = c - row * H;
+            const uint4 a = Hs.s0[i], b = Hs.s1[i];
+            const float X = ((__uint_as_float(a.x) + __uint_as_float(a.z)) + __uint_as_float(b.x)) +
+                            __uint_as_float(b.z);
+            const float C = ((__uint_as_float(a.y) + __uint_as_float(a.w)) + __uint_as_float(b.y)) +
+                            __uint_as_float(b.w);
+            reinterpret_cast<float2 *>(base + (size_t)row * sb + 128 * H)[hg] = make_float2(X, C);
+        }
+    }
 }
 
-__device__ __forceinline__ uint32_t ld_acquire_u32(const uint32_t *p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Producer side: the 8 values of rows 8*blk .. 8*blk+7 of one hidden row of
+// length K go to the global hi/lo row `dst` (10H uint4).
+__device__ __forceinline__ void hs_produce(uint4 *dst, int K, int blk, const float (&e)[8]) {
+    const int H = K >> 5;
+    float hi[8], lo[8], xe = 0.f, xo = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        hi[q] = (float)(_Float16)e[q];
+        lo[q] = (float)(_Float16)(e[q] - hi[q]);
+        if (q & 1) xo += hi[q] + lo[q];
+        else xe += hi[q] + lo[q];
+    }
+    const int hg = blk >> 2, m = blk & 3;
+    dst[m * H + hg] = make_uint4(pack_h2(hi[0], hi[4]), pack_h2(hi[1], hi[5]),
+                                 pack_h2(hi[2], hi[6]), pack_h2(hi[3], hi[7]));
+    dst[4 * H + m * H + hg] = make_uint4(pack_h2(lo[0], lo[4]), pack_h2(lo[1], lo[5]),
+                                         pack_h2(lo[2], lo[6]), pack_h2(lo[3], lo[7]));
+    reinterpret_cast<float2 *>(dst + 8 * H + 2 * hg)[m] =
+        make_float2(xe + xo, fmaf(1024.f, xe, 64.f * xo));
 }
 
-// ---------------------------------------------------------------- top-k
-// Top-k of token t by (logit desc, id asc), or the forced ids; softmax in
-// fp64 over the k selected logits (max-subtracted).  One wave.
-__device__ void topk_token(const DecodeArgs &a, int t, int lane, unsigned char *lds) {
-    double *l = reinterpret_cast<double *>(lds);
-    int *sel = reinterpret_cast<int *>(l + a.E);
+// ------------------------------------------------------------------ top-k
+// Top-k of token t by (logit desc, id asc) -- or the forced ids -- and the
+// softmax in fp64 over the k selected logits (max-subtracted).  Whole WG.
+__device__ void topk_block(const DecodeArgs &a, int t, int tid, unsigned char *lds) {
+    double *l = reinterpret_cast<double *>(lds);            // [E] (+1 pad)
+    double *ex = l + ((a.E + 2) & ~1);                       // [16]
+    int *sel = reinterpret_cast<int *>(ex + 16);             // [16]
+    int *part = sel + 16;                                    // [256]
     __syncthreads();
-    for (int i = lane; i < a.E; i += WAVE) {
+    for (int i = tid; i < a.E; i += WG) {
         const double v = __hip_atomic_load(a.logits + (size_t)t * a.E + i, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
         l[i] = (v != v) ? -__builtin_inf() : v;   // NaN ranks last
     }
+    if (tid == 0) l[a.E] = -__builtin_inf();     // pad for the pairwise reads
     __syncthreads();
     if (a.forced) {
-        uint32_t flags = 0;
-        if (lane < a.k) {
-            int id = a.forced[(size_t)t * a.k + lane];
-            if (id < 0 || id >= a.E) {
-                flags |= TF_FLAG_ID_RANGE;
-                id = id < 0 ? 0 : a.E - 1;
-            }
-            sel[lane] = id;
+        uint32_t fl = 0;
+        if (tid < a.k) {
+            int id = a.forced[(size_t)t * a.k + tid];
+            if (id < 0 || id >= a.E) { fl |= TF_FLAG_ID_RANGE; id = id < 0 ? 0 : a.E - 1; }
+            sel[tid] = id;
         }
         __syncthreads();
-        if (lane < a.k)
-            for (int r = 0; r < lane; ++r)
-                if (sel[r] == sel[lane]) flags |= TF_FLAG_ID_REPEAT;
-        if (flags) atomicOr(a.hdr + HDR_FLAGS, flags);
+        if (tid < a.k)
+            for (int r = 0; r < tid; ++r)
+                if (sel[r] == sel[tid]) fl |= TF_FLAG_ID_REPEAT;
+        if (fl) atomicOr(a.hdr + HDR_FLAGS, fl);
     } else {
-        // k rounds of a wave-wide argmax over the untaken candidates
-        uint32_t taken = 0;   // bit c: candidate lane + 64c taken
-        for (int r = 0; r < a.k; ++r) {
-            double bv = -__builtin_inf();
-            int bi = 0x7FFFFFFF;
-            for (int c = 0, i = lane; i < a.E; ++c, i += WAVE) {
-                if (taken & (1u << c)) continue;
-                const double v = l[i];
-                if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
+        // rank of candidate i = #{j : l_j > l_i or (l_j == l_i and j < i)};
+        // two threads per candidate, each over one half of the j range,
+        // reading the logits two at a time
+        const int half = tid >> 7;
+        const int E2 = ((a.E + 3) >> 2) << 1;   // even split point
+        const int jb = half * E2, je = min(a.E, jb + E2);
+        for (int base = 0; base < a.E; base += 128) {
+            const int i = base + (tid & 127);
+            int cnt = 0;
+            if (i < a.E) {
+                const double li = l[i];
+#pragma unroll 4
+                for (int j = jb; j < je; j += 2) {
+                    const double2 v = *reinterpret_cast<const double2 *>(l + j);
+                    cnt += (v.x > li) | ((v.x == li) & (j < i));
+                    cnt += (j + 1 < je) & ((v.y > li) | ((v.y == li) & (j + 1 < i)));
+                }
             }
-#pragma unroll
-            for (int o = 1; o < WAVE; o <<= 1) {
-                const double ov = __shfl_xor(bv, o);
-                const int oi = __shfl_xor(bi, o);
-                if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+            part[tid] = cnt;
+            __syncthreads();
+            if (tid < 128 && i < a.E) {
+                const int c = part[tid] + part[tid + 128];
+                if (c < a.k) sel[c] = i;
             }
-            if ((bi & (WAVE - 1)) == lane) taken |= 1u << (bi / WAVE);
-            if (lane == 0) sel[r] = bi;
+            __syncthreads();
         }
     }
     __syncthreads();
-    if (lane == 0) {
+    if (tid < a.k) {
         double m = l[sel[0]];
         for (int r = 1; r < a.k; ++r) m = fmax(m, l[sel[r]]);
-        double p[16], s = 0.0;
-        for (int r = 0; r < a.k; ++r) { p[r] = exp(l[sel[r]] - m); s += p[r]; }
-        for (int r = 0; r < a.k; ++r) {
-            a.ids[(size_t)t * a.k + r] = sel[r];
-            a.weights[(size_t)t * a.k + r] = (float)(p[r] / s);
-        }
+        ex[tid] = exp(l[sel[tid]] - m);
+    }
+    __syncthreads();
+    if (tid < a.k) {
+        double s = 0.0;
+        for (int r = 0; r < a.k; ++r) s += ex[r];
+        a.ids[(size_t)t * a.k + tid] = sel[tid];
+        a.weights[(size_t)t * a.k + tid] = (float)(ex[tid] / s);
     }
 }
 
-// Group the T*k (token, rank) pairs by expert: pairs sorted by (expert,
-// token, rank); items hold at most a.tbx pairs of one expert.  One wave.
-__device__ void group_pairs(const DecodeArgs &a, int lane, unsigned char *lds) {
-    const int P = a.T * a.k;
+// Group the T*k (token, rank) pairs by expert: sorted by (expert, token,
+// rank); an item is at most a.tbx consecutive pairs of one expert.  Whole WG.
+__device__ void group_block(const DecodeArgs &a, int tid, unsigned char *lds) {
+    const int P = a.T * a.k;   // <= 256
     int *pid = reinterpret_cast<int *>(lds);
-    int *sorted = pid + P;
+    int *sorted = pid + 256;
+    int *start = sorted + 256;
+    int *end = start + 256;    // one past the last sorted position of the expert
     __syncthreads();
-    for (int p = lane; p < P; p += WAVE)
-        pid[p] = (int)__hip_atomic_load(reinterpret_cast<const uint32_t *>(a.ids) + p,
-                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid < P)
+        pid[tid] = (int)__hip_atomic_load(reinterpret_cast<const uint32_t *>(a.ids) + tid,
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    for (int p = lane; p < P; p += WAVE) {
-        const int e = pid[p];
-        int pos = 0;
-        for (int q = 0; q < P; ++q) pos += (pid[q] < e) | ((pid[q] == e) & (q < p));
-        sorted[pos] = p;
+    if (tid < P) {
+        const int e = pid[tid];
+        int less = 0, same = 0, before = 0;
+        for (int q = 0; q < P; ++q) {
+            const int eq = pid[q];
+            less += eq < e;
+            same += eq == e;
+            before += (eq == e) & (q < tid);
+        }
+        const int pos = less + before;
+        sorted[pos] = tid;
+        start[pos] = (before % a.tbx) == 0;
+        end[pos] = less + same;
     }
     __syncthreads();
-    if (lane == 0) {
+    if (tid < P && start[tid]) {
+        int idx = 0;
+        for (int q = 0; q < tid; ++q) idx += start[q];
+        int *it = a.items + 4 * idx;
+        it[0] = pid[sorted[tid]];
+        it[1] = tid;
+        it[2] = min(a.tbx, end[tid] - tid);
+        it[3] = 0;
+    }
+    if (tid < P) a.pairs[tid] = sorted[tid];
+    if (tid == 0) {
         int n = 0;
-        for (int i = 0; i < P;) {
-            const int e = pid[sorted[i]];
-            int j = i + 1;
-            while (j < P && j - i < a.tbx && pid[sorted[j]] == e) ++j;
-            int *it = a.items + 4 * n;
-            it[0] = e; it[1] = i; it[2] = j - i; it[3] = 0;
-            ++n;
-            i = j;
-        }
+        for (int q = 0; q < P; ++q) n += start[q];
         a.hdr[HDR_NITEMS] = (uint32_t)n;
     }
-    for (int p = lane; p < P; p += WAVE) a.pairs[p] = sorted[p];
 }
 
-// ----------------------------------------------------------- router wave
-// Logit of expert e for token t: sum over 16-element chunks of
-// s_g * sum_i q_i x_i + b_g * sum_i x_i, products and sums in fp64.
-__device__ void router_wave(const DecodeArgs &a, int bid, int lane, unsigned char *lds) {
-    const int t = bid / a.E, e = bid - t * a.E;
+// ------------------------------------------------------------- router
+// Four router rows per workgroup (one per wave).  Logit of expert e: sum
+// over 16-element chunks of s_g * sum_i q_i x_i + b_g * sum_i x_i, products
+// exact and every sum in fp64.
+__device__ void router_block(const DecodeArgs &a, int b, int tid, unsigned char *lds) {
+    const int lane = tid & 63, w = uniform(tid >> 6);
+    const int nrb = (a.E + 3) >> 2;
+    const int t = b / nrb, e = (b - t * nrb) * 4 + w;
     const int d = a.d, NC = d >> 4, G = d >> 6;
     constexpr int JR = 4;   // d <= 4096
+    const bool row_ok = e < a.E;
+    const int er = row_ok ? e : 0;
+    // x as fp64 into LDS: thread c < NC converts 16 values (two uint4 loads)
+    uint4 xv0 = make_uint4(0, 0, 0, 0), xv1 = xv0;
+    if (tid < NC) {
+        const uint4 *xv = reinterpret_cast<const uint4 *>(a.x + (size_t)t * d);
+        xv0 = xv[2 * tid];
+        xv1 = xv[2 * tid + 1];
+    }
     uint4 qv[JR];
-    double sv[JR], bv[JR];
-    const uint4 *qrow = reinterpret_cast<const uint4 *>(a.rq + (size_t)e * d);
+    uint32_t sbw[JR];
+    const uint4 *qrow = reinterpret_cast<const uint4 *>(a.rq + (size_t)er * d);
 #pragma unroll
     for (int j = 0; j < JR; ++j) {
-        const int c = lane + WAVE * j;
-        if (c < NC) {
-            qv[j] = qrow[c];
-            sv[j] = (double)h2f(a.rs[(size_t)e * G + (c >> 2)]);
-            bv[j] = (double)h2f(a.rb[(size_t)e * G + (c >> 2)]);
-        }
+        const int c = min(lane + WAVE * j, NC - 1);
+        qv[j] = qrow[c];
+        sbw[j] = (uint32_t)a.rs[(size_t)er * G + (c >> 2)] |
+                 ((uint32_t)a.rb[(size_t)er * G + (c >> 2)] << 16);
     }
     double *xd = reinterpret_cast<double *>(lds);
     double *x16 = xd + d;
-    const uint4 *xv = reinterpret_cast<const uint4 *>(a.x + (size_t)t * d);
-    for (int c = lane; c < NC; c += WAVE) {
-        const uint4 v0 = xv[2 * c], v1 = xv[2 * c + 1];
-        const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-        double s = 0.0;
+    int *flag = reinterpret_cast<int *>(x16 + NC);
+    if (tid < NC) {
+        const uint32_t w8[8] = {xv0.x, xv0.y, xv0.z, xv0.w, xv1.x, xv1.y, xv1.z, xv1.w};
+        double v[16], s = 0.0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const double lo = (double)h2f((uint16_t)(w[i] & 0xFFFF));
-            const double hi = (double)h2f((uint16_t)(w[i] >> 16));
-            xd[16 * c + 2 * i] = lo;
-            xd[16 * c + 2 * i + 1] = hi;
-            s += lo + hi;
+            v[2 * i] = (double)h2f((uint16_t)(w8[i] & 0xFFFF));
+            v[2 * i + 1] = (double)h2f((uint16_t)(w8[i] >> 16));
+            s += v[2 * i] + v[2 * i + 1];
         }
-        x16[c] = s;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            reinterpret_cast<double2 *>(xd + 16 * tid)[i] = make_double2(v[2 * i], v[2 * i + 1]);
+        x16[tid] = s;
     }
     __syncthreads();
     double acc = 0.0;
 #pragma unroll
     for (int j = 0; j < JR; ++j) {
-        const int c = lane + WAVE * j;
-        if (c < NC) {
-            const uint32_t w[4] = {qv[j].x, qv[j].y, qv[j].z, qv[j].w};
-            const double *xx = xd + 16 * c;
-            double D = 0.0;
+        const int c0 = lane + WAVE * j;
+        const int c = min(c0, NC - 1);
+        const uint32_t w4[4] = {qv[j].x, qv[j].y, qv[j].z, qv[j].w};
+        const double2 *xx = reinterpret_cast<const double2 *>(xd + 16 * c);
+        double D = 0.0;
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                D = fma((double)((w[i >> 2] >> (8 * (i & 3))) & 0xFF), xx[i], D);
-            acc = fma(sv[j], D, fma(bv[j], x16[c], acc));
+        for (int i = 0; i < 8; ++i) {
+            const double2 xp = xx[i];
+            D = fma((double)((w4[i >> 1] >> (16 * (i & 1))) & 0xFF), xp.x, D);
+            D = fma((double)((w4[i >> 1] >> (16 * (i & 1) + 8)) & 0xFF), xp.y, D);
         }
+        const uint32_t sw = (c0 < NC && row_ok) ? sbw[j] : 0u;
+        acc = fma((double)h2f((uint16_t)(sw & 0xFFFF)), D,
+                  fma((double)h2f((uint16_t)(sw >> 16)), x16[c], acc));
     }
     acc = wave_sum_f64(acc);
-    if (lane == 0) a.logits[(size_t)t * a.E + e] = acc;
-    if (!a.topk) return;
-
-    // last router wave of token t: top-k (+ grouping when it is the last token)
-    __threadfence();
-    uint32_t old = 0;
-    if (lane == 0) old = atomicAdd(a.hdr + HDR_TICKET + t, 1u);
-    old = __shfl(old, 0);
-    if (old != (uint32_t)(a.E - 1)) return;
-    __threadfence();
-    if (lane == 0) a.hdr[HDR_TICKET + t] = 0;
-    topk_token(a, t, lane, lds);
-    if (!a.do_group) return;
-    __threadfence();
-    old = 0;
-    if (lane == 0) old = atomicAdd(a.hdr + HDR_TICKET + a.T, 1u);
-    old = __shfl(old, 0);
-    if (old != (uint32_t)(a.T - 1)) return;
-    __threadfence();
-    if (lane == 0) a.hdr[HDR_TICKET + a.T] = 0;
-    group_pairs(a, lane, lds);
-}
-
-// ----------------------------------------------- shared gate/up wave
-template <int J>
-__device__ void shared_gateup_wave(const DecodeArgs &a, int bid, int lane, unsigned char *lds) {
-    const int tiles = a.fs / TILE_ROWS;
-    const int tile = bid % tiles, sb = bid / tiles;
-    const int t0 = sb * a.tbx, nt = min(a.tbx, a.T - t0);
-    const int row0 = tile * TILE_ROWS, H = a.d >> 5;
-    Mat g, u, dn;
-    blob_mats(a.shared_blob, a.d, a.fs, g, u, dn);
-    uint4 qg[J], qu[J];
-    uint32_t sg[J], su[J];
-    load_tile<J>(g, row0, a.d, lane, qg, sg);
-    load_tile<J>(u, row0, a.d, lane, qu, su);
-    for (int i = 0; i < nt; ++i) {
-        uint4 *xp; float *xs;
-        x_stage_ptrs(lds, a.d, i, xp, xs);
-        stage_x_f16(a.x + (size_t)(t0 + i) * a.d, a.d, xp, xs, lane);
+    if (lane == 0 && row_ok) {
+        a.logits[(size_t)t * a.E + e] = acc;
+        __threadfence();
     }
     __syncthreads();
-    for (int i = 0; i < nt; ++i) {
-        uint4 *xp; float *xs;
-        x_stage_ptrs(lds, a.d, i, xp, xs);
-        const float gv = row8_sum(tile_dot_x<J>(qg, sg, xp, xs, H, lane));
-        const float uv = row8_sum(tile_dot_x<J>(qu, su, xp, xs, H, lane));
-        if ((lane & 7) == 0)
-            a.h_s[(size_t)(t0 + i) * a.fs + row0 + (lane >> 3)] = gelu_f(gv, a.act) * uv;
+    if (tid == 0) {
+        const uint32_t old = atomicAdd(a.hdr + HDR_TICKET + t, 1u);
+        *flag = old == (uint32_t)(nrb - 1);
     }
+    __syncthreads();
+    if (!*flag) return;
+    __threadfence();
+    if (tid == 0) a.hdr[HDR_TICKET + t] = 0;
+    topk_block(a, t, tid, lds);
+    if (!a.do_group || a.T == 1) return;
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t old = atomicAdd(a.hdr + HDR_TICKET + a.T, 1u);
+        reinterpret_cast<int *>(lds)[0] = old == (uint32_t)(a.T - 1);
+    }
+    __syncthreads();
+    if (!reinterpret_cast<int *>(lds)[0]) return;
+    __threadfence();
+    if (tid == 0) a.hdr[HDR_TICKET + a.T] = 0;
+    group_block(a, tid, lds);
 }
 
-// ---------------------------------------------- routed gate/up wave
-template <int J>
-__device__ void routed_gateup_wave(const DecodeArgs &a, int bid, int lane, unsigned char *lds) {
-    const int tiles = a.f / TILE_ROWS;
-    const int item = bid / tiles, tile = bid - item * tiles;
-    int e, begin, cnt;
-    if (a.gemv_slot) {               // standalone GEMV: item = pair
+// ------------------------------------------------------- gate/up block
+// 2*RPW output rows of (gate, up) for up to MAX_TB tokens: waves 0/1 gate
+// rows [0, RPW) / [RPW, 2 RPW), waves 2/3 the same up rows; then
+// h = coef * gelu(g) * u, written as hi/lo rows.  routed == false: the shared
+// expert, token sub-batch b / tiles -> h_s; routed == true: expert item
+// b / tiles -> h_r[pair].
+template <int LPR, int J, bool routed>
+__device__ void gateup_block(const DecodeArgs &a, int b, int tid, unsigned char *lds) {
+    constexpr int RPW = WAVE / LPR, RWG = 2 * RPW;
+    const int lane = tid & 63, w = uniform(tid >> 6);
+    const int F = routed ? a.f : a.fs;
+    const int tiles = F / RWG;
+    const int item = b / tiles, rb = b - item * tiles;
+    const int d = a.d, H = d >> 5, G = d >> 6;
+    float *gu = reinterpret_cast<float *>(lds);                      // [4*RPW][MAX_TB]
+    float *hv = gu + 4 * RPW * MAX_TB;                               // [MAX_TB][RWG]
+    uint32_t *lsb = reinterpret_cast<uint32_t *>(hv + RWG * MAX_TB); // [4][RPW*G]
+    unsigned char *xst = reinterpret_cast<unsigned char *>(lsb + 4 * RPW * G);
+
+    int nt, e = 0;
+    int prow[MAX_TB] = {0, 0, 0, 0};   // output row of token slot i (token or pair)
+    float coef[MAX_TB] = {1.f, 1.f, 1.f, 1.f};
+    const uint16_t *rp[4];
+    if (!routed) {
+        const int t0 = item * a.tbx;
+        nt = min(a.tbx, a.T - t0);
+#pragma unroll
+        for (int i = 0; i < MAX_TB; ++i) {
+            prow[i] = t0 + min(i, nt - 1);
+            rp[i] = a.x + (size_t)prow[i] * d;
+        }
+    } else if (a.gemv_slot) {
         if (item >= a.P) return;
-        e = a.gemv_slot[item]; begin = item; cnt = 1;
+        nt = 1;
+        e = a.gemv_slot[item];
+        prow[0] = item;
+        coef[0] = a.gemv_coef ? a.gemv_coef[item] : 1.f;
+        const int tok = a.gemv_token ? a.gemv_token[item] : item;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rp[i] = a.x + (size_t)tok * d;
+    } else if (a.T == 1) {
+        if (item >= a.k) return;
+        nt = 1;
+        e = a.ids[item];
+        prow[0] = item;
+        coef[0] = a.weights[item];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rp[i] = a.x;
     } else {
         if (item >= (int)a.hdr[HDR_NITEMS]) return;
         const int *it = a.items + 4 * item;
-        e = it[0]; begin = it[1]; cnt = it[2];
-    }
-    const int row0 = tile * TILE_ROWS, H = a.d >> 5;
-    Mat g, u, dn;
-    blob_mats(expert_blob(a, e), a.d, a.f, g, u, dn);
-    uint4 qg[J], qu[J];
-    uint32_t sg[J], su[J];
-    load_tile<J>(g, row0, a.d, lane, qg, sg);
-    load_tile<J>(u, row0, a.d, lane, qu, su);
-    int prow[4], tok[4];
-    for (int i = 0; i < cnt; ++i) {
-        if (a.gemv_slot) {
-            prow[i] = begin + i;
-            tok[i] = a.gemv_token ? a.gemv_token[begin + i] : begin + i;
-        } else {
-            prow[i] = a.pairs[begin + i];
-            tok[i] = prow[i] / a.k;
+        e = it[0];
+        nt = it[2];
+#pragma unroll
+        for (int i = 0; i < MAX_TB; ++i) {
+            const int p = a.pairs[it[1] + min(i, nt - 1)];
+            prow[i] = p;
+            coef[i] = a.weights[p];
+            rp[i] = a.x + (size_t)(p / a.k) * d;
         }
-        uint4 *xp; float *xs;
-        x_stage_ptrs(lds, a.d, i, xp, xs);
-        stage_x_f16(a.x + (size_t)tok[i] * a.d, a.d, xp, xs, lane);
+    }
+    // activation loads, then weight loads, then activation processing
+    XStage<(J * LPR + 15) / 16> X;   // <= 4 rows of d/8 <= 4*J*LPR blocks over 256 threads
+    xs_load(X, rp, nt, d, tid);
+    Mat g, u, dn;
+    blob_mats(routed ? expert_blob(a, e) : a.shared_blob, d, F, g, u, dn);
+    Tile<LPR, J> tl;
+    const Mat &mm = (w >> 1) ? u : g;
+    const int row0 = rb * RWG + RPW * (w & 1);
+    tile_load_sb<LPR, J>(tl, mm, row0, d, lane);
+    tile_load_q<LPR, J>(tl, mm, row0, d, lane);
+    xs_store(X, nt, d, xst, tid);
+    tile_store_sb(tl, lsb + w * RPW * G, G, lane);
+    __syncthreads();
+    const int xsb = xst_bytes(d);
+    auto one = [&](int i) {
+        const unsigned char *st = xst + (size_t)i * xsb;
+        const float v = row_sum<LPR>(tile_dot<LPR, J, false>(
+            tl, lsb + w * RPW * G, G, reinterpret_cast<const uint4 *>(st), nullptr,
+            reinterpret_cast<const float2 *>(st + 64 * H), H, lane));
+        if (lane % LPR == 0) gu[(w * RPW + lane / LPR) * MAX_TB + i] = v;
+    };
+    if (nt == 1) {
+        one(0);   // straight line: chunk j waits only for its own load
+    } else {
+        for (int i = 0; i < nt; ++i) one(i);
     }
     __syncthreads();
-    for (int i = 0; i < cnt; ++i) {
-        uint4 *xp; float *xs;
-        x_stage_ptrs(lds, a.d, i, xp, xs);
-        const float gv = row8_sum(tile_dot_x<J>(qg, sg, xp, xs, H, lane));
-        const float uv = row8_sum(tile_dot_x<J>(qu, su, xp, xs, H, lane));
-        if ((lane & 7) == 0)
-            a.h_r[(size_t)prow[i] * a.f + row0 + (lane >> 3)] = gelu_f(gv, a.act) * uv;
+    if (tid < RWG * nt) {
+        const int row = tid % RWG, i = tid / RWG;
+        const int half = row / RPW, rr = row % RPW;
+        const float gv = gu[(half * RPW + rr) * MAX_TB + i];
+        const float uv = gu[((2 + half) * RPW + rr) * MAX_TB + i];
+        hv[i * RWG + row] = gelu_f(gv, a.act) * uv;
+    }
+    __syncthreads();
+    if (tid < (RWG / 8) * nt) {
+        const int i = tid / (RWG / 8), sub = tid % (RWG / 8);
+        const float c = coef[0] * (i == 0) + coef[1] * (i == 1) + coef[2] * (i == 2) +
+                        coef[3] * (i == 3);
+        const int pr = i == 0 ? prow[0] : i == 1 ? prow[1] : i == 2 ? prow[2] : prow[3];
+        float ev[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) ev[q] = c * hv[i * RWG + 8 * sub + q];
+        uint4 *dst = (routed ? a.h_r : a.h_s) + (size_t)pr * (10 * (F >> 5));
+        hs_produce(dst, F, rb * (RWG / 8) + sub, ev);
     }
 }
 
-// ------------------------------------------------- shared down wave
-template <int J>
-__device__ void shared_down_wave(const DecodeArgs &a, int bid, int lane, unsigned char *lds) {
-    const int tiles = a.d / TILE_ROWS;
-    const int tile = bid % tiles, sb = bid / tiles;
+// --------------------------------------------------------- shared down
+// 4*RPW output rows (RPW per wave) of the shared down projection for up to
+// tbh tokens: y_s[t][row].
+template <int LPR, int J>
+__device__ void shared_down_block(const DecodeArgs &a, int b, int tid, unsigned char *lds) {
+    constexpr int RPW = WAVE / LPR;
+    const int lane = tid & 63, w = uniform(tid >> 6);
+    const int tiles = a.d / (4 * RPW);
+    const int sb = b / tiles, rb = b - sb * tiles;
     const int t0 = sb * a.tbh, nt = min(a.tbh, a.T - t0);
-    const int row0 = tile * TILE_ROWS, H = a.fs >> 5;
+    const int K = a.fs, H = K >> 5, G = K >> 6;
+    uint32_t *lsb = reinterpret_cast<uint32_t *>(lds);               // [4][RPW*G]
+    unsigned char *hst = reinterpret_cast<unsigned char *>(lsb + 4 * RPW * G);
+    HStage<(J * LPR + 31) / 32, (J * LPR + 255) / 256> Hs;   // 1 row: 8H copies, H sums
+    hs_load(Hs, a.h_s + (size_t)t0 * 10 * H, nt, K, tid);
     Mat g, u, dn;
     blob_mats(a.shared_blob, a.d, a.fs, g, u, dn);
-    uint4 q[J];
-    uint32_t sbw[J];
-    load_tile<J>(dn, row0, a.fs, lane, q, sbw);
-    for (int i = 0; i < nt; ++i) {
-        uint4 *hp, *lp; float *xs;
-        h_stage_ptrs(lds, a.fs, i, hp, lp, xs);
-        stage_h_f32(a.h_s + (size_t)(t0 + i) * a.fs, 1.f, a.fs, hp, lp, xs, lane);
-    }
+    const int row0 = rb * 4 * RPW + RPW * w;
+    Tile<LPR, J> tl;
+    tile_load_sb<LPR, J>(tl, dn, row0, K, lane);
+    tile_load_q<LPR, J>(tl, dn, row0, K, lane);
+    hs_store(Hs, nt, K, hst, tid);
+    tile_store_sb(tl, lsb + w * RPW * G, G, lane);
     __syncthreads();
-    for (int i = 0; i < nt; ++i) {
-        uint4 *hp, *lp; float *xs;
-        h_stage_ptrs(lds, a.fs, i, hp, lp, xs);
-        const float v = row8_sum(tile_dot_hl<J>(q, sbw, hp, lp, xs, H, lane));
-        if ((lane & 7) == 0) a.y_s[(size_t)(t0 + i) * a.d + row0 + (lane >> 3)] = v;
+    const int hsb = hst_bytes(K);
+    auto one = [&](int i) {
+        const unsigned char *st = hst + (size_t)i * hsb;
+        const float v = row_sum<LPR>(tile_dot<LPR, J, true>(
+            tl, lsb + w * RPW * G, G, reinterpret_cast<const uint4 *>(st),
+            reinterpret_cast<const uint4 *>(st + 64 * H),
+            reinterpret_cast<const float2 *>(st + 128 * H), H, lane));
+        if (lane % LPR == 0) a.y_s[(size_t)(t0 + i) * a.d + row0 + lane / LPR] = v;
+    };
+    if (nt == 1) {
+        one(0);
+    } else {
+        for (int i = 0; i < nt; ++i) one(i);
     }
 }
 
-template <int J>
-__global__ __launch_bounds__(64) void k_stage_a(DecodeArgs a) {
+template <int LPR, int J>
+__global__ __launch_bounds__(256, 4) void k_stage_a(DecodeArgs a) {
     extern __shared__ __align__(16) unsigned char lds[];
-    const int bid = blockIdx.x, lane = threadIdx.x;
-    if (bid < a.a_router_waves)
-        router_wave(a, bid, lane, lds);
+    const int b = blockIdx.x, tid = threadIdx.x;
+    if (b < a.a_router_blocks)
+        router_block(a, b, tid, lds);
     else
-        shared_gateup_wave<J>(a, bid - a.a_router_waves, lane, lds);
+        gateup_block<LPR, J, false>(a, b - a.a_router_blocks, tid, lds);
 }
 
-template <int J>
-__global__ __launch_bounds__(64) void k_stage_b(DecodeArgs a) {
+template <int LPR, int J>
+__global__ __launch_bounds__(256, 4) void k_stage_b(DecodeArgs a) {
     extern __shared__ __align__(16) unsigned char lds[];
-    const int bid = blockIdx.x, lane = threadIdx.x;
-    if (bid < a.b_routed_waves)
-        routed_gateup_wave<J>(a, bid, lane, lds);
+    const int b = blockIdx.x, tid = threadIdx.x;
+    if (b < a.b_routed_blocks)
+        gateup_block<LPR, J, true>(a, b, tid, lds);
     else
-        shared_down_wave<J>(a, bid - a.b_routed_waves, lane, lds);
+        shared_down_block<LPR, J>(a, b - a.b_routed_blocks, tid, lds);
 }
 
-// ------------------------------------------- routed down + combine wave
-// y[t][row] = base[t][row] + sum over the token's pairs (in order) of
-//             W_down,e (coef * h_pair)[row]
-template <int J>
-__global__ __launch_bounds__(64) void k_stage_c(DecodeArgs a) {
+// ---------------------------------------------- routed down + combine
+// One 8-row output tile of one token (8 lanes per row); the token's pairs
+// are split across the four waves (pairs w and w+4 of each pass of up to 8),
+// and the waves' partial sums are added in wave order.  Layer: y = y_s + sum
+// -> fp16 (and y32); standalone GEMV: y32 += sum.
+template <int JF>
+__global__ __launch_bounds__(256, 4) void k_stage_c(DecodeArgs a) {
+    constexpr int LPR = 8;
     extern __shared__ __align__(16) unsigned char lds[];
-    const int lane = threadIdx.x;
-    const int tiles = a.d / TILE_ROWS;
+    const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
+    const int tiles = a.d >> 3;
     const int t = blockIdx.x / tiles, tile = blockIdx.x - t * tiles;
-    const int row0 = tile * TILE_ROWS, H = a.f >> 5;
+    const int row0 = tile * 8, K = a.f, H = K >> 5, G = K >> 6;
+    float *part = reinterpret_cast<float *>(lds);                  // [4][8]
+    uint32_t *lsb = reinterpret_cast<uint32_t *>(part + 32);       // [4 waves][2][8*G]
+    unsigned char *hst = reinterpret_cast<unsigned char *>(lsb + 8 * 8 * G);
+    const int hsb = hst_bytes(K);
     int lo, hi;
     if (a.gemv_slot) {
-        if (a.gemv_token) {           // first pair with token >= t, and > t
+        if (a.gemv_token) {   // pairs are grouped by token: binary search
             int l0 = 0, h0 = a.P;
-            while (l0 < h0) { const int m = (l0 + h0) >> 1; if (a.gemv_token[m] < t) l0 = m + 1; else h0 = m; }
+            while (l0 < h0) { const int mid = (l0 + h0) >> 1; if (a.gemv_token[mid] < t) l0 = mid + 1; else h0 = mid; }
             lo = l0;
             h0 = a.P;
-            while (l0 < h0) { const int m = (l0 + h0) >> 1; if (a.gemv_token[m] <= t) l0 = m + 1; else h0 = m; }
+            while (l0 < h0) { const int mid = (l0 + h0) >> 1; if (a.gemv_token[mid] <= t) l0 = mid + 1; else h0 = mid; }
             hi = l0;
         } else {
             lo = t; hi = t + 1;
@@ -455,44 +730,54 @@ __global__ __launch_bounds__(64) void k_stage_c(DecodeArgs a) {
         lo = t * a.k; hi = lo + a.k;
     }
     float acc = 0.f;
-    for (int p0 = lo; p0 < hi; p0 += a.kcb) {
-        const int np = min(a.kcb, hi - p0);
-        if (p0 != lo) __syncthreads();
-        for (int i = 0; i < np; ++i) {
-            const int p = p0 + i;
-            const float c = a.gemv_slot ? (a.gemv_coef ? a.gemv_coef[p] : 1.f) : a.weights[p];
-            uint4 *hp, *lp; float *xs;
-            h_stage_ptrs(lds, a.f, i, hp, lp, xs);
-            stage_h_f32(a.h_r + (size_t)p * a.f, c, a.f, hp, lp, xs, lane);
-        }
-        Mat g, u, dn;
-        uint4 q[J], qn[J];
-        uint32_t sb[J], sbn[J];
-        const int e0 = a.gemv_slot ? a.gemv_slot[p0] : a.ids[p0];
-        blob_mats(expert_blob(a, e0), a.d, a.f, g, u, dn);
-        load_tile<J>(dn, row0, a.f, lane, q, sb);
+    for (int p0 = lo; p0 < hi; p0 += KC_BATCH) {
+        const int np = min(KC_BATCH, hi - p0);
+        const int pa = min(p0 + w, hi - 1), pb = min(p0 + w + 4, hi - 1);
+        const bool va = w < np, vb = w + 4 < np;
+        const int ea = a.gemv_slot ? a.gemv_slot[pa] : a.ids[pa];
+        const int eb = a.gemv_slot ? a.gemv_slot[pb] : a.ids[pb];
+        if (p0 != lo) __syncthreads();   // the previous pass is done with LDS
+        HStage<(JF * 8 * 8 * 8 + 255) / 256, (JF * 8 * 8 + 255) / 256> Hs;   // 8 rows
+        hs_load(Hs, a.h_r + (size_t)p0 * 10 * H, np, K, tid);
+        Mat ga, ua, da, gb, ub, db;
+        Tile<LPR, JF> ta, tb;
+        blob_mats(expert_blob(a, ea), a.d, a.f, ga, ua, da);
+        blob_mats(expert_blob(a, eb), a.d, a.f, gb, ub, db);
+        tile_load_sb<LPR, JF>(ta, da, row0, K, lane);
+        tile_load_sb<LPR, JF>(tb, db, row0, K, lane);
+        tile_load_q<LPR, JF>(ta, da, row0, K, lane);
+        tile_load_q<LPR, JF>(tb, db, row0, K, lane);
+        hs_store(Hs, np, K, hst, tid);
+        tile_store_sb(ta, lsb + (w * 2) * 8 * G, G, lane);
+        tile_store_sb(tb, lsb + (w * 2 + 1) * 8 * G, G, lane);
         __syncthreads();
-        for (int i = 0; i < np; ++i) {
-            if (i + 1 < np) {         // issue the next expert's rows before this one's math
-                const int p = p0 + i + 1;
-                const int e = a.gemv_slot ? a.gemv_slot[p] : a.ids[p];
-                blob_mats(expert_blob(a, e), a.d, a.f, g, u, dn);
-                load_tile<J>(dn, row0, a.f, lane, qn, sbn);
-            }
-            uint4 *hp, *lp; float *xs;
-            h_stage_ptrs(lds, a.f, i, hp, lp, xs);
-            acc += tile_dot_hl<J>(q, sb, hp, lp, xs, H, lane);
-#pragma unroll
-            for (int j = 0; j < J; ++j) { q[j] = qn[j]; sb[j] = sbn[j]; }
+        if (va) {
+            const unsigned char *st = hst + (size_t)(pa - p0) * hsb;
+            acc += tile_dot<LPR, JF, true>(ta, lsb + (w * 2) * 8 * G, G,
+                                           reinterpret_cast<const uint4 *>(st),
+                                           reinterpret_cast<const uint4 *>(st + 64 * H),
+                                           reinterpret_cast<const float2 *>(st + 128 * H), H,
+                                           lane);
+        }
+        if (vb) {
+            const unsigned char *st = hst + (size_t)(pb - p0) * hsb;
+            acc += tile_dot<LPR, JF, true>(tb, lsb + (w * 2 + 1) * 8 * G, G,
+                                           reinterpret_cast<const uint4 *>(st),
+                                           reinterpret_cast<const uint4 *>(st + 64 * H),
+                                           reinterpret_cast<const float2 *>(st + 128 * H), H,
+                                           lane);
         }
     }
-    acc = row8_sum(acc);
-    if ((lane & 7) == 0) {
-        const size_t o = (size_t)t * a.d + row0 + (lane >> 3);
+    acc = row_sum<LPR>(acc);
+    if ((lane & 7) == 0) part[w * 8 + (lane >> 3)] = acc;
+    __syncthreads();
+    if (tid < 8) {
+        const float sum = ((part[tid] + part[8 + tid]) + part[16 + tid]) + part[24 + tid];
+        const size_t o = (size_t)t * a.d + row0 + tid;
         if (a.gemv_slot) {
-            a.y32[o] = a.y32[o] + acc;
+            a.y32[o] = a.y32[o] + sum;
         } else {
-            const float y = a.y_s[o] + acc;
+            const float y = a.y_s[o] + sum;
             if (a.y32) a.y32[o] = y;
             a.y[o] = f2h(y);
         }
@@ -505,55 +790,125 @@ __global__ __launch_bounds__(256) void k_zero(uint32_t *p, size_t n) {
         p[i] = 0;
 }
 
-template <int J>
-hipError_t launch_abc(const DecodeArgs &a, int which, hipStream_t s) {
+// LDS bytes of each stage (mirrors the device layouts above).
+int lds_a(const DecodeArgs &a, int lpr) {
+    const int d = a.d, NC = d >> 4, rpw = 64 / lpr;
+    int r = 0;
+    if (a.a_router_blocks) {
+        const int route = 8 * d + 8 * NC + 16;
+        const int topk = 8 * (a.E + 2) + 8 * 16 + 4 * 16 + 4 * 256;
+        const int group = a.do_group ? 4 * 4 * 256 : 0;
+        r = max(route, max(topk, group));
+    }
+    int s = 0;
+    if (a.a_shared_blocks)
+        s = 4 * 4 * rpw * MAX_TB + 4 * 2 * rpw * MAX_TB + 4 * 4 * rpw * (d >> 6) +
+            a.tbx * xst_bytes(d);
+    return max(r, s);
+}
+
+int lds_b(const DecodeArgs &a, int lpr) {
+    const int d = a.d, rpw = 64 / lpr;
+    int r = 0, s = 0;
+    if (a.b_routed_blocks)
+        r = 4 * 4 * rpw * MAX_TB + 4 * 2 * rpw * MAX_TB + 4 * 4 * rpw * (d >> 6) +
+            a.tbx * xst_bytes(d);
+    if (a.b_shared_blocks) s = 4 * 4 * rpw * (a.fs >> 6) + a.tbh * hst_bytes(a.fs);
+    return max(r, s);
+}
+
+int lds_c(const DecodeArgs &a) {
+    return 4 * 32 + 4 * 8 * 8 * (a.f >> 6) + KC_BATCH * hst_bytes(a.f);
+}
+
+template <int LPR, int J>
+hipError_t launch_ab(const DecodeArgs &a, int which, hipStream_t s) {
     if (which & STAGE_A) {
-        const int n = a.a_router_waves + a.a_shared_waves;
-        if (n) {
-            // router x staging, then (reusing it) top-k and grouping scratch
-            const int lds_r = max(max(8 * a.d + 8 * (a.d >> 4), 8 * a.E + 4 * 16),
-                                  a.do_group ? 8 * a.T * a.k : 0);
-            const int lds_s = a.a_shared_waves ? a.tbx * x_stage_bytes(a.d) : 0;
-            hipLaunchKernelGGL(k_stage_a<J>, dim3(n), dim3(64), max(lds_r, lds_s), s, a);
-        }
+        const int n = a.a_router_blocks + a.a_shared_blocks;
+        if (n)
+            TF_LAUNCH(TF_KERNEL_ROUTER_SHARED_GATEUP, (k_stage_a<LPR, J>), dim3(n), dim3(WG),
+                      lds_a(a, LPR), s, a);
     }
     if (which & STAGE_B) {
-        const int n = a.b_routed_waves + a.b_shared_waves;
-        if (n) {
-            const int lds_r = a.b_routed_waves ? a.tbx * x_stage_bytes(a.d) : 0;
-            const int lds_s = a.b_shared_waves ? a.tbh * h_stage_bytes(a.fs) : 0;
-            hipLaunchKernelGGL(k_stage_b<J>, dim3(n), dim3(64), max(lds_r, lds_s), s, a);
-        }
-    }
-    if (which & STAGE_C) {
-        const int n = a.T * (a.d / TILE_ROWS);
-        if (n) {
-            const int lds = a.kcb * h_stage_bytes(a.f);
-            hipLaunchKernelGGL(k_stage_c<J>, dim3(n), dim3(64), lds, s, a);
-        }
+        const int n = a.b_routed_blocks + a.b_shared_blocks;
+        if (n)
+            TF_LAUNCH(TF_KERNEL_ROUTED_GATEUP_SHARED_DOWN, (k_stage_b<LPR, J>), dim3(n), dim3(WG),
+                      lds_b(a, LPR), s, a);
     }
     return hipGetLastError();
 }
 
+template <int JF>
+hipError_t launch_c(const DecodeArgs &a, hipStream_t s) {
+    const int n = a.T * (a.d >> 3);
+    if (n) TF_LAUNCH(TF_KERNEL_DOWN_COMBINE, k_stage_c<JF>, dim3(n), dim3(WG), lds_c(a), s, a);
+    return hipGetLastError();
+}
+
+thread_local int g_prof_kernel = 0;
+thread_local hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
+
 }  // namespace
 
-// J = chunks per lane = ceil(K / 256) for the largest K among d, f, fs.
-hipError_t tf_launch_decode(const DecodeArgs &a, int which, hipStream_t s) {
-    int K = a.d;
-    if (a.f > K) K = a.f;
-    if (a.fs > K) K = a.fs;
-    const int J = (K + 255) / 256;
-    switch (J) {
-        case 1: return launch_abc<1>(a, which, s);
-        case 2: return launch_abc<2>(a, which, s);
-        case 3: return launch_abc<3>(a, which, s);
-        case 4: return launch_abc<4>(a, which, s);
-        case 5: case 6: return launch_abc<6>(a, which, s);
-        case 7: case 8: return launch_abc<8>(a, which, s);
-        case 9: case 10: case 11: return launch_abc<11>(a, which, s);
-        case 12: return launch_abc<12>(a, which, s);
-        default: return launch_abc<16>(a, which, s);
+#define TF_J_SWITCH(J, CALL)                         \
+    switch (J) {                                     \
+        case 1: CALL(1); break;                      \
+        case 2: CALL(2); break;                      \
+        case 3: CALL(3); break;                      \
+        case 4: CALL(4); break;                      \
+        case 5: case 6: CALL(6); break;              \
+        case 7: case 8: CALL(8); break;              \
+        case 9: case 10: case 11: CALL(11); break;   \
+        case 12: CALL(12); break;                    \
+        default: CALL(16); break;                    \
     }
+
+void tf_arm_profile(int kernel, hipEvent_t start, hipEvent_t stop) {
+    g_prof_kernel = kernel;
+    g_prof_start = start;
+    g_prof_stop = stop;
+}
+
+bool tf_take_profile(int kernel, hipEvent_t *start, hipEvent_t *stop) {
+    if (!g_prof_kernel || g_prof_kernel != kernel) return false;
+    *start = g_prof_start;
+    *stop = g_prof_stop;
+    g_prof_kernel = 0;
+    return true;
+}
+
+// Stages A/B: 16 lanes per row when every K they read has an even number of
+// 64-groups (so 4 rows of scales fill whole 16-byte loads), else 8;
+// J = 16-byte chunks per lane = ceil(K / (32 * LPR)) for the larger K.
+// Stage C: 8 lanes per row, J = ceil(d_ff / 256).
+int tf_decode_lpr(const DecodeArgs &a) {
+    return ((a.d >> 6) % 2 == 0 && (a.fs >> 6) % 2 == 0) ? 16 : 8;
+}
+
+hipError_t tf_launch_decode(const DecodeArgs &a, int which, hipStream_t s) {
+    hipError_t e = hipSuccess;
+    if (which & (STAGE_A | STAGE_B)) {
+        const int K = a.d > a.fs ? a.d : a.fs;
+        if (tf_decode_lpr(a) == 16) {
+            const int J = (K + 511) / 512;
+#define TF_CALL_AB(JJ) e = launch_ab<16, JJ>(a, which, s)
+            TF_J_SWITCH(J, TF_CALL_AB)
+#undef TF_CALL_AB
+        } else {
+            const int J = (K + 255) / 256;
+#define TF_CALL_AB(JJ) e = launch_ab<8, JJ>(a, which, s)
+            TF_J_SWITCH(J, TF_CALL_AB)
+#undef TF_CALL_AB
+        }
+        if (e != hipSuccess) return e;
+    }
+    if (which & STAGE_C) {
+        const int J = (a.f + 255) / 256;
+#define TF_CALL_C(JJ) e = launch_c<JJ>(a, s)
+        TF_J_SWITCH(J, TF_CALL_C)
+#undef TF_CALL_C
+    }
+    return e;
 }
 
 hipError_t tf_launch_zero(void *p, size_t bytes, hipStream_t s) {

@@ -3,21 +3,22 @@
 // Arithmetic form of the quantised dot product.  A weight is
 // w = s*q + b with q a 4-bit code and (s, b) the fp16 scale and bias of its
 // group of 64 (shilu.ai README translation, "概览": MLX affine 4-bit, group
-// 64).  Over one half-group of 32 elements
-//     sum_i w_i x_i = s * sum_i q_i x_i + b * sum_i x_i .
-// The nibbles are turned into fp16 values 1024+q with one AND-OR against the
-// exponent pattern 0x6400 (1024.0 has an ulp of 1, so the 4-bit code lands
-// exactly in the low mantissa bits), two codes per 32-bit register, and fed
-// to v_dot2_f32_f16 against fp16 pairs of x.  That yields
-//     D = sum_i (1024 + q_i) x_i = sum_i q_i x_i + 1024 X,
-// so the half-group contributes  s*D + (b - 1024 s) * X  with X = sum_i x_i
-// precomputed once per token.  Products are exact in fp32 (11 x 11 bits);
-// only the fp32 sums round.
+// 64).  Over a half-group of 32 elements
+//     sum_i w_i x_i = s * sum_i q_i x_i + b * X,      X = sum_i x_i .
+// Codes become fp16 values with one AND-OR against the exponent pattern
+// 0x6400 (1024.0, whose ulp is 1): an even element (low nibble) lands as
+// 1024+q, an odd element (high nibble, left where it is) as 1024+16q.  Two
+// codes share a 32-bit register and go through v_dot2_f32_f16 against fp16
+// pairs of the activation, the even ones into De and the odd ones into Do:
+//     De + Do/16 = sum_i q_i x_i + C,   C = 1024 X_even + 64 X_odd,
+// so the half-group contributes  s * (De - C + Do/16) + b * X, with X and C
+// computed once per activation row.  Every product is exact in fp32 (11-bit
+// by 11-bit significands); only the fp32 sums round.
 //
 // Register pairing.  One 32-bit word of codes holds elements e0..e7 (low
-// nibble first).  Masking with 0x000F000F after shifts of 0/4/8/12 gives the
-// pairs (e0,e4) (e1,e5) (e2,e6) (e3,e7); the activation is staged in LDS in
-// the same pairing, so no shuffle is needed in the inner loop.
+// nibble first).  Masks 0x000F000F / 0x00F000F0 on the word and on the word
+// shifted right by 8 give the pairs (e0,e4) (e1,e5) (e2,e6) (e3,e7); the
+// activation is staged in the same pairing.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -27,16 +28,14 @@ namespace tfk {
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 
 constexpr int WAVE = 64;
-constexpr int TILE_ROWS = 8;      // rows per wave tile
-constexpr int LANES_PER_ROW = 8;  // lanes cooperating on one row
-constexpr int MAX_J = 16;         // half-group chunks per lane (K <= 4096)
+constexpr uint32_t M_LO = 0x000F000Fu, M_HI = 0x00F000F0u, MAGIC = 0x64006400u;
 
 __device__ __forceinline__ float h2f(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
 }
 
 __device__ __forceinline__ uint16_t f2h(float f) {
-    return __builtin_bit_cast(uint16_t, (_Float16)f);   // v_cvt_f16_f32, RNE
+    return __builtin_bit_cast(uint16_t, (_Float16)f);   // v_cvt_f16_f32, round to nearest even
 }
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
@@ -44,36 +43,88 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                   c, false);
 }
 
-// D = sum over the 32 codes of one 16-byte chunk of (1024+q) * x, with the
-// activation pairs xp[m] (m = 0..3) staged for the four code words.
-__device__ __forceinline__ float q4_chunk_dot(const uint4 q, const uint4 *xp0, const uint4 *xp1,
-                                              const uint4 *xp2, const uint4 *xp3, float acc) {
+// The nibble unpack is an ordered asm statement: it keeps each chunk's
+// unpack (and so its dot products) in place instead of letting the
+// scheduler sink all dot products to the end of the unrolled loop (which
+// keeps every unpacked word live and spills), and it gets v_and_or_b32 with
+// the masks in registers (VOP3 cannot take the literals directly).
+__device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t m, uint32_t c) {
+    uint32_t r;
+    asm volatile("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "v"(m), "s"(c));
+    return r;
+}
+
+// acc += a.lo * b.lo + a.hi * b.hi  (fp16 pairs, fp32 accumulate).  Always
+// the compiler builtin, never asm: the compiler must see the dot product to
+// insert the wait states it needs after a VALU write of its operands.
+__device__ __forceinline__ float dot2c(uint32_t a, uint32_t b, float acc) {
+    return dot2(a, b, acc);
+}
+
+// Materialise a value here (an empty ordered asm): pins the computations
+// feeding it before every later ordered asm statement.
+__device__ __forceinline__ void pin(float &a, float &b) { asm volatile("" : "+v"(a), "+v"(b)); }
+
+// One 16-byte chunk (32 codes of one half-group) against activation pair
+// words X[m] (m = 0..3, one uint4 per code word): accumulates De and Do.
+__device__ __forceinline__ void q4_chunk(const uint4 q, const uint4 X0, const uint4 X1,
+                                         const uint4 X2, const uint4 X3, float &de, float &dd) {
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-    const uint4 *xs[4] = {xp0, xp1, xp2, xp3};
+    const uint4 X[4] = {X0, X1, X2, X3};
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-        const uint4 X = *xs[m];
-        const uint32_t v = w[m];
-        acc = dot2((v & 0x000F000Fu) | 0x64006400u, X.x, acc);
-        acc = dot2(((v >> 4) & 0x000F000Fu) | 0x64006400u, X.y, acc);
-        acc = dot2(((v >> 8) & 0x000F000Fu) | 0x64006400u, X.z, acc);
-        acc = dot2(((v >> 12) & 0x000F000Fu) | 0x64006400u, X.w, acc);
+        const uint32_t v = w[m], v8 = v >> 8;
+        de = dot2c(and_or(v, M_LO, MAGIC), X[m].x, de);
+        dd = dot2c(and_or(v, M_HI, MAGIC), X[m].y, dd);
+        de = dot2c(and_or(v8, M_LO, MAGIC), X[m].z, de);
+        dd = dot2c(and_or(v8, M_HI, MAGIC), X[m].w, dd);
+        pin(de, dd);
     }
-    return acc;
 }
 
-// Sum over the 8 lanes of a row group (lanes 8r..8r+7).
+// DPP lane moves (row = 16 lanes).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                 CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+    const long long b = __builtin_bit_cast(long long, v);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(b & 0xFFFFFFFF), CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned)lo);
+}
+constexpr int DPP_XOR1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141;  // lane i <-> 7-i within 8
+constexpr int DPP_MIRROR = 0x140;       // lane i <-> 15-i within 16
+
+// Sum over the 8 lanes of a row group (lanes 8r..8r+7); every lane of the
+// group gets the sum.
 __device__ __forceinline__ float row8_sum(float v) {
-    v += __shfl_xor(v, 1);
-    v += __shfl_xor(v, 2);
-    v += __shfl_xor(v, 4);
+    v += dpp_f<DPP_XOR1>(v);
+    v += dpp_f<DPP_XOR2>(v);
+    v += dpp_f<DPP_HALF_MIRROR>(v);
     return v;
 }
 
+// Sum over the whole wave in fp64, returned in every lane (fixed order:
+// within rows of 16 by DPP, then rows 0+1 and 2+3, then the two halves).
 __device__ __forceinline__ double wave_sum_f64(double v) {
+    v += dpp_d<DPP_XOR1>(v);
+    v += dpp_d<DPP_XOR2>(v);
+    v += dpp_d<DPP_HALF_MIRROR>(v);
+    v += dpp_d<DPP_MIRROR>(v);
+    const long long b = __builtin_bit_cast(long long, v);
+    double r[4];
 #pragma unroll
-    for (int o = 1; o < WAVE; o <<= 1) v += __shfl_xor(v, o);
-    return v;
+    for (int i = 0; i < 4; ++i) {
+        const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFF), 16 * i);
+        const int hi = __builtin_amdgcn_readlane((int)(b >> 32), 16 * i);
+        r[i] = __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned)lo);
+    }
+    return (r[0] + r[1]) + (r[2] + r[3]);
 }
 
 // Pair eight fp16 values (four words, low half first) as (e0,e4) (e1,e5)
@@ -89,73 +140,6 @@ __device__ __forceinline__ uint4 pair_halves(uint4 v) {
 
 __device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
     return (uint32_t)f2h(lo) | ((uint32_t)f2h(hi) << 16);
-}
-
-// Stage one fp16 activation row x[K] into LDS:
-//   xp[(m*H + hg)]  (uint4) : the four pair words for code word m of half-group hg
-//   xs[hg]          (float) : X = sum of the 32 values of half-group hg
-// H = K/32.  All 64 lanes must call (shuffles inside).
-__device__ __forceinline__ void stage_x_f16(const uint16_t *__restrict__ x, int K, uint4 *xp,
-                                            float *xs, int lane) {
-    const int H = K >> 5, NB = K >> 3;
-    const uint4 *xv = reinterpret_cast<const uint4 *>(x);
-    for (int b0 = 0; b0 < NB; b0 += WAVE) {
-        const int b = b0 + lane;
-        const bool ok = b < NB;
-        uint4 v = ok ? xv[b] : make_uint4(0, 0, 0, 0);
-        float s = 0.f;
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            s += h2f((uint16_t)(w[i] & 0xFFFF)) + h2f((uint16_t)(w[i] >> 16));
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        if (ok) {
-            const int hg = b >> 2, m = b & 3;
-            xp[m * H + hg] = pair_halves(v);
-            if (m == 0) xs[hg] = s;
-        }
-    }
-}
-
-// Stage one fp32 activation row h[K] scaled by c as a hi/lo pair of fp16 rows
-// (h*c = hi + lo + O(2^-22 |h*c|)) in the same pairing, plus
-// xs[hg] = sum over the half-group of (float)hi + (float)lo.
-__device__ __forceinline__ void stage_h_f32(const float *__restrict__ h, float c, int K,
-                                            uint4 *hp, uint4 *lp, float *xs, int lane) {
-    const int H = K >> 5, NB = K >> 3;
-    const float4 *hv = reinterpret_cast<const float4 *>(h);
-    for (int b0 = 0; b0 < NB; b0 += WAVE) {
-        const int b = b0 + lane;
-        const bool ok = b < NB;
-        float e[8];
-        if (ok) {
-            const float4 a = hv[2 * b], d = hv[2 * b + 1];
-            e[0] = a.x; e[1] = a.y; e[2] = a.z; e[3] = a.w;
-            e[4] = d.x; e[5] = d.y; e[6] = d.z; e[7] = d.w;
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) e[i] = 0.f;
-        }
-        float hi[8], lo[8], s = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float v = e[i] * c;
-            hi[i] = (float)(_Float16)v;
-            lo[i] = (float)(_Float16)(v - hi[i]);
-            s += hi[i] + lo[i];
-        }
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        if (ok) {
-            const int hg = b >> 2, m = b & 3;
-            hp[m * H + hg] = make_uint4(pack_h2(hi[0], hi[4]), pack_h2(hi[1], hi[5]),
-                                        pack_h2(hi[2], hi[6]), pack_h2(hi[3], hi[7]));
-            lp[m * H + hg] = make_uint4(pack_h2(lo[0], lo[4]), pack_h2(lo[1], lo[5]),
-                                        pack_h2(lo[2], lo[6]), pack_h2(lo[3], lo[7]));
-            if (m == 0) xs[hg] = s;
-        }
-    }
 }
 
 __device__ __forceinline__ float gelu_f(float z, int tanh_form) {

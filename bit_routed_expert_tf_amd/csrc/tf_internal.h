@@ -1,5 +1,6 @@
 // Internal interface between the C ABI (tf_api.cpp) and the kernel files.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -11,6 +12,9 @@
 enum { HDR_FLAGS = 0, HDR_NITEMS = 1, HDR_TICKET = 2 };
 enum { STAGE_A = 1, STAGE_B = 2, STAGE_C = 4 };
 constexpr int KC_BATCH = 8;       // pairs staged per pass in the down/combine kernel
+
+// Bytes of one hidden row of K values in the global hi/lo layout.
+__host__ __device__ constexpr size_t h_row_bytes(int K) { return (size_t)160 * (K >> 5); }
 constexpr int MAX_DECODE_T = 16;  // tokens per decode step
 constexpr int MAX_TB = 4;         // tokens per expert work item
 
@@ -22,7 +26,7 @@ struct DecodeArgs {
     const uint8_t *shared_blob;
     const uint8_t *pool;
     size_t stride;
-    const int16_t *slot_map;     // expert -> slot (NULL: slot = expert)
+    const int32_t *slot_map;     // expert -> slot (NULL: slot = expert)
     const int32_t *forced;       // NULL or [T][k]
     int32_t *ids;
     float *weights;
@@ -32,11 +36,17 @@ struct DecodeArgs {
     uint32_t *hdr;
     int32_t *items;              // [T*k][4] = expert, begin, count, 0
     int32_t *pairs;              // [T*k] pair index t*k+r sorted by (expert, t, r)
-    float *h_s;                  // [T][fs]
+    // hidden activations as hi/lo fp16 pair rows (9*K/32 uint4 per row, see
+    // tf_decode.hip): shared [T][fs], routed [T*k][f] (or [P][f])
+    uint4 *h_s;
     float *y_s;                  // [T][d]
-    float *h_r;                  // [T*k][f] (or [P][f])
-    int a_router_waves, a_shared_waves, b_routed_waves, b_shared_waves;
-    int tbx, tbh, kcb;           // tokens per x-staged item, per h-staged item, pairs per C pass
+    uint4 *h_r;
+    // grid partition (256-thread workgroups): stage A = router blocks (four
+    // router rows each, per token) then shared gate/up blocks (16 rows, per
+    // token sub-batch); stage B = routed gate/up blocks (16 rows of one expert
+    // item) then shared down blocks (32 rows, per token sub-batch)
+    int a_router_blocks, a_shared_blocks, b_routed_blocks, b_shared_blocks;
+    int tbx, tbh;                // tokens per x-staged item / per h-staged shared-down block
     int topk, do_group;
     // standalone GEMV mode (gemv_slot != NULL): pairs instead of routed items
     const int32_t *gemv_slot, *gemv_token;
@@ -45,4 +55,22 @@ struct DecodeArgs {
 };
 
 hipError_t tf_launch_decode(const DecodeArgs &a, int which, hipStream_t s);
+// Lanes per weight row used by stages A and B for these shapes (8 or 16).
+int tf_decode_lpr(const DecodeArgs &a);
+
+// One-shot kernel timer (tf_profile_kernel): take_profile(kernel, &start, &stop)
+// returns true once for the armed kernel id and disarms it.
+void tf_arm_profile(int kernel, hipEvent_t start, hipEvent_t stop);
+bool tf_take_profile(int kernel, hipEvent_t *start, hipEvent_t *stop);
+
+// Launch through hipExtLaunchKernelGGL with the armed events when `kernel` is
+// armed, plain hipLaunchKernelGGL otherwise.
+#define TF_LAUNCH(kernel_id, fn, grid, block, lds, stream, ...)                            \
+    do {                                                                                   \
+        hipEvent_t ev0_, ev1_;                                                             \
+        if (tf_take_profile(kernel_id, &ev0_, &ev1_))                                      \
+            hipExtLaunchKernelGGL(fn, grid, block, lds, stream, ev0_, ev1_, 0, __VA_ARGS__); \
+        else                                                                               \
+            hipLaunchKernelGGL(fn, grid, block, lds, stream, __VA_ARGS__);                 \
+    } while (0)
 hipError_t tf_launch_zero(void *p, size_t bytes, hipStream_t s);

@@ -29,7 +29,7 @@
 struct SlotDev {
     int L, E, S, k;
     int64_t trace_cap;
-    int16_t *slot_of;          // [L][E]  -1 = not cached
+    int32_t *slot_of;          // [L][E]  -1 = not cached
     int16_t *expert_of;        // [L][S]  -1 = empty
     uint32_t *count;           // [L][S]
     uint32_t *last;            // [L][S]  last-use token
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(64) void k_lookup(SlotDev c, int layer, const int32
                                                int n, int32_t *slots_out, uint32_t *flags) {
     if (threadIdx.x != 0) return;
     const int S = c.S, E = c.E;
-    int16_t *slot_of = c.slot_of + (size_t)layer * E;
+    int32_t *slot_of = c.slot_of + (size_t)layer * E;
     int16_t *expert_of = c.expert_of + (size_t)layer * S;
     uint32_t *count = c.count + (size_t)layer * S;
     uint32_t *last = c.last + (size_t)layer * S;
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(64) void k_lookup(SlotDev c, int layer, const int32
             slot_of[expert_of[v]] = -1;
         }
         expert_of[v] = (int16_t)e;
-        slot_of[e] = (int16_t)v;
+        slot_of[e] = v;
         count[v] = 1;
         last[v] = t;
         pinned |= 1u << v;
@@ -157,7 +157,7 @@ tf_status tf_slot_check_layer(const tf_slot_cache *c, const tf_moe_layer *L, int
 }
 
 hipEvent_t tf_slot_fill_event(tf_slot_cache *c) { return c->ev_fill; }
-const int16_t *tf_slot_map(const tf_slot_cache *c, int32_t layer) {
+const int32_t *tf_slot_map(const tf_slot_cache *c, int32_t layer) {
     return c->d.slot_of + (size_t)layer * c->d.E;
 }
 const uint8_t *tf_slot_pool(const tf_slot_cache *c, int32_t layer) {
@@ -165,8 +165,10 @@ const uint8_t *tf_slot_pool(const tf_slot_cache *c, int32_t layer) {
 }
 
 static tf_status reset_tables(tf_slot_cache *c) {
-    const size_t n16 = (size_t)c->d.L * c->d.E + (size_t)c->d.L * c->d.S;   // slot_of + expert_of
-    hipLaunchKernelGGL(k_fill16, dim3(256), dim3(256), 0, 0, c->d.slot_of, n16, (int16_t)-1);
+    // slot_of (int32) and expert_of (int16) to -1: both are all-ones bit patterns
+    const size_t n16 = 2 * (size_t)c->d.L * c->d.E + (size_t)c->d.L * c->d.S;
+    hipLaunchKernelGGL(k_fill16, dim3(256), dim3(256), 0, 0,
+                       reinterpret_cast<int16_t *>(c->d.slot_of), n16, (int16_t)-1);
     hipError_t e = hipGetLastError();
     const size_t zbytes = (size_t)c->d.L * c->d.S * 8 + (size_t)c->d.L * 4;   // count, last, tok
     if (e == hipSuccess) e = tf_launch_zero(c->d.count, (zbytes + 3) & ~size_t(3), 0);
@@ -205,7 +207,7 @@ tf_status tf_slot_cache_create(int32_t n_layers, int32_t n_experts, int32_t n_sl
     c->stride = blob_stride; c->slot_pool = slot_pool; c->host_pool = host_pool_pinned;
     c->d.trace_cap = trace_cap;
     const size_t o_slot_of = 0;
-    const size_t o_expert_of = o_slot_of + 2 * (size_t)n_layers * n_experts;
+    const size_t o_expert_of = o_slot_of + 4 * (size_t)n_layers * n_experts;
     const size_t o_count = up256(o_expert_of + 2 * (size_t)n_layers * n_slots);
     const size_t o_last = o_count + 4 * (size_t)n_layers * n_slots;
     const size_t o_tok = o_last + 4 * (size_t)n_layers * n_slots;
@@ -216,7 +218,7 @@ tf_status tf_slot_cache_create(int32_t n_layers, int32_t n_experts, int32_t n_sl
     hipError_t e = hipMalloc(&c->dev, total);
     if (e != hipSuccess) { delete c; return fail(TF_E_NOMEM, "device tables: %s", hipGetErrorString(e)); }
     char *b = static_cast<char *>(c->dev);
-    c->d.slot_of = reinterpret_cast<int16_t *>(b + o_slot_of);
+    c->d.slot_of = reinterpret_cast<int32_t *>(b + o_slot_of);
     c->d.expert_of = reinterpret_cast<int16_t *>(b + o_expert_of);
     c->d.count = reinterpret_cast<uint32_t *>(b + o_count);
     c->d.last = reinterpret_cast<uint32_t *>(b + o_last);

@@ -171,6 +171,20 @@ tf_status tf_moe_prefill_chunk(const tf_moe_layer *L, const uint16_t *x, int32_t
                                uint16_t *y, float *y32, int32_t *ids, float *weights,
                                hipStream_t s, void *ws, size_t ws_bytes);
 
+/* ------------------------------------------------------------ profiling */
+/* Kernel ids of the hot path (for tf_profile_kernel). */
+enum {
+    TF_KERNEL_ROUTER_SHARED_GATEUP = 1,      /* decode A: router + top-k + shared gate/up */
+    TF_KERNEL_ROUTED_GATEUP_SHARED_DOWN = 2, /* decode B: routed gate/up + shared down    */
+    TF_KERNEL_DOWN_COMBINE = 4               /* decode C: routed down + combine -> y      */
+};
+/* Arm a one-shot timer: the next launch, by this host thread, of the named
+ * kernel goes through hipExtLaunchKernel with `start` recorded when the
+ * kernel begins and `stop` when it ends, on the stream it runs on.  Events
+ * must be created with timing enabled; hipEventElapsedTime(start, stop) is
+ * then the kernel's own duration.  Pass kernel 0 to disarm. */
+tf_status tf_profile_kernel(int32_t kernel, hipEvent_t start, hipEvent_t stop);
+
 /* ------------------------------------------------------------ slot cache */
 /* Per-layer LFU expert cache in HBM (shilu.ai README translation,
  * "推理引擎的工作原理"; sh.edu-sjtu.cn, "三件事").  Policy: a slot's count is

@@ -1,0 +1,122 @@
+"""Slot-cache path on the GPU: LFU lookup, miss fill, cached decode.
+
+Bars: the hit/slot sequence of every layer equals the oracle's LFU replay
+bitwise; a cached decode step is bitwise identical to the same step with all
+experts resident (the kernels read the same bytes from another pool); sampled
+tokens match the fp64 oracle within the floored 2e-3; the bytes copied equal
+misses x blob stride.  Every layer of a token consumes that token's x, and
+routing is forced by per-layer Zipf(1.1) popularity.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import check_token
+from synth import gen
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tfa():
+    import bit_routed_expert_tf_amd as m
+    from bit_routed_expert_tf_amd import api
+    m.load()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    return api
+
+
+def _stack(api, seed, L, d, E, k, f, fs):
+    """Per-layer router/shared on the device, the expert pool pinned on the
+    host ([L][E][stride]) and the same pool resident on the device."""
+    stride = (gen.blob_bytes(d, f) + 255) // 256 * 256
+    host = api.pinned_host(L * E * stride)
+    hv = host.numpy().reshape(L, E, stride)
+    layers = []
+    for l in range(L):
+        gen.expert_pool(seed, l, d, f, E, stride=stride, out=hv[l])
+        layers.append({"router": gen.router(seed, l, d, E),
+                       "shared_blob": gen.shared_blob(seed, l, d, fs), "pool": hv[l],
+                       "d_model": d, "d_ff": f, "d_ff_shared": fs, "top_k": k})
+    resident = host.cuda().view(L, E, stride)
+    dls = [api.DeviceLayer.from_arrays(Ld["router"], Ld["shared_blob"], resident[l], d, f, fs, k)
+           for l, Ld in enumerate(layers)]
+    return stride, host, layers, dls
+
+
+def _run(api, seed, L, d, E, k, f, fs, S, T, check_tokens):
+    stride, host, layers, dls = _stack(api, seed, L, d, E, k, f, fs)
+    ids = np.stack([gen.zipf_ids(seed, l, T, E, k) for l in range(L)])      # [L][T][k]
+    x = gen.tokens(seed, T, d)
+    slot_pool = torch.empty(L * S * stride, dtype=torch.uint8, device="cuda")
+    cache = api.SlotCache(L, E, S, k, stride, slot_pool, host, trace_cap=T)
+    copy = torch.cuda.Stream()
+    xt = torch.from_numpy(x.view(np.int16)).cuda()
+    ft = torch.from_numpy(ids).cuda()
+    ws = api.workspace(api.tf_moe_workspace_bytes(dls[0], 1))
+    ws_r = api.workspace(api.tf_moe_workspace_bytes(dls[0], 1))
+    y_c = torch.empty((L, T, d), dtype=torch.float16, device="cuda")
+    y_r = torch.empty_like(y_c)
+    id_c = torch.empty((L, T, k), dtype=torch.int32, device="cuda")
+    w_c = torch.empty((L, T, k), dtype=torch.float32, device="cuda")
+    id_r, w_r = torch.empty_like(id_c), torch.empty_like(w_c)
+    for t in range(T):
+        for l in range(L):
+            api.tf_moe_layer_fwd(dls[l], xt[t:t + 1], forced_ids=ft[l, t:t + 1], y=y_c[l, t:t + 1],
+                                 ids=id_c[l, t:t + 1], weights=w_c[l, t:t + 1], cache=cache,
+                                 layer_idx=l, ws=ws, copy_stream=copy)
+            api.tf_moe_layer_fwd(dls[l], xt[t:t + 1], forced_ids=ft[l, t:t + 1], y=y_r[l, t:t + 1],
+                                 ids=id_r[l, t:t + 1], weights=w_r[l, t:t + 1], ws=ws_r)
+    torch.cuda.synchronize()
+    assert api.tf_workspace_flags(ws) == 0 and api.tf_workspace_flags(ws_r) == 0
+    assert np.array_equal(id_c.cpu().numpy(), ids)
+    assert torch.equal(y_c.view(torch.int16), y_r.view(torch.int16)), "cached != resident"
+    assert torch.equal(w_c, w_r)
+    misses = 0
+    for l in range(L):
+        hit, slot = cache.trace(l, T * k)
+        h_ref, s_ref, _, _ = oracle.lfu_replay(ids[l], S, E)
+        assert np.array_equal(hit.reshape(T, k), h_ref), f"layer {l}: hit sequence"
+        assert np.array_equal(slot.reshape(T, k), s_ref), f"layer {l}: slot sequence"
+        misses += int((~h_ref).sum())
+    assert cache.bytes_filled() == misses * stride
+    yc = y_c.cpu().view(torch.int16).numpy().view(np.float16)
+    for l in range(L):
+        ref = oracle.moe_tokens(layers[l], x[check_tokens], ids[l][check_tokens])
+        for i, t in enumerate(check_tokens):
+            check_token(yc[l, t], ref["y"][i])
+    # reset replays the same sequence from an empty cache
+    cache.reset()
+    for t in range(min(T, 8)):
+        api.tf_moe_layer_fwd(dls[0], xt[t:t + 1], forced_ids=ft[0, t:t + 1], y=y_c[0, t:t + 1],
+                             ids=id_c[0, t:t + 1], weights=w_c[0, t:t + 1], cache=cache,
+                             layer_idx=0, ws=ws, copy_stream=copy)
+    torch.cuda.synchronize()
+    hit, slot = cache.trace(0, T * k)
+    h_ref, s_ref, _, _ = oracle.lfu_replay(ids[0][:min(T, 8)], S, E)
+    assert np.array_equal(hit.reshape(-1, k), h_ref) and np.array_equal(slot.reshape(-1, k), s_ref)
+    assert torch.equal(y_c[0, :min(T, 8)].view(torch.int16), y_r[0, :min(T, 8)].view(torch.int16))
+    cache.close()
+    return misses / (L * T * k)
+
+
+def test_slot_cache_small_stack(tfa):
+    print("slot cache: d=256 E=32 k=4 f=128 fs=256 S=8 L=3 T=96", flush=True)
+    miss = _run(tfa, 2, L=3, d=256, E=32, k=4, f=128, fs=256, S=8, T=96, check_tokens=[0, 41, 95])
+    assert 0.0 < miss < 1.0
+
+
+def test_slot_cache_ragged_shapes(tfa):
+    print("slot cache: d=320 E=12 k=3 f=192 fs=320 S=5 L=2 T=40", flush=True)
+    _run(tfa, 5, L=2, d=320, E=12, k=3, f=192, fs=320, S=5, T=40, check_tokens=[0, 39])
+
+
+def test_slot_cache_full_width(tfa):
+    # the slot-cache workload's shapes (d=2816, 128 experts, top-8, 16 slots)
+    # on two layers and 48 tokens
+    print("slot cache: d=2816 E=128 k=8 f=704 fs=2816 S=16 L=2 T=48", flush=True)
+    miss = _run(tfa, 2, L=2, d=2816, E=128, k=8, f=704, fs=2816, S=16, T=48,
+                check_tokens=[0, 47])
+    assert 0.2 < miss < 0.9

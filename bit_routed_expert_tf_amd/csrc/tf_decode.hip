@@ -320,19 +320,35 @@ __device__ __forceinline__ void hs_produce(uint4 *dst, int K, int blk, const flo
 
 // ------------------------------------------------------------------ top-k
 // Top-k of token t by (logit desc, id asc) -- or the forced ids -- and the
-// softmax in fp64 over the k selected logits (max-subtracted).  Whole WG.
+// softmax over the k selected logits (max-subtracted differences in fp64,
+// exponentials in fp32, normalised in fp64).  Whole WG.
+//
+// Rank of candidate i = #{j : l_j > l_i or (l_j == l_i and j < i)}.  It is
+// counted on fp32 copies of the logits: rounding to fp32 is monotone, so
+// f_j > f_i implies l_j > l_i, and only candidates whose fp32 key another
+// candidate shares need the exact fp64 comparison (a second, rare pass).
+// Two threads per candidate, each over one half of the j range, four keys
+// per LDS read.
+__host__ __device__ constexpr int topk_lds_bytes(int E) {
+    return 8 * (E + 2) + 8 * 16 + 4 * 16 + 4 * 256 + 4 * (E + 8);
+}
+
 __device__ void topk_block(const DecodeArgs &a, int t, int tid, unsigned char *lds) {
     double *l = reinterpret_cast<double *>(lds);            // [E] (+1 pad)
     double *ex = l + ((a.E + 2) & ~1);                       // [16]
     int *sel = reinterpret_cast<int *>(ex + 16);             // [16]
     int *part = sel + 16;                                    // [256]
+    float *lf = reinterpret_cast<float *>(part + 256);       // [E + 8], -inf padded
     __syncthreads();
-    for (int i = tid; i < a.E; i += WG) {
-        const double v = __hip_atomic_load(a.logits + (size_t)t * a.E + i, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-        l[i] = (v != v) ? -__builtin_inf() : v;   // NaN ranks last
+    for (int i = tid; i < a.E + 8; i += WG) {
+        double v = -__builtin_inf();
+        if (i < a.E) {
+            v = ld_dev(a.logits + (size_t)t * a.E + i);
+            if (v != v) v = -__builtin_inf();   // NaN ranks last
+            l[i] = v;
+        }
+        lf[i] = (float)v;
     }
-    if (tid == 0) l[a.E] = -__builtin_inf();     // pad for the pairwise reads
     __syncthreads();
     if (a.forced) {
         uint32_t fl = 0;
@@ -347,28 +363,33 @@ __device__ void topk_block(const DecodeArgs &a, int t, int tid, unsigned char *l
                 if (sel[r] == sel[tid]) fl |= TF_FLAG_ID_REPEAT;
         if (fl) atomicOr(a.hdr + HDR_FLAGS, fl);
     } else {
-        // rank of candidate i = #{j : l_j > l_i or (l_j == l_i and j < i)};
-        // two threads per candidate, each over one half of the j range,
-        // reading the logits two at a time
         const int half = tid >> 7;
-        const int E2 = ((a.E + 3) >> 2) << 1;   // even split point
-        const int jb = half * E2, je = min(a.E, jb + E2);
+        const int E2 = ((a.E + 7) >> 3) << 2;   // half range, a multiple of 4
+        const int jb = half * E2;
         for (int base = 0; base < a.E; base += 128) {
             const int i = base + (tid & 127);
-            int cnt = 0;
+            int gt = 0, eq = 0;
             if (i < a.E) {
-                const double li = l[i];
+                const float fi = lf[i];
+                const float4 *q = reinterpret_cast<const float4 *>(lf + jb);
 #pragma unroll 4
-                for (int j = jb; j < je; j += 2) {
-                    const double2 v = *reinterpret_cast<const double2 *>(l + j);
-                    cnt += (v.x > li) | ((v.x == li) & (j < i));
-                    cnt += (j + 1 < je) & ((v.y > li) | ((v.y == li) & (j + 1 < i)));
+                for (int j = 0; j < E2 / 4; ++j) {
+                    const float4 v = q[j];
+                    gt += (v.x > fi) + (v.y > fi) + (v.z > fi) + (v.w > fi);
+                    eq += (v.x == fi) + (v.y == fi) + (v.z == fi) + (v.w == fi);
                 }
             }
-            part[tid] = cnt;
+            part[tid] = gt | (eq << 16);
             __syncthreads();
             if (tid < 128 && i < a.E) {
-                const int c = part[tid] + part[tid + 128];
+                const int p0 = part[tid], p1 = part[tid + 128];
+                int c = (p0 & 0xFFFF) + (p1 & 0xFFFF);
+                if ((p0 >> 16) + (p1 >> 16) > 1) {   // fp32 key shared: exact order
+                    const double li = l[i];
+                    const float fi = lf[i];
+                    for (int j = 0; j < a.E; ++j)
+                        if (j != i && lf[j] == fi) c += (l[j] > li) | ((l[j] == li) & (j < i));
+                }
                 if (c < a.k) sel[c] = i;
             }
             __syncthreads();
@@ -378,14 +399,14 @@ __device__ void topk_block(const DecodeArgs &a, int t, int tid, unsigned char *l
     if (tid < a.k) {
         double m = l[sel[0]];
         for (int r = 1; r < a.k; ++r) m = fmax(m, l[sel[r]]);
-        ex[tid] = exp(l[sel[tid]] - m);
+        ex[tid] = (double)expf((float)(l[sel[tid]] - m));
     }
     __syncthreads();
     if (tid < a.k) {
         double s = 0.0;
         for (int r = 0; r < a.k; ++r) s += ex[r];
-        a.ids[(size_t)t * a.k + tid] = sel[tid];
-        a.weights[(size_t)t * a.k + tid] = (float)(ex[tid] / s);
+        st_dev(a.ids + (size_t)t * a.k + tid, (int32_t)sel[tid]);
+        st_dev(a.weights + (size_t)t * a.k + tid, (float)(ex[tid] / s));
     }
 }
 
@@ -500,10 +521,8 @@ __device__ void router_block(const DecodeArgs &a, int b, int tid, unsigned char 
                   fma((double)h2f((uint16_t)(sw >> 16)), x16[c], acc));
     }
     acc = wave_sum_f64(acc);
-    if (lane == 0 && row_ok) {
-        a.logits[(size_t)t * a.E + e] = acc;
-        __threadfence();
-    }
+    if (lane == 0 && row_ok) st_dev(a.logits + (size_t)t * a.E + e, acc);
+    stores_done();
     __syncthreads();
     if (tid == 0) {
         const uint32_t old = atomicAdd(a.hdr + HDR_TICKET + t, 1u);
@@ -511,11 +530,10 @@ __device__ void router_block(const DecodeArgs &a, int b, int tid, unsigned char 
     }
     __syncthreads();
     if (!*flag) return;
-    __threadfence();
-    if (tid == 0) a.hdr[HDR_TICKET + t] = 0;
+    if (tid == 0) st_dev(a.hdr + HDR_TICKET + t, 0u);
     topk_block(a, t, tid, lds);
     if (!a.do_group || a.T == 1) return;
-    __threadfence();
+    stores_done();
     __syncthreads();
     if (tid == 0) {
         const uint32_t old = atomicAdd(a.hdr + HDR_TICKET + a.T, 1u);
@@ -523,8 +541,7 @@ __device__ void router_block(const DecodeArgs &a, int b, int tid, unsigned char 
     }
     __syncthreads();
     if (!reinterpret_cast<int *>(lds)[0]) return;
-    __threadfence();
-    if (tid == 0) a.hdr[HDR_TICKET + a.T] = 0;
+    if (tid == 0) st_dev(a.hdr + HDR_TICKET + a.T, 0u);
     group_block(a, tid, lds);
 }
 
@@ -796,7 +813,7 @@ int lds_a(const DecodeArgs &a, int lpr) {
     int r = 0;
     if (a.a_router_blocks) {
         const int route = 8 * d + 8 * NC + 16;
-        const int topk = 8 * (a.E + 2) + 8 * 16 + 4 * 16 + 4 * 256;
+        const int topk = topk_lds_bytes(a.E);
         const int group = a.do_group ? 4 * 4 * 256 : 0;
         r = max(route, max(topk, group));
     }

@@ -82,6 +82,25 @@ __device__ __forceinline__ void q4_chunk(const uint4 q, const uint4 X0, const ui
     }
 }
 
+// Device-coherent accesses (agent-scope relaxed atomics: coherent across the
+// XCDs' L2 caches).  Data one workgroup writes and another workgroup of the
+// same launch reads goes through these; the writer waits for its stores
+// (stores_done) before it takes a ticket, so the hand-off needs no
+// cache-wide write-back or invalidation.
+template <typename T>
+__device__ __forceinline__ T ld_dev(const T *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ void st_dev(T *p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// This thread's stores have completed; also a compiler barrier for memory
+// operations.
+__device__ __forceinline__ void stores_done() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+}
 // DPP lane moves (row = 16 lanes).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {

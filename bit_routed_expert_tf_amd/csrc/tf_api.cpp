@@ -71,7 +71,7 @@ struct WsLayout {
 WsLayout decode_layout(int d, int f, int fs, int E, int k, int T) {
     WsLayout w{};
     size_t o = 0;
-    w.hdr = o; o += 256;
+    w.hdr = o; o += up256((size_t)4 * (HDR_TICKET + T + 1) > 256 ? (size_t)4 * (HDR_TICKET + T + 1) : 256);
     w.logits = o; o += up256((size_t)8 * T * E);
     w.items = o; o += up256((size_t)16 * T * k);
     w.pairs = o; o += up256((size_t)4 * T * k);
@@ -261,7 +261,8 @@ tf_status tf_moe_layer_fwd(const tf_moe_layer *L, const uint16_t *x, int32_t T,
     a.y_s = at<float>(ws, w.ys);
     a.h_r = at<uint4>(ws, w.hr);
     a.do_group = 1;
-    const int max_items = T == 1 ? a.k : T * a.k;
+    // T == 1: one item per rank; else one item per selected expert
+    const int max_items = T == 1 ? a.k : (T * a.k < a.E ? T * a.k : a.E);
     const int n_router = ((a.E + 3) / 4) * T;
     // rows per workgroup: gate/up 2*RPW, shared down 4*RPW (RPW = 64 / lanes per row)
     const int rpw = 64 / tf_decode_lpr(a);
@@ -312,29 +313,58 @@ extern "C" {
 
 size_t tf_prefill_workspace_bytes(const tf_moe_layer *L, int32_t T) {
     if (!L || T <= 0) return 0;
-    const int Tb = T < MAX_DECODE_T ? T : MAX_DECODE_T;
-    return decode_layout(L->d_model, L->d_ff, L->d_ff_shared, L->n_experts, L->top_k, Tb).total;
+    const WsLayout w = decode_layout(L->d_model, L->d_ff, L->d_ff_shared, L->n_experts, L->top_k, T);
+    return w.total + up256((size_t)4 * T * L->top_k * L->d_model);
 }
 
-// Chunked prefill: the chunk runs as decode steps of up to 16 tokens each;
-// inside a step the (token, rank) pairs are grouped by expert.
+// Chunked prefill (shilu.ai README translation, "推理引擎的工作原理": chunks
+// of at most 128 tokens, so each fetched expert serves several rows).  The
+// chunk's (token, rank) pairs are grouped by expert and every expert's
+// weights are read once:
+//   A  router rows + top-k per token, grouping; shared gate/up (16 tokens
+//      per block, the weight tile reused across them)
+//   B  routed gate/up per expert item (all its tokens); shared down (8
+//      tokens per block)
+//   C  routed down per expert item -> y_e per pair
+//   D  y = y_s + sum over ranks of y_e, fp16
 tf_status tf_moe_prefill_chunk(const tf_moe_layer *L, const uint16_t *x, int32_t T, uint16_t *y,
                                float *y32, int32_t *ids, float *weights, hipStream_t s, void *ws,
                                size_t ws_bytes) {
-    if (T < 0 || T > 128) return fail(TF_E_ARG, "T must be in [0, 128]");
+    if (T < 0 || T > MAX_PREFILL_T) return fail(TF_E_ARG, "T must be in [0, %d]", MAX_PREFILL_T);
     if (T == 0) return TF_OK;
     tf_status st = check_layer(L);
     if (st) return st;
     if (!x || !y || !ids || !weights || !ws) return fail(TF_E_ARG, "NULL x/y/ids/weights/ws");
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, 256) || (y32 && !aligned(y32, 16)))
+        return fail(TF_E_ALIGN, "x/y/y32 16-byte, ws 256-byte alignment");
     if (ws_bytes < tf_prefill_workspace_bytes(L, T)) return fail(TF_E_NOMEM, "workspace too small");
-    const size_t d = L->d_model, k = L->top_k;
-    for (int t0 = 0; t0 < T; t0 += MAX_DECODE_T) {
-        const int n = T - t0 < MAX_DECODE_T ? T - t0 : MAX_DECODE_T;
-        st = tf_moe_layer_fwd(L, x + t0 * d, n, nullptr, y + t0 * d, y32 ? y32 + t0 * d : nullptr,
-                              ids + t0 * k, weights + t0 * k, nullptr, 0, s, s, ws, ws_bytes);
-        if (st) return st;
-    }
-    return TF_OK;
+    if (T == 1)   // a single token is a decode step
+        return tf_moe_layer_fwd(L, x, 1, nullptr, y, y32, ids, weights, nullptr, 0, s, s, ws,
+                                ws_bytes);
+    const WsLayout w = decode_layout(L->d_model, L->d_ff, L->d_ff_shared, L->n_experts, L->top_k, T);
+    DecodeArgs a;
+    fill_common(a, L, T);
+    a.x = x; a.ids = ids; a.weights = weights; a.y = y; a.y32 = y32;
+    a.hdr = at<uint32_t>(ws, w.hdr);
+    a.logits = at<double>(ws, w.logits);
+    a.items = at<int32_t>(ws, w.items);
+    a.pairs = at<int32_t>(ws, w.pairs);
+    a.h_s = at<uint4>(ws, w.hs);
+    a.y_s = at<float>(ws, w.ys);
+    a.h_r = at<uint4>(ws, w.hr);
+    a.y_e = at<float>(ws, w.total);
+    a.do_group = 1;
+    a.tbx = T < 16 ? T : 16;
+    a.tbh = T < 8 ? T : 8;
+    const int rpw = 64 / tf_decode_lpr(a);
+    const int max_items = T * a.k < a.E ? T * a.k : a.E;
+    a.a_router_blocks = ((a.E + 3) / 4) * T;
+    a.a_shared_blocks = (a.fs / (2 * rpw)) * ((T + a.tbx - 1) / a.tbx);
+    a.b_routed_blocks = (a.f / (2 * rpw)) * max_items;
+    a.b_shared_blocks = (a.d / (4 * rpw)) * ((T + a.tbh - 1) / a.tbh);
+    hipError_t e = tf_launch_decode(a, STAGE_A | STAGE_B, s);
+    if (e == hipSuccess) e = tf_launch_prefill_tail(a, max_items, s);
+    return e == hipSuccess ? TF_OK : hip_fail(e, "prefill launch");
 }
 
 }  // extern "C"

@@ -410,48 +410,77 @@ __device__ void topk_block(const DecodeArgs &a, int t, int tid, unsigned char *l
     }
 }
 
-// Group the T*k (token, rank) pairs by expert: sorted by (expert, token,
-// rank); an item is at most a.tbx consecutive pairs of one expert.  Whole WG.
+// Group the T*k (token, rank) pairs by expert, sorted by (expert, token,
+// rank): one item per selected expert, [expert, first sorted position,
+// count, 0] (shilu.ai README translation, "推理引擎的工作原理": a chunk's
+// rows share each fetched expert).  Token t's pair with expert e lands at
+// offs[e] + #{t' < t that selected e}, counted on a per-expert bit mask over
+// the tokens (T <= 128), so the order never depends on thread timing.
+// Positions start out holding their own index, so repeated ids (flagged by
+// the top-k) can never leave an out-of-range pair behind.  Whole WG.
+__host__ __device__ constexpr int group_lds_bytes(int E, int T) {
+    return 4 * E * ((T + 31) >> 5) + 12 * E + 8 * 4;
+}
+
 __device__ void group_block(const DecodeArgs &a, int tid, unsigned char *lds) {
-    const int P = a.T * a.k;   // <= 256
-    int *pid = reinterpret_cast<int *>(lds);
-    int *sorted = pid + 256;
-    int *start = sorted + 256;
-    int *end = start + 256;    // one past the last sorted position of the expert
+    const int P = a.T * a.k, E = a.E, NW = (a.T + 31) >> 5;
+    const int lane = tid & 63, w = tid >> 6;
+    uint32_t *mask = reinterpret_cast<uint32_t *>(lds);       // [E][NW]
+    int *cnt = reinterpret_cast<int *>(mask + E * NW);        // [E]
+    int *offs = cnt + E;                                      // [E]
+    int *iidx = offs + E;                                     // [E] item index
+    int *wsum = iidx + E;                                     // [4][2]
     __syncthreads();
-    if (tid < P)
-        pid[tid] = (int)__hip_atomic_load(reinterpret_cast<const uint32_t *>(a.ids) + tid,
-                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = tid; i < E * NW; i += WG) mask[i] = 0;
+    for (int p = tid; p < P; p += WG) st_dev(a.pairs + p, (int32_t)p);
     __syncthreads();
-    if (tid < P) {
-        const int e = pid[tid];
-        int less = 0, same = 0, before = 0;
-        for (int q = 0; q < P; ++q) {
-            const int eq = pid[q];
-            less += eq < e;
-            same += eq == e;
-            before += (eq == e) & (q < tid);
-        }
-        const int pos = less + before;
-        sorted[pos] = tid;
-        start[pos] = (before % a.tbx) == 0;
-        end[pos] = less + same;
+    for (int p = tid; p < P; p += WG) {
+        const int e = min(max((int)ld_dev(a.ids + p), 0), E - 1);
+        const int t = p / a.k;
+        atomicOr(&mask[e * NW + (t >> 5)], 1u << (t & 31));
     }
     __syncthreads();
-    if (tid < P && start[tid]) {
-        int idx = 0;
-        for (int q = 0; q < tid; ++q) idx += start[q];
-        int *it = a.items + 4 * idx;
-        it[0] = pid[sorted[tid]];
-        it[1] = tid;
-        it[2] = min(a.tbx, end[tid] - tid);
-        it[3] = 0;
+    // counts, and exclusive scans of the counts and of (count > 0); thread
+    // tid owns experts [tid*per, tid*per + per)
+    const int per = (E + WG - 1) / WG, e0 = tid * per, e1 = min(E, e0 + per);
+    int sc = 0, sn = 0;
+    for (int e = e0; e < e1; ++e) {
+        int c = 0;
+        for (int q = 0; q < NW; ++q) c += __popc(mask[e * NW + q]);
+        cnt[e] = c;
+        sc += c;
+        sn += c > 0;
     }
-    if (tid < P) a.pairs[tid] = sorted[tid];
-    if (tid == 0) {
-        int n = 0;
-        for (int q = 0; q < P; ++q) n += start[q];
-        a.hdr[HDR_NITEMS] = (uint32_t)n;
+    int ic = sc, in = sn;
+    for (int o = 1; o < WAVE; o <<= 1) {
+        const int vc = __shfl_up(ic, o), vn = __shfl_up(in, o);
+        if (lane >= o) { ic += vc; in += vn; }
+    }
+    if (lane == WAVE - 1) { wsum[2 * w] = ic; wsum[2 * w + 1] = in; }
+    __syncthreads();
+    int oc = ic - sc, on = in - sn;
+    for (int q = 0; q < w; ++q) { oc += wsum[2 * q]; on += wsum[2 * q + 1]; }
+    for (int e = e0; e < e1; ++e) {
+        offs[e] = oc;
+        iidx[e] = on;
+        oc += cnt[e];
+        on += cnt[e] > 0;
+    }
+    if (tid == WG - 1) st_dev(a.hdr + HDR_NITEMS, (uint32_t)on);
+    __syncthreads();
+    for (int e = tid; e < E; e += WG)
+        if (cnt[e])
+            st_dev(reinterpret_cast<uint4 *>(a.items + 4 * iidx[e]),
+                   make_uint4((uint32_t)e, (uint32_t)offs[e], (uint32_t)cnt[e], 0u));
+    stores_done();
+    __syncthreads();   // the default positions are written before the scatter
+    for (int p = tid; p < P; p += WG) {
+        const int e = min(max((int)ld_dev(a.ids + p), 0), E - 1);
+        const int t = p / a.k;
+        int r = __popc(mask[e * NW + (t >> 5)] & ((1u << (t & 31)) - 1u));
+        for (int q = 0; q < (t >> 5); ++q) r += __popc(mask[e * NW + q]);
+        const int pos = offs[e] + r;
+        if (pos < P) st_dev(a.pairs + pos, (int32_t)p);
     }
 }
 
@@ -546,12 +575,14 @@ __device__ void router_block(const DecodeArgs &a, int b, int tid, unsigned char 
 }
 
 // ------------------------------------------------------- gate/up block
-// 2*RPW output rows of (gate, up) for up to MAX_TB tokens: waves 0/1 gate
-// rows [0, RPW) / [RPW, 2 RPW), waves 2/3 the same up rows; then
-// h = coef * gelu(g) * u, written as hi/lo rows.  routed == false: the shared
-// expert, token sub-batch b / tiles -> h_s; routed == true: expert item
-// b / tiles -> h_r[pair].
-template <int LPR, int J, bool routed>
+// 2*RPW output rows of (gate, up): waves 0/1 gate rows [0, RPW) / [RPW,
+// 2 RPW), waves 2/3 the same up rows; h = coef * gelu(g) * u, written as
+// hi/lo rows.  routed == false: the shared expert for tokens
+// [b / tiles * tbx, +tbx) -> h_s; routed == true: expert item b / tiles ->
+// h_r[pair].  The weight tile is loaded once and stays in registers while
+// the item's tokens pass through in groups of MAX_TB (MULTI: more than one
+// pass may be needed; otherwise an item has at most MAX_TB tokens).
+template <int LPR, int J, bool routed, bool MULTI>
 __device__ void gateup_block(const DecodeArgs &a, int b, int tid, unsigned char *lds) {
     constexpr int RPW = WAVE / LPR, RWG = 2 * RPW;
     const int lane = tid & 63, w = uniform(tid >> 6);
@@ -564,100 +595,129 @@ __device__ void gateup_block(const DecodeArgs &a, int b, int tid, unsigned char 
     uint32_t *lsb = reinterpret_cast<uint32_t *>(hv + RWG * MAX_TB); // [4][RPW*G]
     unsigned char *xst = reinterpret_cast<unsigned char *>(lsb + 4 * RPW * G);
 
-    int nt, e = 0;
-    int prow[MAX_TB] = {0, 0, 0, 0};   // output row of token slot i (token or pair)
-    float coef[MAX_TB] = {1.f, 1.f, 1.f, 1.f};
-    const uint16_t *rp[4];
+    // the item: expert e and nt token slots; slot i -> x row, output row, coef
+    // (mode 0: shared, tokens base + i; 1: a single slot; 2: item pairs)
+    int nt, e = 0, base = 0, mode, row1 = 0, xrow1 = 0;
+    float coef1 = 1.f;
     if (!routed) {
-        const int t0 = item * a.tbx;
-        nt = min(a.tbx, a.T - t0);
-#pragma unroll
-        for (int i = 0; i < MAX_TB; ++i) {
-            prow[i] = t0 + min(i, nt - 1);
-            rp[i] = a.x + (size_t)prow[i] * d;
-        }
+        base = item * a.tbx;
+        nt = min(a.tbx, a.T - base);
+        mode = 0;
     } else if (a.gemv_slot) {
         if (item >= a.P) return;
         nt = 1;
+        mode = 1;
         e = a.gemv_slot[item];
-        prow[0] = item;
-        coef[0] = a.gemv_coef ? a.gemv_coef[item] : 1.f;
-        const int tok = a.gemv_token ? a.gemv_token[item] : item;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) rp[i] = a.x + (size_t)tok * d;
+        row1 = item;
+        coef1 = a.gemv_coef ? a.gemv_coef[item] : 1.f;
+        xrow1 = a.gemv_token ? a.gemv_token[item] : item;
     } else if (a.T == 1) {
         if (item >= a.k) return;
         nt = 1;
-        e = a.ids[item];
-        prow[0] = item;
-        coef[0] = a.weights[item];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) rp[i] = a.x;
+        mode = 1;
+        e = ld_dev(a.ids + item);
+        row1 = item;
+        coef1 = ld_dev(a.weights + item);
     } else {
-        if (item >= (int)a.hdr[HDR_NITEMS]) return;
-        const int *it = a.items + 4 * item;
-        e = it[0];
-        nt = it[2];
+        if (item >= (int)ld_dev(a.hdr + HDR_NITEMS)) return;
+        const uint4 it = ld_dev(reinterpret_cast<const uint4 *>(a.items + 4 * item));
+        e = (int)it.x;
+        base = (int)it.y;
+        nt = (int)it.z;
+        mode = 2;
+    }
+    int prow[MAX_TB];
+    float coef[MAX_TB];
+    const uint16_t *rp[4];
+    auto rows = [&](int s0, int ns) {
 #pragma unroll
         for (int i = 0; i < MAX_TB; ++i) {
-            const int p = a.pairs[it[1] + min(i, nt - 1)];
-            prow[i] = p;
-            coef[i] = a.weights[p];
-            rp[i] = a.x + (size_t)(p / a.k) * d;
+            const int si = s0 + min(i, ns - 1);
+            int xr = xrow1, orow = row1;
+            float c = coef1;
+            if (mode == 0) {
+                xr = orow = base + si;
+                c = 1.f;
+            } else if (mode == 2) {
+                const int pr = ld_dev(a.pairs + base + si);
+                xr = pr / a.k;
+                orow = pr;
+                c = ld_dev(a.weights + pr);
+            }
+            prow[i] = orow;
+            coef[i] = c;
+            rp[i] = a.x + (size_t)xr * d;
         }
-    }
-    // activation loads, then weight loads, then activation processing
-    XStage<(J * LPR + 15) / 16> X;   // <= 4 rows of d/8 <= 4*J*LPR blocks over 256 threads
-    xs_load(X, rp, nt, d, tid);
+    };
     Mat g, u, dn;
     blob_mats(routed ? expert_blob(a, e) : a.shared_blob, d, F, g, u, dn);
     Tile<LPR, J> tl;
     const Mat &mm = (w >> 1) ? u : g;
     const int row0 = rb * RWG + RPW * (w & 1);
+    const int xsb = xst_bytes(d);
+    // compute one pass of ns tokens from the staged rows and write their h
+    auto finish = [&](int ns) {
+        auto one = [&](int i) {
+            const unsigned char *st = xst + (size_t)i * xsb;
+            const float v = row_sum<LPR>(tile_dot<LPR, J, false>(
+                tl, lsb + w * RPW * G, G, reinterpret_cast<const uint4 *>(st), nullptr,
+                reinterpret_cast<const float2 *>(st + 64 * H), H, lane));
+            if (lane % LPR == 0) gu[(w * RPW + lane / LPR) * MAX_TB + i] = v;
+        };
+        if (ns == 1) {
+            one(0);   // straight line: chunk j waits only for its own load
+        } else {
+            for (int i = 0; i < ns; ++i) one(i);
+        }
+        __syncthreads();
+        if (tid < RWG * ns) {
+            const int row = tid % RWG, i = tid / RWG;
+            const int half = row / RPW, rr = row % RPW;
+            const float gv = gu[(half * RPW + rr) * MAX_TB + i];
+            const float uv = gu[((2 + half) * RPW + rr) * MAX_TB + i];
+            hv[i * RWG + row] = gelu_f(gv, a.act) * uv;
+        }
+        __syncthreads();
+        if (tid < (RWG / 8) * ns) {
+            const int i = tid / (RWG / 8), sub = tid % (RWG / 8);
+            const float c = coef[0] * (i == 0) + coef[1] * (i == 1) + coef[2] * (i == 2) +
+                            coef[3] * (i == 3);
+            const int pr = i == 0 ? prow[0] : i == 1 ? prow[1] : i == 2 ? prow[2] : prow[3];
+            float ev[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) ev[q] = c * hv[i * RWG + 8 * sub + q];
+            uint4 *dst = (routed ? a.h_r : a.h_s) + (size_t)pr * (10 * (F >> 5));
+            hs_produce(dst, F, rb * (RWG / 8) + sub, ev);
+        }
+    };
+    // first pass: activation loads, then weight loads, then activation processing
+    XStage<(J * LPR + 15) / 16> X;   // <= 4 rows of d/8 <= 4*J*LPR blocks over 256 threads
+    const int ns0 = min(MAX_TB, nt);
+    rows(0, ns0);
+    xs_load(X, rp, ns0, d, tid);
     tile_load_sb<LPR, J>(tl, mm, row0, d, lane);
     tile_load_q<LPR, J>(tl, mm, row0, d, lane);
-    xs_store(X, nt, d, xst, tid);
+    xs_store(X, ns0, d, xst, tid);
     tile_store_sb(tl, lsb + w * RPW * G, G, lane);
     __syncthreads();
-    const int xsb = xst_bytes(d);
-    auto one = [&](int i) {
-        const unsigned char *st = xst + (size_t)i * xsb;
-        const float v = row_sum<LPR>(tile_dot<LPR, J, false>(
-            tl, lsb + w * RPW * G, G, reinterpret_cast<const uint4 *>(st), nullptr,
-            reinterpret_cast<const float2 *>(st + 64 * H), H, lane));
-        if (lane % LPR == 0) gu[(w * RPW + lane / LPR) * MAX_TB + i] = v;
-    };
-    if (nt == 1) {
-        one(0);   // straight line: chunk j waits only for its own load
-    } else {
-        for (int i = 0; i < nt; ++i) one(i);
-    }
-    __syncthreads();
-    if (tid < RWG * nt) {
-        const int row = tid % RWG, i = tid / RWG;
-        const int half = row / RPW, rr = row % RPW;
-        const float gv = gu[(half * RPW + rr) * MAX_TB + i];
-        const float uv = gu[((2 + half) * RPW + rr) * MAX_TB + i];
-        hv[i * RWG + row] = gelu_f(gv, a.act) * uv;
-    }
-    __syncthreads();
-    if (tid < (RWG / 8) * nt) {
-        const int i = tid / (RWG / 8), sub = tid % (RWG / 8);
-        const float c = coef[0] * (i == 0) + coef[1] * (i == 1) + coef[2] * (i == 2) +
-                        coef[3] * (i == 3);
-        const int pr = i == 0 ? prow[0] : i == 1 ? prow[1] : i == 2 ? prow[2] : prow[3];
-        float ev[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) ev[q] = c * hv[i * RWG + 8 * sub + q];
-        uint4 *dst = (routed ? a.h_r : a.h_s) + (size_t)pr * (10 * (F >> 5));
-        hs_produce(dst, F, rb * (RWG / 8) + sub, ev);
+    finish(ns0);
+    if (MULTI)
+    for (int s0 = MAX_TB; s0 < nt; s0 += MAX_TB) {   // further passes reuse the tile
+        const int ns = min(MAX_TB, nt - s0);
+        __syncthreads();
+        rows(s0, ns);
+        xs_load(X, rp, ns, d, tid);
+        xs_store(X, ns, d, xst, tid);
+        __syncthreads();
+        finish(ns);
     }
 }
 
 // --------------------------------------------------------- shared down
-// 4*RPW output rows (RPW per wave) of the shared down projection for up to
-// tbh tokens: y_s[t][row].
-template <int LPR, int J>
+// 4*RPW output rows (RPW per wave) of the shared down projection for tokens
+// [b / tiles * tbh, +tbh): y_s[t][row], one token per pass with the weight
+// tile kept in registers (MULTI: more than one token per block).
+template <int LPR, int J, bool MULTI>
 __device__ void shared_down_block(const DecodeArgs &a, int b, int tid, unsigned char *lds) {
     constexpr int RPW = WAVE / LPR;
     const int lane = tid & 63, w = uniform(tid >> 6);
@@ -668,50 +728,53 @@ __device__ void shared_down_block(const DecodeArgs &a, int b, int tid, unsigned 
     uint32_t *lsb = reinterpret_cast<uint32_t *>(lds);               // [4][RPW*G]
     unsigned char *hst = reinterpret_cast<unsigned char *>(lsb + 4 * RPW * G);
     HStage<(J * LPR + 31) / 32, (J * LPR + 255) / 256> Hs;   // 1 row: 8H copies, H sums
-    hs_load(Hs, a.h_s + (size_t)t0 * 10 * H, nt, K, tid);
+    hs_load(Hs, a.h_s + (size_t)t0 * 10 * H, 1, K, tid);
     Mat g, u, dn;
     blob_mats(a.shared_blob, a.d, a.fs, g, u, dn);
     const int row0 = rb * 4 * RPW + RPW * w;
     Tile<LPR, J> tl;
     tile_load_sb<LPR, J>(tl, dn, row0, K, lane);
     tile_load_q<LPR, J>(tl, dn, row0, K, lane);
-    hs_store(Hs, nt, K, hst, tid);
+    hs_store(Hs, 1, K, hst, tid);
     tile_store_sb(tl, lsb + w * RPW * G, G, lane);
     __syncthreads();
-    const int hsb = hst_bytes(K);
     auto one = [&](int i) {
-        const unsigned char *st = hst + (size_t)i * hsb;
         const float v = row_sum<LPR>(tile_dot<LPR, J, true>(
-            tl, lsb + w * RPW * G, G, reinterpret_cast<const uint4 *>(st),
-            reinterpret_cast<const uint4 *>(st + 64 * H),
-            reinterpret_cast<const float2 *>(st + 128 * H), H, lane));
+            tl, lsb + w * RPW * G, G, reinterpret_cast<const uint4 *>(hst),
+            reinterpret_cast<const uint4 *>(hst + 64 * H),
+            reinterpret_cast<const float2 *>(hst + 128 * H), H, lane));
         if (lane % LPR == 0) a.y_s[(size_t)(t0 + i) * a.d + row0 + lane / LPR] = v;
     };
-    if (nt == 1) {
-        one(0);
-    } else {
-        for (int i = 0; i < nt; ++i) one(i);
+    one(0);
+    if (MULTI)
+    for (int i = 1; i < nt; ++i) {
+        __syncthreads();   // the previous token is done with the staged row
+        HStage<(J * LPR + 31) / 32, (J * LPR + 255) / 256> Hn;
+        hs_load(Hn, a.h_s + (size_t)(t0 + i) * 10 * H, 1, K, tid);
+        hs_store(Hn, 1, K, hst, tid);
+        __syncthreads();
+        one(i);
     }
 }
 
-template <int LPR, int J>
-__global__ __launch_bounds__(256, 4) void k_stage_a(DecodeArgs a) {
+template <int LPR, int J, bool MULTI>
+__global__ __launch_bounds__(256, MULTI ? 2 : 4) void k_stage_a(DecodeArgs a) {
     extern __shared__ __align__(16) unsigned char lds[];
     const int b = blockIdx.x, tid = threadIdx.x;
     if (b < a.a_router_blocks)
         router_block(a, b, tid, lds);
     else
-        gateup_block<LPR, J, false>(a, b - a.a_router_blocks, tid, lds);
+        gateup_block<LPR, J, false, MULTI>(a, b - a.a_router_blocks, tid, lds);
 }
 
-template <int LPR, int J>
-__global__ __launch_bounds__(256, 4) void k_stage_b(DecodeArgs a) {
+template <int LPR, int J, bool MULTI>
+__global__ __launch_bounds__(256, MULTI ? 2 : 4) void k_stage_b(DecodeArgs a) {
     extern __shared__ __align__(16) unsigned char lds[];
     const int b = blockIdx.x, tid = threadIdx.x;
     if (b < a.b_routed_blocks)
-        gateup_block<LPR, J, true>(a, b, tid, lds);
+        gateup_block<LPR, J, true, MULTI>(a, b, tid, lds);
     else
-        shared_down_block<LPR, J>(a, b - a.b_routed_blocks, tid, lds);
+        shared_down_block<LPR, J, MULTI>(a, b - a.b_routed_blocks, tid, lds);
 }
 
 // ---------------------------------------------- routed down + combine
@@ -801,6 +864,65 @@ __global__ __launch_bounds__(256, 4) void k_stage_c(DecodeArgs a) {
     }
 }
 
+// ------------------------------------------------- prefill: down, combine
+// Routed down projection per expert item (prefill chunks): 32 output rows
+// (8 lanes per row, 8 rows per wave) of the item's W_down, applied to each
+// of its pairs in turn with the weight tile kept in registers:
+// y_e[pair][row] (fp32, the coefficient is already in h).
+template <int JF>
+__global__ __launch_bounds__(256, 4) void k_pf_down(DecodeArgs a) {
+    constexpr int LPR = 8, RPW = 8;
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
+    const int tiles = a.d >> 5;
+    const int item = blockIdx.x / tiles, rb = blockIdx.x - item * tiles;
+    if (item >= (int)ld_dev(a.hdr + HDR_NITEMS)) return;
+    const uint4 it = ld_dev(reinterpret_cast<const uint4 *>(a.items + 4 * item));
+    const int e = (int)it.x, base = (int)it.y, nt = (int)it.z;
+    const int K = a.f, H = K >> 5, G = K >> 6;
+    uint32_t *lsb = reinterpret_cast<uint32_t *>(lds);               // [4][RPW*G]
+    unsigned char *hst = reinterpret_cast<unsigned char *>(lsb + 4 * RPW * G);
+    HStage<(JF * LPR + 31) / 32, (JF * LPR + 255) / 256> Hs;   // 1 row
+    int pr = ld_dev(a.pairs + base);
+    hs_load(Hs, a.h_r + (size_t)pr * 10 * H, 1, K, tid);
+    Mat g, u, dn;
+    blob_mats(expert_blob(a, e), a.d, a.f, g, u, dn);
+    const int row0 = rb * 32 + RPW * w;
+    Tile<LPR, JF> tl;
+    tile_load_sb<LPR, JF>(tl, dn, row0, K, lane);
+    tile_load_q<LPR, JF>(tl, dn, row0, K, lane);
+    hs_store(Hs, 1, K, hst, tid);
+    tile_store_sb(tl, lsb + w * RPW * G, G, lane);
+    __syncthreads();
+    for (int i = 0; i < nt; ++i) {
+        if (i) {
+            __syncthreads();
+            pr = ld_dev(a.pairs + base + i);
+            hs_load(Hs, a.h_r + (size_t)pr * 10 * H, 1, K, tid);
+            hs_store(Hs, 1, K, hst, tid);
+            __syncthreads();
+        }
+        const float v = row_sum<LPR>(tile_dot<LPR, JF, true>(
+            tl, lsb + w * RPW * G, G, reinterpret_cast<const uint4 *>(hst),
+            reinterpret_cast<const uint4 *>(hst + 64 * H),
+            reinterpret_cast<const float2 *>(hst + 128 * H), H, lane));
+        if (lane % LPR == 0) a.y_e[(size_t)pr * a.d + row0 + lane / LPR] = v;
+    }
+}
+
+// Combine: y[t] = y_s[t] + sum over ranks r of y_e[t*k + r], in rank order,
+// then fp16 round to nearest even (and the fp32 value when asked).
+__global__ __launch_bounds__(256) void k_pf_combine(DecodeArgs a) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (size_t)a.T * a.d) return;
+    const size_t t = i / a.d, c = i - t * a.d;
+    float s = 0.f;
+    for (int r = 0; r < a.k; ++r) s += a.y_e[(t * a.k + r) * a.d + c];
+    const float y = a.y_s[i] + s;
+    if (a.y32) a.y32[i] = y;
+    a.y[i] = f2h(y);
+}
+
 __global__ __launch_bounds__(256) void k_zero(uint32_t *p, size_t n) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
          i += (size_t)gridDim.x * blockDim.x)
@@ -808,29 +930,31 @@ __global__ __launch_bounds__(256) void k_zero(uint32_t *p, size_t n) {
 }
 
 // LDS bytes of each stage (mirrors the device layouts above).
+int gateup_lds(const DecodeArgs &a, int lpr, int rows) {
+    const int rpw = 64 / lpr;
+    return 4 * 4 * rpw * MAX_TB + 4 * 2 * rpw * MAX_TB + 4 * 4 * rpw * (a.d >> 6) +
+           rows * xst_bytes(a.d);
+}
+
 int lds_a(const DecodeArgs &a, int lpr) {
-    const int d = a.d, NC = d >> 4, rpw = 64 / lpr;
+    const int d = a.d, NC = d >> 4;
     int r = 0;
     if (a.a_router_blocks) {
         const int route = 8 * d + 8 * NC + 16;
         const int topk = topk_lds_bytes(a.E);
-        const int group = a.do_group ? 4 * 4 * 256 : 0;
+        const int group = a.do_group ? group_lds_bytes(a.E, a.T) : 0;
         r = max(route, max(topk, group));
     }
     int s = 0;
-    if (a.a_shared_blocks)
-        s = 4 * 4 * rpw * MAX_TB + 4 * 2 * rpw * MAX_TB + 4 * 4 * rpw * (d >> 6) +
-            a.tbx * xst_bytes(d);
+    if (a.a_shared_blocks) s = gateup_lds(a, lpr, min(a.tbx, MAX_TB));
     return max(r, s);
 }
 
 int lds_b(const DecodeArgs &a, int lpr) {
-    const int d = a.d, rpw = 64 / lpr;
+    const int rpw = 64 / lpr;
     int r = 0, s = 0;
-    if (a.b_routed_blocks)
-        r = 4 * 4 * rpw * MAX_TB + 4 * 2 * rpw * MAX_TB + 4 * 4 * rpw * (d >> 6) +
-            a.tbx * xst_bytes(d);
-    if (a.b_shared_blocks) s = 4 * 4 * rpw * (a.fs >> 6) + a.tbh * hst_bytes(a.fs);
+    if (a.b_routed_blocks) r = gateup_lds(a, lpr, a.T > 1 && !a.gemv_slot ? MAX_TB : 1);
+    if (a.b_shared_blocks) s = 4 * 4 * rpw * (a.fs >> 6) + hst_bytes(a.fs);
     return max(r, s);
 }
 
@@ -842,15 +966,27 @@ template <int LPR, int J>
 hipError_t launch_ab(const DecodeArgs &a, int which, hipStream_t s) {
     if (which & STAGE_A) {
         const int n = a.a_router_blocks + a.a_shared_blocks;
-        if (n)
-            TF_LAUNCH(TF_KERNEL_ROUTER_SHARED_GATEUP, (k_stage_a<LPR, J>), dim3(n), dim3(WG),
-                      lds_a(a, LPR), s, a);
+        if (n) {
+            if (a.tbx > MAX_TB)
+                TF_LAUNCH(TF_KERNEL_ROUTER_SHARED_GATEUP, (k_stage_a<LPR, J, true>), dim3(n),
+                          dim3(WG), lds_a(a, LPR), s, a);
+            else
+                TF_LAUNCH(TF_KERNEL_ROUTER_SHARED_GATEUP, (k_stage_a<LPR, J, false>), dim3(n),
+                          dim3(WG), lds_a(a, LPR), s, a);
+        }
     }
     if (which & STAGE_B) {
         const int n = a.b_routed_blocks + a.b_shared_blocks;
-        if (n)
-            TF_LAUNCH(TF_KERNEL_ROUTED_GATEUP_SHARED_DOWN, (k_stage_b<LPR, J>), dim3(n), dim3(WG),
-                      lds_b(a, LPR), s, a);
+        if (n) {
+            // an expert item can hold more than MAX_TB tokens, or a shared-down
+            // block more than one
+            if ((a.T > MAX_TB && !a.gemv_slot) || a.tbh > 1)
+                TF_LAUNCH(TF_KERNEL_ROUTED_GATEUP_SHARED_DOWN, (k_stage_b<LPR, J, true>), dim3(n),
+                          dim3(WG), lds_b(a, LPR), s, a);
+            else
+                TF_LAUNCH(TF_KERNEL_ROUTED_GATEUP_SHARED_DOWN, (k_stage_b<LPR, J, false>), dim3(n),
+                          dim3(WG), lds_b(a, LPR), s, a);
+        }
     }
     return hipGetLastError();
 }
@@ -859,6 +995,14 @@ template <int JF>
 hipError_t launch_c(const DecodeArgs &a, hipStream_t s) {
     const int n = a.T * (a.d >> 3);
     if (n) TF_LAUNCH(TF_KERNEL_DOWN_COMBINE, k_stage_c<JF>, dim3(n), dim3(WG), lds_c(a), s, a);
+    return hipGetLastError();
+}
+
+template <int JF>
+hipError_t launch_pf_down(const DecodeArgs &a, int max_items, hipStream_t s) {
+    const int n = max_items * (a.d >> 5);
+    const int lds = 4 * 4 * 8 * (a.f >> 6) + hst_bytes(a.f);
+    if (n) hipLaunchKernelGGL(k_pf_down<JF>, dim3(n), dim3(WG), lds, s, a);
     return hipGetLastError();
 }
 
@@ -926,6 +1070,19 @@ hipError_t tf_launch_decode(const DecodeArgs &a, int which, hipStream_t s) {
 #undef TF_CALL_C
     }
     return e;
+}
+
+// Prefill tail: routed down per expert item (y_e per pair), then the combine.
+hipError_t tf_launch_prefill_tail(const DecodeArgs &a, int max_items, hipStream_t s) {
+    hipError_t e = hipSuccess;
+    const int J = (a.f + 255) / 256;
+#define TF_CALL_PF(JJ) e = launch_pf_down<JJ>(a, max_items, s)
+    TF_J_SWITCH(J, TF_CALL_PF)
+#undef TF_CALL_PF
+    if (e != hipSuccess) return e;
+    const size_t n = (size_t)a.T * a.d;
+    hipLaunchKernelGGL(k_pf_combine, dim3((unsigned)((n + 255) / 256)), dim3(WG), 0, s, a);
+    return hipGetLastError();
 }
 
 hipError_t tf_launch_zero(void *p, size_t bytes, hipStream_t s) {

@@ -16,7 +16,8 @@ constexpr int KC_BATCH = 8;       // pairs staged per pass in the down/combine k
 // Bytes of one hidden row of K values in the global hi/lo layout.
 __host__ __device__ constexpr size_t h_row_bytes(int K) { return (size_t)160 * (K >> 5); }
 constexpr int MAX_DECODE_T = 16;  // tokens per decode step
-constexpr int MAX_TB = 4;         // tokens per expert work item
+constexpr int MAX_PREFILL_T = 128;  // tokens per prefill chunk
+constexpr int MAX_TB = 4;         // tokens staged per pass of a gate/up block
 
 struct DecodeArgs {
     int d, f, fs, E, k, T, act;
@@ -34,19 +35,20 @@ struct DecodeArgs {
     uint16_t *y;
     float *y32;
     uint32_t *hdr;
-    int32_t *items;              // [T*k][4] = expert, begin, count, 0
+    int32_t *items;              // [E][4] = expert, first sorted pair, count, 0
     int32_t *pairs;              // [T*k] pair index t*k+r sorted by (expert, t, r)
     // hidden activations as hi/lo fp16 pair rows (9*K/32 uint4 per row, see
     // tf_decode.hip): shared [T][fs], routed [T*k][f] (or [P][f])
     uint4 *h_s;
     float *y_s;                  // [T][d]
     uint4 *h_r;
+    float *y_e;                  // prefill: [T*k][d] p-weighted expert outputs per pair
     // grid partition (256-thread workgroups): stage A = router blocks (four
     // router rows each, per token) then shared gate/up blocks (16 rows, per
     // token sub-batch); stage B = routed gate/up blocks (16 rows of one expert
     // item) then shared down blocks (32 rows, per token sub-batch)
     int a_router_blocks, a_shared_blocks, b_routed_blocks, b_shared_blocks;
-    int tbx, tbh;                // tokens per x-staged item / per h-staged shared-down block
+    int tbx, tbh;                // tokens per shared gate/up block / per shared-down block
     int topk, do_group;
     // standalone GEMV mode (gemv_slot != NULL): pairs instead of routed items
     const int32_t *gemv_slot, *gemv_token;
@@ -55,6 +57,9 @@ struct DecodeArgs {
 };
 
 hipError_t tf_launch_decode(const DecodeArgs &a, int which, hipStream_t s);
+// Prefill after stages A and B: routed down per expert item into y_e, then
+// y = y_s + sum over ranks of y_e -> fp16.
+hipError_t tf_launch_prefill_tail(const DecodeArgs &a, int max_items, hipStream_t s);
 // Lanes per weight row used by stages A and B for these shapes (8 or 16).
 int tf_decode_lpr(const DecodeArgs &a);
 

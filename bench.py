@@ -239,6 +239,282 @@ def cpu_baseline(args, router, shared_blob, pool, X, wl):
                       f"({dt:.1f} s, C fp64 oracle, OpenMP over rows)"}
 
 
+def _profile(lib, h, kernels, step, nprof, stream):
+    """Average durations of the named kernels (hipExtLaunchKernel start/stop
+    events on the compute stream) over nprof eager calls of step(i)."""
+    import torch
+
+    from bit_routed_expert_tf_amd import _lib
+    out = {}
+    for kid, name in kernels.items():
+        evs = [(_event(h), _event(h)) for _ in range(nprof)]
+        with torch.cuda.stream(stream):
+            for i in range(nprof):
+                _lib.check(lib.tf_profile_kernel(kid, evs[i][0], evs[i][1]))
+                step(i)
+        torch.cuda.synchronize()
+        durs = []
+        for a, b in evs:
+            v = ctypes.c_float()
+            h.hipEventElapsedTime(ctypes.byref(v), a, b)
+            durs.append(v.value * 1e3)
+            h.hipEventDestroy(a)
+            h.hipEventDestroy(b)
+        durs.sort()
+        out[name] = {"avg_us": round(sum(durs) / len(durs), 3),
+                     "median_us": round(durs[len(durs) // 2], 3), "min_us": round(durs[0], 3),
+                     "launches": len(durs)}
+    return out
+
+
+def _graphs(step, n, chunk, stream):
+    """HIP graphs of `chunk` consecutive steps each, covering steps 0..n-1."""
+    import torch
+    graphs = []
+    for j in range(0, n, chunk):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(j, min(n, j + chunk)):
+                step(i)
+        graphs.append((g, min(n, j + chunk) - j))
+    torch.cuda.synchronize()
+    return graphs
+
+
+def _replay(graphs, nsteps, stream):
+    import torch
+    done, j = 0, 0
+    with torch.cuda.stream(stream):
+        while done < nsteps:
+            g, c = graphs[j % len(graphs)]
+            g.replay()
+            done += c
+            j += 1
+    return done
+
+
+def _timed(graphs, nsteps, warmup, stream):
+    import torch
+    _replay(graphs, warmup, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    steps = _replay(graphs, nsteps, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return steps, e0.elapsed_time(e1)
+
+
+def run_prefill(args):
+    """128-token chunks through one full-width layer (natural routing)."""
+    import numpy as np
+    import torch
+
+    from bit_routed_expert_tf_amd import _lib, api
+    from synth import gen
+    wl = gen.WORKLOADS[3]
+    d, E, k, f, fs, C = wl.d_model, wl.n_experts, wl.top_k, wl.d_ff, wl.d_ff_shared, wl.chunk
+    nch = wl.n_tokens // C
+    lib = _lib.load()
+    dev = torch.device("cuda:0")
+    router = gen.router(wl.seed, 0, d, E)
+    D = api.DeviceLayer.from_arrays(router, gen.shared_blob(wl.seed, 0, d, fs),
+                                    gen.expert_pool(wl.seed, 0, d, f, E), d, f, fs, k, device=dev)
+    X = torch.from_numpy(gen.tokens(wl.seed, wl.n_tokens, d).view(np.int16)).to(dev)
+    Y = torch.empty((wl.n_tokens, d), dtype=torch.int16, device=dev)
+    IDS = torch.empty((wl.n_tokens, k), dtype=torch.int32, device=dev)
+    W = torch.empty((wl.n_tokens, k), dtype=torch.float32, device=dev)
+    ws = api.workspace(api.tf_prefill_workspace_bytes(D, C), dev)
+    stream = torch.cuda.Stream(device=dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    Lp = ctypes.byref(D.struct)
+
+    def step(i):
+        j = i % nch
+        _lib.check(lib.tf_moe_prefill_chunk(
+            Lp, ctypes.c_void_p(X.data_ptr() + 2 * d * C * j), C,
+            ctypes.c_void_p(Y.data_ptr() + 2 * d * C * j), None,
+            ctypes.c_void_p(IDS.data_ptr() + 4 * k * C * j),
+            ctypes.c_void_p(W.data_ptr() + 4 * k * C * j), sh, ctypes.c_void_p(ws.data_ptr()),
+            ws.numel()))
+
+    with torch.cuda.stream(stream):
+        step(0)
+    torch.cuda.synchronize()
+    graphs = _graphs(step, nch, nch, stream)
+    steps, ms = _timed(graphs, args.steps or nch, nch, stream)
+    ids = IDS.cpu().numpy().reshape(nch, C * k)
+    distinct = float(np.mean([len(np.unique(r)) for r in ids]))
+    qb = lambda n, kk, bits=4: n * kk * bits // 8 + 4 * n * (kk // 64)   # noqa: E731
+    blob = 2 * qb(f, d) + qb(d, f)
+    chunk_bytes = qb(E, d, 8) + 2 * qb(fs, d) + qb(d, fs) + distinct * blob + 4 * C * d
+    kern = _profile(lib, _hip(), {
+        _lib.TF_KERNEL_ROUTER_SHARED_GATEUP: "router_topk_group_shared_gateup",
+        _lib.TF_KERNEL_ROUTED_GATEUP_SHARED_DOWN: "routed_gateup_shared_down",
+        _lib.TF_KERNEL_PREFILL_DOWN: "routed_down_per_expert",
+        _lib.TF_KERNEL_PREFILL_COMBINE: "combine"}, step, min(args.prof_steps, 64), stream)
+    us = ms * 1e3 / steps
+    return {"metric": "prefill tokens/s (128-token chunks, one layer)",
+            "value": round(C * steps / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+            "steps": steps, "us_per_chunk": round(us, 2), "higher_is_better": True,
+            "data": "synthetic (seeded)", "dtype": "fp32",
+            "config": {"workload": wl.name, "chunk": C, "chunks": nch,
+                       "distinct_experts_per_chunk": distinct},
+            "chunk_bytes": int(chunk_bytes),
+            "GBps": round(chunk_bytes / (us * 1e-6) / 1e9, 1),
+            "frac_of_hbm_peak": round(chunk_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "kernels": kern}
+
+
+def run_stack(args):
+    """30 resident layers, batch 1 and 16 independent tokens per step, forced
+    uniform routing; every layer of a step consumes the step's x."""
+    import numpy as np
+    import torch
+
+    from bit_routed_expert_tf_amd import _lib, api
+    from synth import gen
+    wl = gen.WORKLOADS[4]
+    d, E, k, f, fs, L = wl.d_model, wl.n_experts, wl.top_k, wl.d_ff, wl.d_ff_shared, wl.n_layers
+    nsteps = args.steps or wl.n_tokens
+    warm = wl.extra.get("warmup_steps", 50)
+    lib = _lib.load()
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    stride = gen.blob_bytes(d, f)
+    layers = []
+    host = torch.empty((E, stride), dtype=torch.uint8, pin_memory=True)
+    for l in range(L):
+        gen.expert_pool(wl.seed, l, d, f, E, out=host.numpy(), threads=16)
+        pool = host.to(dev, non_blocking=False)
+        layers.append(api.DeviceLayer.from_arrays(gen.router(wl.seed, l, d, E),
+                                                  gen.shared_blob(wl.seed, l, d, fs), pool,
+                                                  d, f, fs, k, device=dev))
+        print(f"stack: layer {l} resident ({time.time() - t0:.0f} s)", file=sys.stderr, flush=True)
+    setup = time.time() - t0
+    res = {}
+    for B in wl.batches:
+        ntok = (nsteps + warm) * B
+        X = torch.from_numpy(gen.tokens(wl.seed, ntok, d).view(np.int16)).to(dev)
+        ids_f = np.stack([gen.uniform_ids(wl.seed, l, ntok, E, k) for l in range(L)])
+        F = torch.from_numpy(ids_f).to(dev)
+        Y = torch.empty((L, B, d), dtype=torch.int16, device=dev)
+        IDS = torch.empty((L, B, k), dtype=torch.int32, device=dev)
+        W = torch.empty((L, B, k), dtype=torch.float32, device=dev)
+        ws = api.workspace(api.tf_moe_workspace_bytes(layers[0], B), dev)
+        stream = torch.cuda.Stream(device=dev)
+        sh = ctypes.c_void_p(stream.cuda_stream)
+        Ls = [ctypes.byref(D.struct) for D in layers]
+
+        def step(i, B=B, X=X, F=F, Y=Y, IDS=IDS, W=W, ws=ws, sh=sh, Ls=Ls, ntok=ntok):
+            r0 = (i % (ntok // B)) * B
+            for l in range(L):
+                _lib.check(lib.tf_moe_layer_fwd(
+                    Ls[l], ctypes.c_void_p(X.data_ptr() + 2 * d * r0), B,
+                    ctypes.c_void_p(F.data_ptr() + 4 * k * (l * ntok + r0)),
+                    ctypes.c_void_p(Y.data_ptr() + 2 * d * B * l), None,
+                    ctypes.c_void_p(IDS.data_ptr() + 4 * k * B * l),
+                    ctypes.c_void_p(W.data_ptr() + 4 * k * B * l), None, 0, sh, sh,
+                    ctypes.c_void_p(ws.data_ptr()), ws.numel()))
+
+        with torch.cuda.stream(stream):
+            step(0)
+        torch.cuda.synchronize()
+        graphs = _graphs(step, nsteps + warm, 50, stream)
+        steps, ms = _timed(graphs, nsteps, warm, stream)
+        # algorithmic bytes: per layer router + shared + distinct experts of the step
+        qb = lambda n, kk, bits=4: n * kk * bits // 8 + 4 * n * (kk // 64)   # noqa: E731
+        blob = 2 * qb(f, d) + qb(d, f)
+        core = qb(E, d, 8) + 2 * qb(fs, d) + qb(d, fs)
+        rows = ids_f[:, :(nsteps + warm) * B].reshape(L, nsteps + warm, B * k)
+        distinct = float(np.mean([[len(np.unique(r)) for r in lay] for lay in rows]))
+        step_bytes = L * (core + distinct * blob + 4 * B * d)
+        kern = _profile(lib, _hip(), {
+            _lib.TF_KERNEL_ROUTER_SHARED_GATEUP: "router_shared_gateup",
+            _lib.TF_KERNEL_ROUTED_GATEUP_SHARED_DOWN: "routed_gateup_shared_down",
+            _lib.TF_KERNEL_DOWN_COMBINE: "down_combine"}, step, min(args.prof_steps, 100), stream)
+        us = ms * 1e3 / steps
+        kb = (B * k if B * k < distinct else distinct) * 2 * qb(f, d) + qb(d, fs)
+        dur_b = kern["routed_gateup_shared_down"]["avg_us"] * 1e-6
+        res[f"batch{B}"] = {
+            "tokens_per_s": round(B * steps / (ms / 1e3), 1), "us_per_step": round(us, 2),
+            "distinct_experts_per_layer": round(distinct, 2), "step_bytes": int(step_bytes),
+            "GBps": round(step_bytes / (us * 1e-6) / 1e9, 1),
+            "frac_of_hbm_peak": round(step_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "gemv_kernel": {"name": "routed_gateup_shared_down", "bytes_per_launch": int(kb),
+                            "GBps": round(kb / dur_b / 1e9, 1),
+                            "frac": round(kb / dur_b / 1e9 / HBM_PEAK_GBPS, 4)},
+            "kernels_per_layer": kern}
+        del X, F, Y, IDS, W, ws, graphs
+        torch.cuda.synchronize()
+    return {"metric": "30-layer resident MoE stack decode tokens/s", "workload": wl.name,
+            "setup_s": round(setup, 1), "steps": nsteps, "warmup": warm, "results": res}
+
+
+def run_slot(args):
+    """30 layers, 16-slot LFU cache per layer in HBM, experts in pinned host
+    memory, Zipf(1.1) forced routing; misses copied while the shared branch
+    runs."""
+    import numpy as np
+    import torch
+
+    from bit_routed_expert_tf_amd import _lib, api
+    from synth import gen
+    wl = gen.WORKLOADS[2]
+    d, E, k, f, fs, L, S = (wl.d_model, wl.n_experts, wl.top_k, wl.d_ff, wl.d_ff_shared,
+                            wl.n_layers, wl.n_slots)
+    ntok = args.steps or wl.n_tokens
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    stride = gen.blob_bytes(d, f)
+    host = torch.empty(L * E * stride, dtype=torch.uint8, pin_memory=True)
+    hv = host.numpy().reshape(L, E, stride)
+    layers = []
+    for l in range(L):
+        gen.expert_pool(wl.seed, l, d, f, E, out=hv[l], threads=16)
+        layers.append(api.DeviceLayer.from_arrays(gen.router(wl.seed, l, d, E),
+                                                  gen.shared_blob(wl.seed, l, d, fs),
+                                                  torch.empty((S, stride), dtype=torch.uint8,
+                                                              device=dev), d, f, fs, k, device=dev))
+        print(f"slot: layer {l} generated ({time.time() - t0:.0f} s)", file=sys.stderr, flush=True)
+    setup = time.time() - t0
+    slot_pool = torch.empty(L * S * stride, dtype=torch.uint8, device=dev)
+    cache = api.SlotCache(L, E, S, k, stride, slot_pool, host, trace_cap=ntok)
+    X = torch.from_numpy(gen.tokens(wl.seed, ntok, d).view(np.int16)).to(dev)
+    F = torch.from_numpy(np.stack([gen.zipf_ids(wl.seed, l, ntok, E, k) for l in range(L)])).to(dev)
+    Y = torch.empty((L, ntok, d), dtype=torch.float16, device=dev)
+    ws = api.workspace(api.tf_moe_workspace_bytes(layers[0], 1), dev)
+    copy = torch.cuda.Stream(device=dev)
+    # same-run pinned H2D peak: one large copy
+    big = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    c0 = time.perf_counter()
+    for _ in range(4):
+        big.copy_(host[:256 << 20], non_blocking=True)
+    torch.cuda.synchronize()
+    peak = 4 * (256 << 20) / (time.perf_counter() - c0) / 1e9
+    del big
+    w0 = time.perf_counter()
+    for t in range(ntok):
+        for l in range(L):
+            api.tf_moe_layer_fwd(layers[l], X[t:t + 1], forced_ids=F[l, t:t + 1],
+                                 y=Y[l, t:t + 1], cache=cache, layer_idx=l, ws=ws,
+                                 copy_stream=copy)
+        if t % 256 == 255:
+            print(f"slot: token {t + 1}", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    hits = sum(int(cache.trace(l, ntok * k)[0].sum()) for l in range(L))
+    filled = cache.bytes_filled()
+    cache.close()
+    return {"metric": "slot-cache stack decode tokens/s (30 layers, 16 slots, PCIe misses)",
+            "workload": wl.name, "tokens": ntok, "value": round(ntok / wall, 2),
+            "unit": "tokens/s", "hit_rate": round(hits / (L * ntok * k), 4),
+            "h2d_bytes": filled, "h2d_GBps": round(filled / wall / 1e9, 2),
+            "pinned_h2d_peak_GBps": round(peak, 2), "setup_s": round(setup, 1),
+            "wall_s": round(wall, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -248,13 +524,22 @@ def main():
     ap.add_argument("--prof-steps", type=int, default=300)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", choices=["decode", "prefill", "stack", "slot-cache"],
+                    default="decode",
+                    help="decode (default, the headline line); the others measure the "
+                         "prefill chunk, the 30-layer resident stack and the slot-cache stack")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this hot path is built and measured on a single "
               "MI355X (the multi-GPU design is expert sharding, not implemented here).",
               file=sys.stderr)
         sys.exit(2)
-    out = run_decode(args)
+    if args.workload == "decode":
+        out = run_decode(args)
+    else:
+        if "--steps" not in sys.argv:
+            args.steps = 0   # the workload's own count
+        out = {"prefill": run_prefill, "stack": run_stack, "slot-cache": run_slot}[args.workload](args)
     print(json.dumps(out), flush=True)
 
 

@@ -20,6 +20,7 @@ STATUS_NAMES = {0: "TF_OK", 1: "TF_E_ARG", 2: "TF_E_SHAPE", 3: "TF_E_ALIGN", 4: 
 TF_GELU_ERF, TF_GELU_TANH = 0, 1
 TF_FLAG_ID_RANGE, TF_FLAG_ID_REPEAT = 1, 2
 TF_KERNEL_ROUTER_SHARED_GATEUP, TF_KERNEL_ROUTED_GATEUP_SHARED_DOWN, TF_KERNEL_DOWN_COMBINE = 1, 2, 4
+TF_KERNEL_PREFILL_DOWN, TF_KERNEL_PREFILL_COMBINE = 8, 16
 
 c_void_p, c_int32, c_int64, c_size_t = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 

@@ -94,6 +94,7 @@ void fill_common(DecodeArgs &a, const tf_moe_layer *L, int T) {
     a.shared_blob = L->shared_blob; a.pool = L->pool; a.stride = L->blob_stride;
     a.tbx = T < MAX_TB ? T : MAX_TB;
     a.tbh = 1;
+    a.tbi = MAX_TB;   // decode: items of up to MAX_TB tokens, one pass each
     a.topk = 1;
 }
 
@@ -213,7 +214,7 @@ tf_status tf_expert_q4_gemv(const uint8_t *pool, size_t blob_stride, int32_t d_m
     a.hdr = at<uint32_t>(ws, 0);
     a.h_r = at<uint4>(ws, 256);
     a.gemv_slot = slot; a.gemv_token = token; a.gemv_coef = coef; a.P = P;
-    a.tbx = 1; a.tbh = 1;
+    a.tbx = 1; a.tbh = 1; a.tbi = 1;
     a.b_routed_blocks = P * (d_ff / (2 * (64 / tf_decode_lpr(a))));
     hipError_t e = tf_launch_decode(a, STAGE_B | STAGE_C, s);
     return e == hipSuccess ? TF_OK : hip_fail(e, "gemv launch");
@@ -261,8 +262,10 @@ tf_status tf_moe_layer_fwd(const tf_moe_layer *L, const uint16_t *x, int32_t T,
     a.y_s = at<float>(ws, w.ys);
     a.h_r = at<uint4>(ws, w.hr);
     a.do_group = 1;
-    // T == 1: one item per rank; else one item per selected expert
-    const int max_items = T == 1 ? a.k : (T * a.k < a.E ? T * a.k : a.E);
+    // T == 1: one item per rank; else items of up to tbi pairs of one expert
+    // (at most E + T*k/tbi of them)
+    const int max_items = T == 1 ? a.k
+                          : (T * a.k < a.E + T * a.k / a.tbi ? T * a.k : a.E + T * a.k / a.tbi);
     const int n_router = ((a.E + 3) / 4) * T;
     // rows per workgroup: gate/up 2*RPW, shared down 4*RPW (RPW = 64 / lanes per row)
     const int rpw = 64 / tf_decode_lpr(a);
@@ -356,6 +359,7 @@ tf_status tf_moe_prefill_chunk(const tf_moe_layer *L, const uint16_t *x, int32_t
     a.do_group = 1;
     a.tbx = T < 16 ? T : 16;
     a.tbh = T < 8 ? T : 8;
+    a.tbi = T;   // one item per expert: its weights are read once per chunk
     const int rpw = 64 / tf_decode_lpr(a);
     const int max_items = T * a.k < a.E ? T * a.k : a.E;
     a.a_router_blocks = ((a.E + 3) / 4) * T;

@@ -411,9 +411,9 @@ __device__ void topk_block(const DecodeArgs &a, int t, int tid, unsigned char *l
 }
 
 // Group the T*k (token, rank) pairs by expert, sorted by (expert, token,
-// rank): one item per selected expert, [expert, first sorted position,
-// count, 0] (shilu.ai README translation, "推理引擎的工作原理": a chunk's
-// rows share each fetched expert).  Token t's pair with expert e lands at
+// rank): items of at most a.tbi consecutive pairs of one expert, [expert,
+// first sorted position, count, 0] (shilu.ai README translation,
+// "推理引擎的工作原理": a chunk's rows share each fetched expert).  Token t's pair with expert e lands at
 // offs[e] + #{t' < t that selected e}, counted on a per-expert bit mask over
 // the tokens (T <= 128), so the order never depends on thread timing.
 // Positions start out holding their own index, so repeated ids (flagged by
@@ -421,6 +421,7 @@ __device__ void topk_block(const DecodeArgs &a, int t, int tid, unsigned char *l
 __host__ __device__ constexpr int group_lds_bytes(int E, int T) {
     return 4 * E * ((T + 31) >> 5) + 12 * E + 8 * 4;
 }
+__host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 __device__ void group_block(const DecodeArgs &a, int tid, unsigned char *lds) {
     const int P = a.T * a.k, E = a.E, NW = (a.T + 31) >> 5;
@@ -449,7 +450,7 @@ __device__ void group_block(const DecodeArgs &a, int tid, unsigned char *lds) {
         for (int q = 0; q < NW; ++q) c += __popc(mask[e * NW + q]);
         cnt[e] = c;
         sc += c;
-        sn += c > 0;
+        sn += ceil_div(c, a.tbi);
     }
     int ic = sc, in = sn;
     for (int o = 1; o < WAVE; o <<= 1) {
@@ -464,14 +465,15 @@ __device__ void group_block(const DecodeArgs &a, int tid, unsigned char *lds) {
         offs[e] = oc;
         iidx[e] = on;
         oc += cnt[e];
-        on += cnt[e] > 0;
+        on += ceil_div(cnt[e], a.tbi);
     }
     if (tid == WG - 1) st_dev(a.hdr + HDR_NITEMS, (uint32_t)on);
     __syncthreads();
     for (int e = tid; e < E; e += WG)
-        if (cnt[e])
-            st_dev(reinterpret_cast<uint4 *>(a.items + 4 * iidx[e]),
-                   make_uint4((uint32_t)e, (uint32_t)offs[e], (uint32_t)cnt[e], 0u));
+        for (int q = 0; q < cnt[e]; q += a.tbi)
+            st_dev(reinterpret_cast<uint4 *>(a.items + 4 * (iidx[e] + q / a.tbi)),
+                   make_uint4((uint32_t)e, (uint32_t)(offs[e] + q),
+                              (uint32_t)min(a.tbi, cnt[e] - q), 0u));
     stores_done();
     __syncthreads();   // the default positions are written before the scatter
     for (int p = tid; p < P; p += WG) {
@@ -980,7 +982,7 @@ hipError_t launch_ab(const DecodeArgs &a, int which, hipStream_t s) {
         if (n) {
             // an expert item can hold more than MAX_TB tokens, or a shared-down
             // block more than one
-            if ((a.T > MAX_TB && !a.gemv_slot) || a.tbh > 1)
+            if ((a.tbi > MAX_TB && !a.gemv_slot) || a.tbh > 1)
                 TF_LAUNCH(TF_KERNEL_ROUTED_GATEUP_SHARED_DOWN, (k_stage_b<LPR, J, true>), dim3(n),
                           dim3(WG), lds_b(a, LPR), s, a);
             else
@@ -1002,7 +1004,7 @@ template <int JF>
 hipError_t launch_pf_down(const DecodeArgs &a, int max_items, hipStream_t s) {
     const int n = max_items * (a.d >> 5);
     const int lds = 4 * 4 * 8 * (a.f >> 6) + hst_bytes(a.f);
-    if (n) hipLaunchKernelGGL(k_pf_down<JF>, dim3(n), dim3(WG), lds, s, a);
+    if (n) TF_LAUNCH(TF_KERNEL_PREFILL_DOWN, k_pf_down<JF>, dim3(n), dim3(WG), lds, s, a);
     return hipGetLastError();
 }
 
@@ -1081,7 +1083,8 @@ hipError_t tf_launch_prefill_tail(const DecodeArgs &a, int max_items, hipStream_
 #undef TF_CALL_PF
     if (e != hipSuccess) return e;
     const size_t n = (size_t)a.T * a.d;
-    hipLaunchKernelGGL(k_pf_combine, dim3((unsigned)((n + 255) / 256)), dim3(WG), 0, s, a);
+    TF_LAUNCH(TF_KERNEL_PREFILL_COMBINE, k_pf_combine, dim3((unsigned)((n + 255) / 256)), dim3(WG), 0,
+              s, a);
     return hipGetLastError();
 }
 

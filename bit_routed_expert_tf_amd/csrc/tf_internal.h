@@ -49,6 +49,7 @@ struct DecodeArgs {
     // item) then shared down blocks (32 rows, per token sub-batch)
     int a_router_blocks, a_shared_blocks, b_routed_blocks, b_shared_blocks;
     int tbx, tbh;                // tokens per shared gate/up block / per shared-down block
+    int tbi;                     // tokens per routed expert item (grouped steps)
     int topk, do_group;
     // standalone GEMV mode (gemv_slot != NULL): pairs instead of routed items
     const int32_t *gemv_slot, *gemv_token;

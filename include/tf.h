@@ -176,7 +176,9 @@ tf_status tf_moe_prefill_chunk(const tf_moe_layer *L, const uint16_t *x, int32_t
 enum {
     TF_KERNEL_ROUTER_SHARED_GATEUP = 1,      /* decode A: router + top-k + shared gate/up */
     TF_KERNEL_ROUTED_GATEUP_SHARED_DOWN = 2, /* decode B: routed gate/up + shared down    */
-    TF_KERNEL_DOWN_COMBINE = 4               /* decode C: routed down + combine -> y      */
+    TF_KERNEL_DOWN_COMBINE = 4,              /* decode C: routed down + combine -> y      */
+    TF_KERNEL_PREFILL_DOWN = 8,              /* prefill: routed down per expert -> y_e    */
+    TF_KERNEL_PREFILL_COMBINE = 16           /* prefill: y_s + sum of y_e -> y            */
 };
 /* Arm a one-shot timer: the next launch, by this host thread, of the named
  * kernel goes through hipExtLaunchKernel with `start` recorded when the

@@ -73,7 +73,7 @@ WsLayout decode_layout(int d, int f, int fs, int E, int k, int T) {
     size_t o = 0;
     w.hdr = o; o += up256((size_t)4 * (HDR_TICKET + T + 1) > 256 ? (size_t)4 * (HDR_TICKET + T + 1) : 256);
     w.logits = o; o += up256((size_t)8 * T * E);
-    w.items = o; o += up256((size_t)16 * T * k);
+    w.items = o; o += up256((size_t)4 * ITEM_INTS * T * k);
     w.pairs = o; o += up256((size_t)4 * T * k);
     w.hs = o; o += up256(h_row_bytes(fs) * T);
     w.ys = o; o += up256((size_t)4 * T * d);

@@ -411,9 +411,12 @@ __device__ void topk_block(const DecodeArgs &a, int t, int tid, unsigned char *l
 }
 
 // Group the T*k (token, rank) pairs by expert, sorted by (expert, token,
-// rank): items of at most a.tbi consecutive pairs of one expert, [expert,
-// first sorted position, count, 0] (shilu.ai README translation,
-// "推理引擎的工作原理": a chunk's rows share each fetched expert).  Token t's pair with expert e lands at
+// rank): items of at most a.tbi consecutive pairs of one expert (shilu.ai
+// README translation, "推理引擎的工作原理": a chunk's rows share each fetched
+// expert).  An item record is ITEM_INTS ints: expert, first sorted
+// position, count, 0, then -- for its first MAX_TB pairs -- the pair indices
+// and their router weights, so a gate/up block learns everything it needs
+// in one load.  Token t's pair with expert e lands at
 // offs[e] + #{t' < t that selected e}, counted on a per-expert bit mask over
 // the tokens (T <= 128), so the order never depends on thread timing.
 // Positions start out holding their own index, so repeated ids (flagged by
@@ -471,7 +474,7 @@ __device__ void group_block(const DecodeArgs &a, int tid, unsigned char *lds) {
     __syncthreads();
     for (int e = tid; e < E; e += WG)
         for (int q = 0; q < cnt[e]; q += a.tbi)
-            st_dev(reinterpret_cast<uint4 *>(a.items + 4 * (iidx[e] + q / a.tbi)),
+            st_dev(reinterpret_cast<uint4 *>(a.items + ITEM_INTS * (iidx[e] + q / a.tbi)),
                    make_uint4((uint32_t)e, (uint32_t)(offs[e] + q),
                               (uint32_t)min(a.tbi, cnt[e] - q), 0u));
     stores_done();
@@ -483,6 +486,12 @@ __device__ void group_block(const DecodeArgs &a, int tid, unsigned char *lds) {
         for (int q = 0; q < (t >> 5); ++q) r += __popc(mask[e * NW + q]);
         const int pos = offs[e] + r;
         if (pos < P) st_dev(a.pairs + pos, (int32_t)p);
+        const int slot = r % a.tbi;
+        if (slot < MAX_TB) {
+            int32_t *rec = a.items + ITEM_INTS * (iidx[e] + r / a.tbi);
+            st_dev(rec + 4 + slot, (int32_t)p);
+            st_dev(reinterpret_cast<float *>(rec) + 8 + slot, ld_dev(a.weights + p));
+        }
     }
 }
 
@@ -598,9 +607,12 @@ __device__ void gateup_block(const DecodeArgs &a, int b, int tid, unsigned char 
     unsigned char *xst = reinterpret_cast<unsigned char *>(lsb + 4 * RPW * G);
 
     // the item: expert e and nt token slots; slot i -> x row, output row, coef
-    // (mode 0: shared, tokens base + i; 1: a single slot; 2: item pairs)
+    // (mode 0: shared, tokens base + i; 1: a single slot; 2: item pairs from
+    // the pair list; 3: item pairs from the item record)
     int nt, e = 0, base = 0, mode, row1 = 0, xrow1 = 0;
     float coef1 = 1.f;
+    int rp4[MAX_TB] = {0, 0, 0, 0};
+    float cf4[MAX_TB] = {0.f, 0.f, 0.f, 0.f};
     if (!routed) {
         base = item * a.tbx;
         nt = min(a.tbx, a.T - base);
@@ -622,11 +634,21 @@ __device__ void gateup_block(const DecodeArgs &a, int b, int tid, unsigned char 
         coef1 = ld_dev(a.weights + item);
     } else {
         if (item >= (int)ld_dev(a.hdr + HDR_NITEMS)) return;
-        const uint4 it = ld_dev(reinterpret_cast<const uint4 *>(a.items + 4 * item));
+        const uint4 *rec = reinterpret_cast<const uint4 *>(a.items + ITEM_INTS * item);
+        const uint4 it = ld_dev(rec);
         e = (int)it.x;
         base = (int)it.y;
         nt = (int)it.z;
         mode = 2;
+        if (!MULTI) {   // at most MAX_TB pairs: all of them are in the record
+            const uint4 pp = ld_dev(rec + 1), cc = ld_dev(rec + 2);
+            const int pmax = a.T * a.k - 1;
+            rp4[0] = min((int)pp.x, pmax); rp4[1] = min((int)pp.y, pmax);
+            rp4[2] = min((int)pp.z, pmax); rp4[3] = min((int)pp.w, pmax);
+            cf4[0] = __uint_as_float(cc.x); cf4[1] = __uint_as_float(cc.y);
+            cf4[2] = __uint_as_float(cc.z); cf4[3] = __uint_as_float(cc.w);
+            mode = 3;
+        }
     }
     int prow[MAX_TB];
     float coef[MAX_TB];
@@ -640,6 +662,11 @@ __device__ void gateup_block(const DecodeArgs &a, int b, int tid, unsigned char 
             if (mode == 0) {
                 xr = orow = base + si;
                 c = 1.f;
+            } else if (mode == 3) {
+                const int pr = si == 0 ? rp4[0] : si == 1 ? rp4[1] : si == 2 ? rp4[2] : rp4[3];
+                xr = pr / a.k;
+                orow = pr;
+                c = si == 0 ? cf4[0] : si == 1 ? cf4[1] : si == 2 ? cf4[2] : cf4[3];
             } else if (mode == 2) {
                 const int pr = ld_dev(a.pairs + base + si);
                 xr = pr / a.k;
@@ -879,7 +906,7 @@ __global__ __launch_bounds__(256, 4) void k_pf_down(DecodeArgs a) {
     const int tiles = a.d >> 5;
     const int item = blockIdx.x / tiles, rb = blockIdx.x - item * tiles;
     if (item >= (int)ld_dev(a.hdr + HDR_NITEMS)) return;
-    const uint4 it = ld_dev(reinterpret_cast<const uint4 *>(a.items + 4 * item));
+    const uint4 it = ld_dev(reinterpret_cast<const uint4 *>(a.items + ITEM_INTS * item));
     const int e = (int)it.x, base = (int)it.y, nt = (int)it.z;
     const int K = a.f, H = K >> 5, G = K >> 6;
     uint32_t *lsb = reinterpret_cast<uint32_t *>(lds);               // [4][RPW*G]

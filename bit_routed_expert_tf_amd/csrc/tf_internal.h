@@ -18,6 +18,7 @@ __host__ __device__ constexpr size_t h_row_bytes(int K) { return (size_t)160 * (
 constexpr int MAX_DECODE_T = 16;  // tokens per decode step
 constexpr int MAX_PREFILL_T = 128;  // tokens per prefill chunk
 constexpr int MAX_TB = 4;         // tokens staged per pass of a gate/up block
+constexpr int ITEM_INTS = 16;     // ints per expert item record (see group_block)
 
 struct DecodeArgs {
     int d, f, fs, E, k, T, act;
@@ -35,7 +36,7 @@ struct DecodeArgs {
     uint16_t *y;
     float *y32;
     uint32_t *hdr;
-    int32_t *items;              // [E][4] = expert, first sorted pair, count, 0
+    int32_t *items;              // [items][ITEM_INTS] expert item records
     int32_t *pairs;              // [T*k] pair index t*k+r sorted by (expert, t, r)
     // hidden activations as hi/lo fp16 pair rows (9*K/32 uint4 per row, see
     // tf_decode.hip): shared [T][fs], routed [T*k][f] (or [P][f])

@@ -93,7 +93,6 @@ void fill_common(DecodeArgs &a, const tf_moe_layer *L, int T) {
     a.rq = L->router.q; a.rs = L->router.scale; a.rb = L->router.bias;
     a.shared_blob = L->shared_blob; a.pool = L->pool; a.stride = L->blob_stride;
     a.tbx = T < MAX_TB ? T : MAX_TB;
-    a.tbh = 1;
     a.tbi = MAX_TB;   // decode: items of up to MAX_TB tokens, one pass each
     a.topk = 1;
 }
@@ -214,7 +213,7 @@ tf_status tf_expert_q4_gemv(const uint8_t *pool, size_t blob_stride, int32_t d_m
     a.hdr = at<uint32_t>(ws, 0);
     a.h_r = at<uint4>(ws, 256);
     a.gemv_slot = slot; a.gemv_token = token; a.gemv_coef = coef; a.P = P;
-    a.tbx = 1; a.tbh = 1; a.tbi = 1;
+    a.tbx = 1; a.tbi = 1;
     a.b_routed_blocks = P * (d_ff / (2 * (64 / tf_decode_lpr(a))));
     hipError_t e = tf_launch_decode(a, STAGE_B | STAGE_C, s);
     return e == hipSuccess ? TF_OK : hip_fail(e, "gemv launch");
@@ -271,7 +270,7 @@ tf_status tf_moe_layer_fwd(const tf_moe_layer *L, const uint16_t *x, int32_t T,
     const int rpw = 64 / tf_decode_lpr(a);
     const int n_shared_a = (a.fs / (2 * rpw)) * ((T + a.tbx - 1) / a.tbx);
     const int n_routed_b = (a.f / (2 * rpw)) * max_items;
-    const int n_shared_b = (a.d / (4 * rpw)) * ((T + a.tbh - 1) / a.tbh);
+    const int n_shared_b = (a.d / (4 * rpw)) * T;   // one token per shared-down block
     hipError_t e;
 
     if (!cache) {
@@ -324,11 +323,10 @@ size_t tf_prefill_workspace_bytes(const tf_moe_layer *L, int32_t T) {
 // of at most 128 tokens, so each fetched expert serves several rows).  The
 // chunk's (token, rank) pairs are grouped by expert and every expert's
 // weights are read once:
-//   A  router rows + top-k per token, grouping; shared gate/up (16 tokens
-//      per block, the weight tile reused across them)
-//   B  routed gate/up per expert item (all its tokens); shared down (8
-//      tokens per block)
-//   C  routed down per expert item -> y_e per pair
+//   A  router rows + top-k per token, grouping into items of <= 16 tokens
+//   B  gate/up on the matrix cores: shared expert per 16 tokens, routed
+//      expert per item -> h_s, h_r
+//   C  down on the matrix cores -> y_s, y_e per pair
 //   D  y = y_s + sum over ranks of y_e, fp16
 tf_status tf_moe_prefill_chunk(const tf_moe_layer *L, const uint16_t *x, int32_t T, uint16_t *y,
                                float *y32, int32_t *ids, float *weights, hipStream_t s, void *ws,
@@ -357,17 +355,12 @@ tf_status tf_moe_prefill_chunk(const tf_moe_layer *L, const uint16_t *x, int32_t
     a.h_r = at<uint4>(ws, w.hr);
     a.y_e = at<float>(ws, w.total);
     a.do_group = 1;
-    a.tbx = T < 16 ? T : 16;
-    a.tbh = T < 8 ? T : 8;
-    a.tbi = T;   // one item per expert: its weights are read once per chunk
-    const int rpw = 64 / tf_decode_lpr(a);
-    const int max_items = T * a.k < a.E ? T * a.k : a.E;
+    a.tbi = 16;   // items of up to 16 tokens: one MFMA token tile each
+    const int P = T * a.k;
+    const int max_items = P < a.E + P / a.tbi ? P : a.E + P / a.tbi;
     a.a_router_blocks = ((a.E + 3) / 4) * T;
-    a.a_shared_blocks = (a.fs / (2 * rpw)) * ((T + a.tbx - 1) / a.tbx);
-    a.b_routed_blocks = (a.f / (2 * rpw)) * max_items;
-    a.b_shared_blocks = (a.d / (4 * rpw)) * ((T + a.tbh - 1) / a.tbh);
-    hipError_t e = tf_launch_decode(a, STAGE_A | STAGE_B, s);
-    if (e == hipSuccess) e = tf_launch_prefill_tail(a, max_items, s);
+    hipError_t e = tf_launch_decode(a, STAGE_A, s);
+    if (e == hipSuccess) e = tf_launch_prefill_mfma(a, max_items, s);
     return e == hipSuccess ? TF_OK : hip_fail(e, "prefill launch");
 }
 

@@ -27,41 +27,11 @@
 // so repeated runs are bitwise identical.
 #include "tf_device.h"
 #include "tf_internal.h"
+#include "tf_layer.h"
 
 using namespace tfk;
 
 namespace {
-
-constexpr int WG = 256;
-
-struct Mat {
-    const uint8_t *q;
-    const uint16_t *s;
-    const uint16_t *b;
-};
-
-__device__ __forceinline__ void blob_mats(const uint8_t *blob, int d, int f, Mat &g, Mat &u,
-                                          Mat &dn) {
-    const size_t qb = (size_t)f * d / 2, sb = (size_t)f * (d / 64) * 2;
-    const size_t dqb = (size_t)d * f / 2, dsb = (size_t)d * (f / 64) * 2;
-    const uint8_t *p = blob;
-    g.q = p; p += qb;
-    g.s = reinterpret_cast<const uint16_t *>(p); p += sb;
-    g.b = reinterpret_cast<const uint16_t *>(p); p += sb;
-    u.q = p; p += qb;
-    u.s = reinterpret_cast<const uint16_t *>(p); p += sb;
-    u.b = reinterpret_cast<const uint16_t *>(p); p += sb;
-    dn.q = p; p += dqb;
-    dn.s = reinterpret_cast<const uint16_t *>(p); p += dsb;
-    dn.b = reinterpret_cast<const uint16_t *>(p);
-}
-
-__device__ __forceinline__ const uint8_t *expert_blob(const DecodeArgs &a, int e) {
-    const int slot = a.slot_map ? a.slot_map[e] : e;
-    return a.pool + (size_t)slot * a.stride;
-}
-
-__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // ----------------------------------------------------------- weight tile
 // RPW = 64/LPR rows of one q4 matrix with K columns per wave: lane (r, s)
@@ -179,11 +149,6 @@ __device__ __forceinline__ float tile_dot(const Tile<LPR, J> &t, const uint32_t 
     return acc;
 }
 
-// LDS stage layouts (bytes): fp16 row  = pairs [4H] uint4 + S [H] float2
-//                            hi/lo row = hi [4H] uint4 + lo [4H] uint4 + S [H] float2
-__host__ __device__ constexpr int xst_bytes(int K) { return 72 * (K >> 5); }
-__host__ __device__ constexpr int hst_bytes(int K) { return 136 * (K >> 5); }
-
 // ------------------------------------------------------- fp16 x staging
 // Up to 4 rows (row i at rp[i]) of K fp16 values, 8-value blocks, thread t
 // takes blocks t, t+256, ...: loads first (xs_load), processing later
@@ -295,27 +260,6 @@ __device__ __forceinline__ void hs_store(const HStage<MAXI, MAXS> &Hs, int rows,
             reinterpret_cast<float2 *>(base + (size_t)row * sb + 128 * H)[hg] = make_float2(X, C);
         }
     }
-}
-
-// Producer side: the 8 values of rows 8*blk .. 8*blk+7 of one hidden row of
-// length K go to the global hi/lo row `dst` (10H uint4).
-__device__ __forceinline__ void hs_produce(uint4 *dst, int K, int blk, const float (&e)[8]) {
-    const int H = K >> 5;
-    float hi[8], lo[8], xe = 0.f, xo = 0.f;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        hi[q] = (float)(_Float16)e[q];
-        lo[q] = (float)(_Float16)(e[q] - hi[q]);
-        if (q & 1) xo += hi[q] + lo[q];
-        else xe += hi[q] + lo[q];
-    }
-    const int hg = blk >> 2, m = blk & 3;
-    dst[m * H + hg] = make_uint4(pack_h2(hi[0], hi[4]), pack_h2(hi[1], hi[5]),
-                                 pack_h2(hi[2], hi[6]), pack_h2(hi[3], hi[7]));
-    dst[4 * H + m * H + hg] = make_uint4(pack_h2(lo[0], lo[4]), pack_h2(lo[1], lo[5]),
-                                         pack_h2(lo[2], lo[6]), pack_h2(lo[3], lo[7]));
-    reinterpret_cast<float2 *>(dst + 8 * H + 2 * hg)[m] =
-        make_float2(xe + xo, fmaf(1024.f, xe, 64.f * xo));
 }
 
 // ------------------------------------------------------------------ top-k
@@ -590,10 +534,8 @@ __device__ void router_block(const DecodeArgs &a, int b, int tid, unsigned char 
 // 2 RPW), waves 2/3 the same up rows; h = coef * gelu(g) * u, written as
 // hi/lo rows.  routed == false: the shared expert for tokens
 // [b / tiles * tbx, +tbx) -> h_s; routed == true: expert item b / tiles ->
-// h_r[pair].  The weight tile is loaded once and stays in registers while
-// the item's tokens pass through in groups of MAX_TB (MULTI: more than one
-// pass may be needed; otherwise an item has at most MAX_TB tokens).
-template <int LPR, int J, bool routed, bool MULTI>
+// h_r[pair].  An item has at most MAX_TB tokens, staged together.
+template <int LPR, int J, bool routed>
 __device__ void gateup_block(const DecodeArgs &a, int b, int tid, unsigned char *lds) {
     constexpr int RPW = WAVE / LPR, RWG = 2 * RPW;
     const int lane = tid & 63, w = uniform(tid >> 6);
@@ -607,8 +549,8 @@ __device__ void gateup_block(const DecodeArgs &a, int b, int tid, unsigned char 
     unsigned char *xst = reinterpret_cast<unsigned char *>(lsb + 4 * RPW * G);
 
     // the item: expert e and nt token slots; slot i -> x row, output row, coef
-    // (mode 0: shared, tokens base + i; 1: a single slot; 2: item pairs from
-    // the pair list; 3: item pairs from the item record)
+    // (mode 0: shared, tokens base + i; 1: a single slot; 3: item pairs from
+    // the item record)
     int nt, e = 0, base = 0, mode, row1 = 0, xrow1 = 0;
     float coef1 = 1.f;
     int rp4[MAX_TB] = {0, 0, 0, 0};
@@ -634,21 +576,17 @@ __device__ void gateup_block(const DecodeArgs &a, int b, int tid, unsigned char 
         coef1 = ld_dev(a.weights + item);
     } else {
         if (item >= (int)ld_dev(a.hdr + HDR_NITEMS)) return;
+        // at most MAX_TB pairs: all of them are in the item record
         const uint4 *rec = reinterpret_cast<const uint4 *>(a.items + ITEM_INTS * item);
-        const uint4 it = ld_dev(rec);
+        const uint4 it = ld_dev(rec), pp = ld_dev(rec + 1), cc = ld_dev(rec + 2);
         e = (int)it.x;
-        base = (int)it.y;
-        nt = (int)it.z;
-        mode = 2;
-        if (!MULTI) {   // at most MAX_TB pairs: all of them are in the record
-            const uint4 pp = ld_dev(rec + 1), cc = ld_dev(rec + 2);
-            const int pmax = a.T * a.k - 1;
-            rp4[0] = min((int)pp.x, pmax); rp4[1] = min((int)pp.y, pmax);
-            rp4[2] = min((int)pp.z, pmax); rp4[3] = min((int)pp.w, pmax);
-            cf4[0] = __uint_as_float(cc.x); cf4[1] = __uint_as_float(cc.y);
-            cf4[2] = __uint_as_float(cc.z); cf4[3] = __uint_as_float(cc.w);
-            mode = 3;
-        }
+        nt = min((int)it.z, MAX_TB);
+        const int pmax = a.T * a.k - 1;
+        rp4[0] = min((int)pp.x, pmax); rp4[1] = min((int)pp.y, pmax);
+        rp4[2] = min((int)pp.z, pmax); rp4[3] = min((int)pp.w, pmax);
+        cf4[0] = __uint_as_float(cc.x); cf4[1] = __uint_as_float(cc.y);
+        cf4[2] = __uint_as_float(cc.z); cf4[3] = __uint_as_float(cc.w);
+        mode = 3;
     }
     int prow[MAX_TB];
     float coef[MAX_TB];
@@ -667,11 +605,6 @@ __device__ void gateup_block(const DecodeArgs &a, int b, int tid, unsigned char 
                 xr = pr / a.k;
                 orow = pr;
                 c = si == 0 ? cf4[0] : si == 1 ? cf4[1] : si == 2 ? cf4[2] : cf4[3];
-            } else if (mode == 2) {
-                const int pr = ld_dev(a.pairs + base + si);
-                xr = pr / a.k;
-                orow = pr;
-                c = ld_dev(a.weights + pr);
             }
             prow[i] = orow;
             coef[i] = c;
@@ -730,29 +663,17 @@ __device__ void gateup_block(const DecodeArgs &a, int b, int tid, unsigned char 
     tile_store_sb(tl, lsb + w * RPW * G, G, lane);
     __syncthreads();
     finish(ns0);
-    if (MULTI)
-    for (int s0 = MAX_TB; s0 < nt; s0 += MAX_TB) {   // further passes reuse the tile
-        const int ns = min(MAX_TB, nt - s0);
-        __syncthreads();
-        rows(s0, ns);
-        xs_load(X, rp, ns, d, tid);
-        xs_store(X, ns, d, xst, tid);
-        __syncthreads();
-        finish(ns);
-    }
 }
 
 // --------------------------------------------------------- shared down
 // 4*RPW output rows (RPW per wave) of the shared down projection for tokens
-// [b / tiles * tbh, +tbh): y_s[t][row], one token per pass with the weight
-// tile kept in registers (MULTI: more than one token per block).
-template <int LPR, int J, bool MULTI>
+// b / tiles: y_s[t][row].
+template <int LPR, int J>
 __device__ void shared_down_block(const DecodeArgs &a, int b, int tid, unsigned char *lds) {
     constexpr int RPW = WAVE / LPR;
     const int lane = tid & 63, w = uniform(tid >> 6);
     const int tiles = a.d / (4 * RPW);
-    const int sb = b / tiles, rb = b - sb * tiles;
-    const int t0 = sb * a.tbh, nt = min(a.tbh, a.T - t0);
+    const int t0 = b / tiles, rb = b - t0 * tiles;
     const int K = a.fs, H = K >> 5, G = K >> 6;
     uint32_t *lsb = reinterpret_cast<uint32_t *>(lds);               // [4][RPW*G]
     unsigned char *hst = reinterpret_cast<unsigned char *>(lsb + 4 * RPW * G);
@@ -775,35 +696,26 @@ __device__ void shared_down_block(const DecodeArgs &a, int b, int tid, unsigned 
         if (lane % LPR == 0) a.y_s[(size_t)(t0 + i) * a.d + row0 + lane / LPR] = v;
     };
     one(0);
-    if (MULTI)
-    for (int i = 1; i < nt; ++i) {
-        __syncthreads();   // the previous token is done with the staged row
-        HStage<(J * LPR + 31) / 32, (J * LPR + 255) / 256> Hn;
-        hs_load(Hn, a.h_s + (size_t)(t0 + i) * 10 * H, 1, K, tid);
-        hs_store(Hn, 1, K, hst, tid);
-        __syncthreads();
-        one(i);
-    }
 }
 
-template <int LPR, int J, bool MULTI>
-__global__ __launch_bounds__(256, MULTI ? 2 : 4) void k_stage_a(DecodeArgs a) {
+template <int LPR, int J>
+__global__ __launch_bounds__(256, 4) void k_stage_a(DecodeArgs a) {
     extern __shared__ __align__(16) unsigned char lds[];
     const int b = blockIdx.x, tid = threadIdx.x;
     if (b < a.a_router_blocks)
         router_block(a, b, tid, lds);
     else
-        gateup_block<LPR, J, false, MULTI>(a, b - a.a_router_blocks, tid, lds);
+        gateup_block<LPR, J, false>(a, b - a.a_router_blocks, tid, lds);
 }
 
-template <int LPR, int J, bool MULTI>
-__global__ __launch_bounds__(256, MULTI ? 2 : 4) void k_stage_b(DecodeArgs a) {
+template <int LPR, int J>
+__global__ __launch_bounds__(256, 4) void k_stage_b(DecodeArgs a) {
     extern __shared__ __align__(16) unsigned char lds[];
     const int b = blockIdx.x, tid = threadIdx.x;
     if (b < a.b_routed_blocks)
-        gateup_block<LPR, J, true, MULTI>(a, b, tid, lds);
+        gateup_block<LPR, J, true>(a, b, tid, lds);
     else
-        shared_down_block<LPR, J, MULTI>(a, b - a.b_routed_blocks, tid, lds);
+        shared_down_block<LPR, J>(a, b - a.b_routed_blocks, tid, lds);
 }
 
 // ---------------------------------------------- routed down + combine
@@ -893,52 +805,7 @@ __global__ __launch_bounds__(256, 4) void k_stage_c(DecodeArgs a) {
     }
 }
 
-// ------------------------------------------------- prefill: down, combine
-// Routed down projection per expert item (prefill chunks): 32 output rows
-// (8 lanes per row, 8 rows per wave) of the item's W_down, applied to each
-// of its pairs in turn with the weight tile kept in registers:
-// y_e[pair][row] (fp32, the coefficient is already in h).
-template <int JF>
-__global__ __launch_bounds__(256, 4) void k_pf_down(DecodeArgs a) {
-    constexpr int LPR = 8, RPW = 8;
-    extern __shared__ __align__(16) unsigned char lds[];
-    const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
-    const int tiles = a.d >> 5;
-    const int item = blockIdx.x / tiles, rb = blockIdx.x - item * tiles;
-    if (item >= (int)ld_dev(a.hdr + HDR_NITEMS)) return;
-    const uint4 it = ld_dev(reinterpret_cast<const uint4 *>(a.items + ITEM_INTS * item));
-    const int e = (int)it.x, base = (int)it.y, nt = (int)it.z;
-    const int K = a.f, H = K >> 5, G = K >> 6;
-    uint32_t *lsb = reinterpret_cast<uint32_t *>(lds);               // [4][RPW*G]
-    unsigned char *hst = reinterpret_cast<unsigned char *>(lsb + 4 * RPW * G);
-    HStage<(JF * LPR + 31) / 32, (JF * LPR + 255) / 256> Hs;   // 1 row
-    int pr = ld_dev(a.pairs + base);
-    hs_load(Hs, a.h_r + (size_t)pr * 10 * H, 1, K, tid);
-    Mat g, u, dn;
-    blob_mats(expert_blob(a, e), a.d, a.f, g, u, dn);
-    const int row0 = rb * 32 + RPW * w;
-    Tile<LPR, JF> tl;
-    tile_load_sb<LPR, JF>(tl, dn, row0, K, lane);
-    tile_load_q<LPR, JF>(tl, dn, row0, K, lane);
-    hs_store(Hs, 1, K, hst, tid);
-    tile_store_sb(tl, lsb + w * RPW * G, G, lane);
-    __syncthreads();
-    for (int i = 0; i < nt; ++i) {
-        if (i) {
-            __syncthreads();
-            pr = ld_dev(a.pairs + base + i);
-            hs_load(Hs, a.h_r + (size_t)pr * 10 * H, 1, K, tid);
-            hs_store(Hs, 1, K, hst, tid);
-            __syncthreads();
-        }
-        const float v = row_sum<LPR>(tile_dot<LPR, JF, true>(
-            tl, lsb + w * RPW * G, G, reinterpret_cast<const uint4 *>(hst),
-            reinterpret_cast<const uint4 *>(hst + 64 * H),
-            reinterpret_cast<const float2 *>(hst + 128 * H), H, lane));
-        if (lane % LPR == 0) a.y_e[(size_t)pr * a.d + row0 + lane / LPR] = v;
-    }
-}
-
+// ------------------------------------------------------ prefill combine
 // Combine: y[t] = y_s[t] + sum over ranks r of y_e[t*k + r], in rank order,
 // then fp16 round to nearest even (and the fp32 value when asked).
 __global__ __launch_bounds__(256) void k_pf_combine(DecodeArgs a) {
@@ -982,7 +849,7 @@ int lds_a(const DecodeArgs &a, int lpr) {
 int lds_b(const DecodeArgs &a, int lpr) {
     const int rpw = 64 / lpr;
     int r = 0, s = 0;
-    if (a.b_routed_blocks) r = gateup_lds(a, lpr, a.T > 1 && !a.gemv_slot ? MAX_TB : 1);
+    if (a.b_routed_blocks) r = gateup_lds(a, lpr, a.T > 1 && !a.gemv_slot ? min(a.T, MAX_TB) : 1);
     if (a.b_shared_blocks) s = 4 * 4 * rpw * (a.fs >> 6) + hst_bytes(a.fs);
     return max(r, s);
 }
@@ -995,27 +862,15 @@ template <int LPR, int J>
 hipError_t launch_ab(const DecodeArgs &a, int which, hipStream_t s) {
     if (which & STAGE_A) {
         const int n = a.a_router_blocks + a.a_shared_blocks;
-        if (n) {
-            if (a.tbx > MAX_TB)
-                TF_LAUNCH(TF_KERNEL_ROUTER_SHARED_GATEUP, (k_stage_a<LPR, J, true>), dim3(n),
-                          dim3(WG), lds_a(a, LPR), s, a);
-            else
-                TF_LAUNCH(TF_KERNEL_ROUTER_SHARED_GATEUP, (k_stage_a<LPR, J, false>), dim3(n),
-                          dim3(WG), lds_a(a, LPR), s, a);
-        }
+        if (n)
+            TF_LAUNCH(TF_KERNEL_ROUTER_SHARED_GATEUP, (k_stage_a<LPR, J>), dim3(n), dim3(WG),
+                      lds_a(a, LPR), s, a);
     }
     if (which & STAGE_B) {
         const int n = a.b_routed_blocks + a.b_shared_blocks;
-        if (n) {
-            // an expert item can hold more than MAX_TB tokens, or a shared-down
-            // block more than one
-            if ((a.tbi > MAX_TB && !a.gemv_slot) || a.tbh > 1)
-                TF_LAUNCH(TF_KERNEL_ROUTED_GATEUP_SHARED_DOWN, (k_stage_b<LPR, J, true>), dim3(n),
-                          dim3(WG), lds_b(a, LPR), s, a);
-            else
-                TF_LAUNCH(TF_KERNEL_ROUTED_GATEUP_SHARED_DOWN, (k_stage_b<LPR, J, false>), dim3(n),
-                          dim3(WG), lds_b(a, LPR), s, a);
-        }
+        if (n)
+            TF_LAUNCH(TF_KERNEL_ROUTED_GATEUP_SHARED_DOWN, (k_stage_b<LPR, J>), dim3(n), dim3(WG),
+                      lds_b(a, LPR), s, a);
     }
     return hipGetLastError();
 }
@@ -1024,14 +879,6 @@ template <int JF>
 hipError_t launch_c(const DecodeArgs &a, hipStream_t s) {
     const int n = a.T * (a.d >> 3);
     if (n) TF_LAUNCH(TF_KERNEL_DOWN_COMBINE, k_stage_c<JF>, dim3(n), dim3(WG), lds_c(a), s, a);
-    return hipGetLastError();
-}
-
-template <int JF>
-hipError_t launch_pf_down(const DecodeArgs &a, int max_items, hipStream_t s) {
-    const int n = max_items * (a.d >> 5);
-    const int lds = 4 * 4 * 8 * (a.f >> 6) + hst_bytes(a.f);
-    if (n) TF_LAUNCH(TF_KERNEL_PREFILL_DOWN, k_pf_down<JF>, dim3(n), dim3(WG), lds, s, a);
     return hipGetLastError();
 }
 
@@ -1101,14 +948,8 @@ hipError_t tf_launch_decode(const DecodeArgs &a, int which, hipStream_t s) {
     return e;
 }
 
-// Prefill tail: routed down per expert item (y_e per pair), then the combine.
-hipError_t tf_launch_prefill_tail(const DecodeArgs &a, int max_items, hipStream_t s) {
-    hipError_t e = hipSuccess;
-    const int J = (a.f + 255) / 256;
-#define TF_CALL_PF(JJ) e = launch_pf_down<JJ>(a, max_items, s)
-    TF_J_SWITCH(J, TF_CALL_PF)
-#undef TF_CALL_PF
-    if (e != hipSuccess) return e;
+// Prefill: y = y_s + sum over ranks of y_e -> fp16.
+hipError_t tf_launch_prefill_combine(const DecodeArgs &a, hipStream_t s) {
     const size_t n = (size_t)a.T * a.d;
     TF_LAUNCH(TF_KERNEL_PREFILL_COMBINE, k_pf_combine, dim3((unsigned)((n + 255) / 256)), dim3(WG), 0,
               s, a);

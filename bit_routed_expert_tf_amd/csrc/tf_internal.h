@@ -49,7 +49,7 @@ struct DecodeArgs {
     // token sub-batch); stage B = routed gate/up blocks (16 rows of one expert
     // item) then shared down blocks (32 rows, per token sub-batch)
     int a_router_blocks, a_shared_blocks, b_routed_blocks, b_shared_blocks;
-    int tbx, tbh;                // tokens per shared gate/up block / per shared-down block
+    int tbx;                     // tokens per shared gate/up block (<= MAX_TB)
     int tbi;                     // tokens per routed expert item (grouped steps)
     int topk, do_group;
     // standalone GEMV mode (gemv_slot != NULL): pairs instead of routed items
@@ -59,9 +59,11 @@ struct DecodeArgs {
 };
 
 hipError_t tf_launch_decode(const DecodeArgs &a, int which, hipStream_t s);
-// Prefill after stages A and B: routed down per expert item into y_e, then
-// y = y_s + sum over ranks of y_e -> fp16.
-hipError_t tf_launch_prefill_tail(const DecodeArgs &a, int max_items, hipStream_t s);
+// Prefill combine: y = y_s + sum over ranks of y_e -> fp16.
+hipError_t tf_launch_prefill_combine(const DecodeArgs &a, hipStream_t s);
+// Prefill on the matrix cores after the router launch (items of at most 16
+// tokens): gate/up, down and the combine.
+hipError_t tf_launch_prefill_mfma(const DecodeArgs &a, int max_items, hipStream_t s);
 // Lanes per weight row used by stages A and B for these shapes (8 or 16).
 int tf_decode_lpr(const DecodeArgs &a);
 

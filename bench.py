@@ -349,9 +349,9 @@ def run_prefill(args):
     blob = 2 * qb(f, d) + qb(d, f)
     chunk_bytes = qb(E, d, 8) + 2 * qb(fs, d) + qb(d, fs) + distinct * blob + 4 * C * d
     kern = _profile(lib, _hip(), {
-        _lib.TF_KERNEL_ROUTER_SHARED_GATEUP: "router_topk_group_shared_gateup",
-        _lib.TF_KERNEL_ROUTED_GATEUP_SHARED_DOWN: "routed_gateup_shared_down",
-        _lib.TF_KERNEL_PREFILL_DOWN: "routed_down_per_expert",
+        _lib.TF_KERNEL_ROUTER_SHARED_GATEUP: "router_topk_group",
+        _lib.TF_KERNEL_PREFILL_GATEUP: "gateup_mfma",
+        _lib.TF_KERNEL_PREFILL_DOWN: "down_mfma",
         _lib.TF_KERNEL_PREFILL_COMBINE: "combine"}, step, min(args.prof_steps, 64), stream)
     us = ms * 1e3 / steps
     return {"metric": "prefill tokens/s (128-token chunks, one layer)",

@@ -18,7 +18,7 @@ __all__ = [
     "DeviceLayer", "workspace", "tf_expert_blob_bytes", "tf_moe_workspace_bytes",
     "tf_moe_layer_fwd", "tf_router_workspace_bytes", "tf_router_topk",
     "tf_gemv_workspace_bytes", "tf_expert_q4_gemv", "tf_prefill_workspace_bytes",
-    "tf_moe_prefill_chunk", "tf_workspace_flags", "tf_workspace_zero", "SlotCache",
+    "tf_moe_prefill_chunk", "tf_group_workspace_bytes", "tf_group_by_expert", "tf_workspace_flags", "tf_workspace_zero", "SlotCache",
     "pinned_host", "stream_handle",
 ]
 
@@ -190,6 +190,27 @@ def tf_moe_prefill_chunk(layer, x, y=None, y32=None, ids=None, weights=None, ws=
     check(load().tf_moe_prefill_chunk(_layer_ptr(layer), _p(x), T, _p(y), _p(y32), _p(ids),
                                       _p(weights), stream_handle(stream), _p(ws), ws.numel()))
     return y, ids, weights, y32
+
+
+def tf_group_workspace_bytes(n_experts, T, top_k):
+    return int(load().tf_group_workspace_bytes(n_experts, T, top_k))
+
+
+def tf_group_by_expert(ids, n_experts, counts=None, offsets=None, pairs=None, ws=None,
+                       stream=None):
+    T, k = ids.shape
+    dev = ids.device
+    if counts is None:
+        counts = torch.empty(n_experts, dtype=torch.int32, device=dev)
+    if offsets is None:
+        offsets = torch.empty(n_experts + 1, dtype=torch.int32, device=dev)
+    if pairs is None:
+        pairs = torch.empty(T * k, dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = workspace(tf_group_workspace_bytes(n_experts, T, k), dev)
+    check(load().tf_group_by_expert(_p(ids), T, k, n_experts, _p(counts), _p(offsets), _p(pairs),
+                                    _p(ws), ws.numel(), stream_handle(stream)))
+    return counts, offsets, pairs
 
 
 def tf_workspace_zero(ws, stream=None):

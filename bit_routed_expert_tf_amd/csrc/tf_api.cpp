@@ -364,4 +364,37 @@ tf_status tf_moe_prefill_chunk(const tf_moe_layer *L, const uint16_t *x, int32_t
     return e == hipSuccess ? TF_OK : hip_fail(e, "prefill launch");
 }
 
+// Grouping alone: the same block the prefill and batched decode steps run
+// after their top-k, here on caller ids (shilu.ai README translation,
+// "推理引擎的工作原理").  Workspace: a 256-B header, then the item records.
+size_t tf_group_workspace_bytes(int32_t n_experts, int32_t T, int32_t top_k) {
+    if (n_experts <= 0 || T <= 0 || top_k <= 0) return 256;
+    return 256 + up256((size_t)4 * ITEM_INTS * ((size_t)n_experts + (size_t)T * top_k));
+}
+
+tf_status tf_group_by_expert(const int32_t *ids, int32_t T, int32_t top_k, int32_t n_experts,
+                             int32_t *counts, int32_t *offsets, int32_t *pairs, void *ws,
+                             size_t ws_bytes, hipStream_t s) {
+    if (T < 0 || T > MAX_PREFILL_T) return fail(TF_E_SHAPE, "T must be in [0, %d]", MAX_PREFILL_T);
+    if (T == 0) return TF_OK;
+    if (top_k < 1 || top_k > 16 || n_experts < top_k || n_experts > 1024)
+        return fail(TF_E_SHAPE, "need 1 <= top_k <= 16 and top_k <= n_experts <= 1024");
+    if (!ids || !counts || !offsets || !pairs || !ws) return fail(TF_E_ARG, "NULL ids/counts/offsets/pairs/ws");
+    if (!aligned(ids, 4) || !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(pairs, 4) ||
+        !aligned(ws, 256))
+        return fail(TF_E_ALIGN, "int32 arrays 4-byte, ws 256-byte alignment");
+    if (ws_bytes < tf_group_workspace_bytes(n_experts, T, top_k)) return fail(TF_E_NOMEM, "workspace too small");
+    DecodeArgs a;
+    memset(&a, 0, sizeof a);
+    a.E = n_experts; a.k = top_k; a.T = T;
+    a.ids = const_cast<int32_t *>(ids);   // read only by the grouping
+    a.pairs = pairs;
+    a.g_counts = counts; a.g_offsets = offsets;
+    a.hdr = at<uint32_t>(ws, 0);
+    a.items = at<int32_t>(ws, 256);
+    a.tbi = 16;   // items of <= 16 tokens, as in a prefill chunk
+    hipError_t e = tf_launch_group(a, s);
+    return e == hipSuccess ? TF_OK : hip_fail(e, "grouping launch");
+}
+
 }  // extern "C"

@@ -415,6 +415,13 @@ __device__ void group_block(const DecodeArgs &a, int tid, unsigned char *lds) {
         on += ceil_div(cnt[e], a.tbi);
     }
     if (tid == WG - 1) st_dev(a.hdr + HDR_NITEMS, (uint32_t)on);
+    if (a.g_counts) {
+        for (int e = e0; e < e1; ++e) {
+            st_dev(a.g_counts + e, (int32_t)cnt[e]);
+            st_dev(a.g_offsets + e, (int32_t)offs[e]);
+        }
+        if (tid == WG - 1) st_dev(a.g_offsets + E, (int32_t)oc);   // the total
+    }
     __syncthreads();
     for (int e = tid; e < E; e += WG)
         for (int q = 0; q < cnt[e]; q += a.tbi)
@@ -434,7 +441,8 @@ __device__ void group_block(const DecodeArgs &a, int tid, unsigned char *lds) {
         if (slot < MAX_TB) {
             int32_t *rec = a.items + ITEM_INTS * (iidx[e] + r / a.tbi);
             st_dev(rec + 4 + slot, (int32_t)p);
-            st_dev(reinterpret_cast<float *>(rec) + 8 + slot, ld_dev(a.weights + p));
+            st_dev(reinterpret_cast<float *>(rec) + 8 + slot,
+                   a.weights ? ld_dev(a.weights + p) : 0.f);
         }
     }
 }
@@ -819,6 +827,11 @@ __global__ __launch_bounds__(256) void k_pf_combine(DecodeArgs a) {
     a.y[i] = f2h(y);
 }
 
+__global__ __launch_bounds__(256) void k_group(DecodeArgs a) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    group_block(a, threadIdx.x, lds);
+}
+
 __global__ __launch_bounds__(256) void k_zero(uint32_t *p, size_t n) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
          i += (size_t)gridDim.x * blockDim.x)
@@ -946,6 +959,11 @@ hipError_t tf_launch_decode(const DecodeArgs &a, int which, hipStream_t s) {
 #undef TF_CALL_C
     }
     return e;
+}
+
+hipError_t tf_launch_group(const DecodeArgs &a, hipStream_t s) {
+    TF_LAUNCH(TF_KERNEL_GROUP, k_group, dim3(1), dim3(WG), group_lds_bytes(a.E, a.T), s, a);
+    return hipGetLastError();
 }
 
 // Prefill: y = y_s + sum over ranks of y_e -> fp16.

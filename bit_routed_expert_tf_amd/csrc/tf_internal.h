@@ -38,7 +38,8 @@ struct DecodeArgs {
     uint32_t *hdr;
     int32_t *items;              // [items][ITEM_INTS] expert item records
     int32_t *pairs;              // [T*k] pair index t*k+r sorted by (expert, t, r)
-    // hidden activations as hi/lo fp16 pair rows (9*K/32 uint4 per row, see
+    int32_t *g_counts, *g_offsets;  // grouping outputs [E], [E+1] (NULL in layer calls)
+    // hidden activations as hi/lo fp16 pair rows (10*K/32 uint4 per row, see
     // tf_decode.hip): shared [T][fs], routed [T*k][f] (or [P][f])
     uint4 *h_s;
     float *y_s;                  // [T][d]
@@ -59,6 +60,8 @@ struct DecodeArgs {
 };
 
 hipError_t tf_launch_decode(const DecodeArgs &a, int which, hipStream_t s);
+// Grouping alone (one workgroup): pairs, item records, counts and offsets.
+hipError_t tf_launch_group(const DecodeArgs &a, hipStream_t s);
 // Prefill combine: y = y_s + sum over ranks of y_e -> fp16.
 hipError_t tf_launch_prefill_combine(const DecodeArgs &a, hipStream_t s);
 // Prefill on the matrix cores after the router launch (items of at most 16

@@ -281,7 +281,7 @@ hipError_t tf_launch_prefill_mfma(const DecodeArgs &a0, int max_items, hipStream
     const int ttiles = (a.T + MM_TOK - 1) / MM_TOK;
     a.a_shared_blocks = ttiles * (a.fs / 32);
     const int n_gu = a.a_shared_blocks + max_items * (a.f / 32);
-    TF_LAUNCH(TF_KERNEL_ROUTED_GATEUP_SHARED_DOWN, k_mm_gateup, dim3(n_gu), dim3(WG), 0, s, a);
+    TF_LAUNCH(TF_KERNEL_PREFILL_GATEUP, k_mm_gateup, dim3(n_gu), dim3(WG), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     a.b_shared_blocks = ttiles * (a.d / 64);

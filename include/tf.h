@@ -171,14 +171,36 @@ tf_status tf_moe_prefill_chunk(const tf_moe_layer *L, const uint16_t *x, int32_t
                                uint16_t *y, float *y32, int32_t *ids, float *weights,
                                hipStream_t s, void *ws, size_t ws_bytes);
 
+/* Grouping of a chunk's (token, rank) pairs by expert, the step that lets
+ * one fetched expert serve several rows of a prefill chunk (shilu.ai README
+ * translation, "推理引擎的工作原理").  tf_moe_prefill_chunk and batched
+ * tf_moe_layer_fwd run the same code after their top-k; this call runs it
+ * alone on given ids.
+ *   ids     [T][top_k] int32 device, in [0, n_experts) and distinct within a
+ *           token (ids out of range are clamped; a repeated id leaves the
+ *           outputs unspecified but in range).
+ *   counts  [n_experts] int32 device out: pairs per expert.
+ *   offsets [n_experts + 1] int32 device out: exclusive prefix sums of counts.
+ *   pairs   [T * top_k] int32 device out: pair index t*top_k + r, sorted by
+ *           (expert, t, r); expert e owns pairs[offsets[e] .. offsets[e+1]).
+ * 1 <= top_k <= 16, top_k <= n_experts <= 1024, T <= 128 (TF_E_SHAPE);
+ * T == 0 returns TF_OK with no launch.  One workgroup, stream-ordered.
+ * ws: tf_group_workspace_bytes(n_experts, T, top_k) bytes, 256-B aligned. */
+size_t tf_group_workspace_bytes(int32_t n_experts, int32_t T, int32_t top_k);
+tf_status tf_group_by_expert(const int32_t *ids, int32_t T, int32_t top_k, int32_t n_experts,
+                             int32_t *counts, int32_t *offsets, int32_t *pairs, void *ws,
+                             size_t ws_bytes, hipStream_t s);
+
 /* ------------------------------------------------------------ profiling */
 /* Kernel ids of the hot path (for tf_profile_kernel). */
 enum {
     TF_KERNEL_ROUTER_SHARED_GATEUP = 1,      /* decode A: router + top-k + shared gate/up */
     TF_KERNEL_ROUTED_GATEUP_SHARED_DOWN = 2, /* decode B: routed gate/up + shared down    */
     TF_KERNEL_DOWN_COMBINE = 4,              /* decode C: routed down + combine -> y      */
-    TF_KERNEL_PREFILL_DOWN = 8,              /* prefill: routed down per expert -> y_e    */
-    TF_KERNEL_PREFILL_COMBINE = 16           /* prefill: y_s + sum of y_e -> y            */
+    TF_KERNEL_PREFILL_DOWN = 8,              /* prefill: shared and per-item down (MFMA)  */
+    TF_KERNEL_PREFILL_COMBINE = 16,          /* prefill: y_s + sum of y_e -> y            */
+    TF_KERNEL_PREFILL_GATEUP = 32,           /* prefill: shared and per-item gate/up (MFMA) */
+    TF_KERNEL_GROUP = 64                     /* tf_group_by_expert                        */
 };
 /* Arm a one-shot timer: the next launch, by this host thread, of the named
  * kernel goes through hipExtLaunchKernel with `start` recorded when the

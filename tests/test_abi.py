@@ -119,3 +119,21 @@ def test_slot_cache_create_argument_errors():
     assert lib.tf_slot_cache_lookup(None, 0, p, 8, None, None) == _lib.TF_E_ARG
     assert lib.tf_slot_cache_fill(None, 0, None, None, None) == _lib.TF_E_ARG
     assert lib.tf_slot_cache_bytes_filled(None) == -1
+
+
+def test_group_argument_errors():
+    lib = tfa.load()
+    p = ctypes.c_void_p(1 << 20)
+    ws = ctypes.c_void_p(1 << 28)
+    need = lib.tf_group_workspace_bytes(128, 128, 8)
+    assert need >= 256 + 4 * 16 * (128 + 1024)
+    g = lib.tf_group_by_expert
+    assert g(p, 0, 8, 128, p, p, p, ws, need, None) == 0                              # T=0
+    assert g(p, 129, 8, 128, p, p, p, ws, 1 << 30, None) == _lib.TF_E_SHAPE          # T > 128
+    assert g(p, 4, 17, 128, p, p, p, ws, 1 << 30, None) == _lib.TF_E_SHAPE           # k > 16
+    assert g(p, 4, 8, 4, p, p, p, ws, 1 << 30, None) == _lib.TF_E_SHAPE              # E < k
+    assert g(p, 4, 8, 1025, p, p, p, ws, 1 << 30, None) == _lib.TF_E_SHAPE           # E > 1024
+    assert g(None, 4, 8, 128, p, p, p, ws, 1 << 30, None) == _lib.TF_E_ARG
+    assert g(p, 4, 8, 128, p, p, p, ctypes.c_void_p((1 << 28) + 4), 1 << 30, None) == _lib.TF_E_ALIGN
+    assert g(p, 128, 8, 128, p, p, p, ws, need - 1, None) == _lib.TF_E_NOMEM
+    assert b"workspace" in lib.tf_last_error()

@@ -429,22 +429,32 @@ def run_stack(args):
         rows = ids_f[:, :(nsteps + warm) * B].reshape(L, nsteps + warm, B * k)
         distinct = float(np.mean([[len(np.unique(r)) for r in lay] for lay in rows]))
         step_bytes = L * (core + distinct * blob + 4 * B * d)
-        kern = _profile(lib, _hip(), {
-            _lib.TF_KERNEL_ROUTER_SHARED_GATEUP: "router_shared_gateup",
-            _lib.TF_KERNEL_ROUTED_GATEUP_SHARED_DOWN: "routed_gateup_shared_down",
-            _lib.TF_KERNEL_DOWN_COMBINE: "down_combine"}, step, min(args.prof_steps, 100), stream)
+        nexp = B * k if B * k < distinct else distinct
+        if B == 1:   # decode kernels A, B, C; B = routed gate/up + shared down
+            names = {_lib.TF_KERNEL_ROUTER_SHARED_GATEUP: "router_shared_gateup",
+                     _lib.TF_KERNEL_ROUTED_GATEUP_SHARED_DOWN: "routed_gateup_shared_down",
+                     _lib.TF_KERNEL_DOWN_COMBINE: "down_combine"}
+            gemv = {"routed_gateup_shared_down": nexp * 2 * qb(f, d) + qb(d, fs)}
+        else:        # grouped step: router + grouping, gate/up, down, combine
+            names = {_lib.TF_KERNEL_ROUTER_SHARED_GATEUP: "router_topk_group",
+                     _lib.TF_KERNEL_PREFILL_GATEUP: "gateup_mfma",
+                     _lib.TF_KERNEL_PREFILL_DOWN: "down_mfma",
+                     _lib.TF_KERNEL_PREFILL_COMBINE: "combine"}
+            gemv = {"gateup_mfma": nexp * 2 * qb(f, d) + 2 * qb(fs, d),
+                    "down_mfma": nexp * qb(d, f) + qb(d, fs)}
+        kern = _profile(lib, _hip(), names, step, min(args.prof_steps, 100), stream)
         us = ms * 1e3 / steps
-        kb = (B * k if B * k < distinct else distinct) * 2 * qb(f, d) + qb(d, fs)
-        dur_b = kern["routed_gateup_shared_down"]["avg_us"] * 1e-6
+        gk = {}
+        for name, kb in gemv.items():
+            dur = kern[name]["avg_us"] * 1e-6
+            gk[name] = {"bytes_per_launch": int(kb), "GBps": round(kb / dur / 1e9, 1),
+                        "frac": round(kb / dur / 1e9 / HBM_PEAK_GBPS, 4)}
         res[f"batch{B}"] = {
             "tokens_per_s": round(B * steps / (ms / 1e3), 1), "us_per_step": round(us, 2),
             "distinct_experts_per_layer": round(distinct, 2), "step_bytes": int(step_bytes),
             "GBps": round(step_bytes / (us * 1e-6) / 1e9, 1),
             "frac_of_hbm_peak": round(step_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-            "gemv_kernel": {"name": "routed_gateup_shared_down", "bytes_per_launch": int(kb),
-                            "GBps": round(kb / dur_b / 1e9, 1),
-                            "frac": round(kb / dur_b / 1e9 / HBM_PEAK_GBPS, 4)},
-            "kernels_per_layer": kern}
+            "gemv_kernels": gk, "kernels_per_layer": kern}
         del X, F, Y, IDS, W, ws, graphs
         torch.cuda.synchronize()
     return {"metric": "30-layer resident MoE stack decode tokens/s", "workload": wl.name,

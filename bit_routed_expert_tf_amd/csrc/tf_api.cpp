@@ -97,6 +97,46 @@ void fill_common(DecodeArgs &a, const tf_moe_layer *L, int T) {
     a.topk = 1;
 }
 
+// Workspace of a grouped step (prefill, decode of T >= 2): the decode layout
+// plus the per-pair down outputs y_e fp32 [T*k][d].
+size_t grouped_ws_bytes(const tf_moe_layer *L, int T) {
+    const WsLayout w = decode_layout(L->d_model, L->d_ff, L->d_ff_shared, L->n_experts, L->top_k, T);
+    return w.total + up256((size_t)4 * T * L->top_k * L->d_model);
+}
+
+// Grouped step of T >= 2 tokens, all experts resident (shilu.ai README
+// translation, "推理引擎的工作原理": a chunk's tokens share each fetched
+// expert).  Arguments are checked by the caller.
+//   A  router rows + top-k per token, grouping into items of <= 16 tokens
+//   B  gate/up on the matrix cores: shared expert per 16 tokens, routed
+//      expert per item -> h_s, h_r
+//   C  down on the matrix cores -> y_s, y_e per pair
+//   D  y = y_s + sum over ranks of y_e, fp16
+hipError_t grouped_step(const tf_moe_layer *L, const uint16_t *x, int T, const int32_t *forced,
+                        uint16_t *y, float *y32, int32_t *ids, float *weights, void *ws,
+                        hipStream_t s) {
+    const WsLayout w = decode_layout(L->d_model, L->d_ff, L->d_ff_shared, L->n_experts, L->top_k, T);
+    DecodeArgs a;
+    fill_common(a, L, T);
+    a.x = x; a.forced = forced; a.ids = ids; a.weights = weights; a.y = y; a.y32 = y32;
+    a.hdr = at<uint32_t>(ws, w.hdr);
+    a.logits = at<double>(ws, w.logits);
+    a.items = at<int32_t>(ws, w.items);
+    a.pairs = at<int32_t>(ws, w.pairs);
+    a.h_s = at<uint4>(ws, w.hs);
+    a.y_s = at<float>(ws, w.ys);
+    a.h_r = at<uint4>(ws, w.hr);
+    a.y_e = at<float>(ws, w.total);
+    a.do_group = 1;
+    a.tbi = 16;   // items of up to 16 tokens: one MFMA tile each
+    const int P = T * a.k;
+    const int max_items = P < a.E + P / a.tbi ? P : a.E + P / a.tbi;
+    a.a_router_blocks = ((a.E + 3) / 4) * T;
+    hipError_t e = tf_launch_decode(a, STAGE_A, s);
+    if (e == hipSuccess) e = tf_launch_grouped(a, max_items, s);
+    return e;
+}
+
 }  // namespace
 
 void tf_set_error(const char *msg) { g_err = msg; }
@@ -228,6 +268,7 @@ tf_status tf_profile_kernel(int32_t kernel, hipEvent_t start, hipEvent_t stop) {
 
 size_t tf_moe_workspace_bytes(const tf_moe_layer *L, int32_t T) {
     if (!L || T <= 0) return 0;
+    if (T >= 2) return grouped_ws_bytes(L, T);
     return decode_layout(L->d_model, L->d_ff, L->d_ff_shared, L->n_experts, L->top_k, T).total;
 }
 
@@ -242,13 +283,19 @@ tf_status tf_moe_layer_fwd(const tf_moe_layer *L, const uint16_t *x, int32_t T,
     if (!x || !y || !ids || !weights || !ws) return fail(TF_E_ARG, "NULL x/y/ids/weights/ws");
     if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, 256) || (y32 && !aligned(y32, 16)))
         return fail(TF_E_ALIGN, "x/y/y32 16-byte, ws 256-byte alignment");
-    const WsLayout w = decode_layout(L->d_model, L->d_ff, L->d_ff_shared, L->n_experts, L->top_k, T);
-    if (ws_bytes < w.total) return fail(TF_E_NOMEM, "workspace too small (%zu < %zu)", ws_bytes, w.total);
+    const size_t need = tf_moe_workspace_bytes(L, T);
+    if (ws_bytes < need) return fail(TF_E_NOMEM, "workspace too small (%zu < %zu)", ws_bytes, need);
     if (cache) {
         if (T != 1) return fail(TF_E_ARG, "the slot-cache path takes one token per call");
         st = tf_slot_check_layer(cache, L, layer);
         if (st) return st;
     }
+    hipError_t e;
+    if (T >= 2) {   // several tokens: grouped by expert, as a prefill chunk
+        e = grouped_step(L, x, T, forced_ids, y, y32, ids, weights, ws, compute);
+        return e == hipSuccess ? TF_OK : hip_fail(e, "grouped decode launch");
+    }
+    const WsLayout w = decode_layout(L->d_model, L->d_ff, L->d_ff_shared, L->n_experts, L->top_k, T);
 
     DecodeArgs a;
     fill_common(a, L, T);
@@ -271,7 +318,6 @@ tf_status tf_moe_layer_fwd(const tf_moe_layer *L, const uint16_t *x, int32_t T,
     const int n_shared_a = (a.fs / (2 * rpw)) * ((T + a.tbx - 1) / a.tbx);
     const int n_routed_b = (a.f / (2 * rpw)) * max_items;
     const int n_shared_b = (a.d / (4 * rpw)) * T;   // one token per shared-down block
-    hipError_t e;
 
     if (!cache) {
         a.a_router_blocks = n_router;
@@ -315,19 +361,12 @@ extern "C" {
 
 size_t tf_prefill_workspace_bytes(const tf_moe_layer *L, int32_t T) {
     if (!L || T <= 0) return 0;
-    const WsLayout w = decode_layout(L->d_model, L->d_ff, L->d_ff_shared, L->n_experts, L->top_k, T);
-    return w.total + up256((size_t)4 * T * L->top_k * L->d_model);
+    return grouped_ws_bytes(L, T);
 }
 
 // Chunked prefill (shilu.ai README translation, "推理引擎的工作原理": chunks
-// of at most 128 tokens, so each fetched expert serves several rows).  The
-// chunk's (token, rank) pairs are grouped by expert and every expert's
-// weights are read once:
-//   A  router rows + top-k per token, grouping into items of <= 16 tokens
-//   B  gate/up on the matrix cores: shared expert per 16 tokens, routed
-//      expert per item -> h_s, h_r
-//   C  down on the matrix cores -> y_s, y_e per pair
-//   D  y = y_s + sum over ranks of y_e, fp16
+// of at most 128 tokens, so each fetched expert serves several rows): the
+// grouped step, whose every expert's weights are read once per chunk.
 tf_status tf_moe_prefill_chunk(const tf_moe_layer *L, const uint16_t *x, int32_t T, uint16_t *y,
                                float *y32, int32_t *ids, float *weights, hipStream_t s, void *ws,
                                size_t ws_bytes) {
@@ -342,25 +381,7 @@ tf_status tf_moe_prefill_chunk(const tf_moe_layer *L, const uint16_t *x, int32_t
     if (T == 1)   // a single token is a decode step
         return tf_moe_layer_fwd(L, x, 1, nullptr, y, y32, ids, weights, nullptr, 0, s, s, ws,
                                 ws_bytes);
-    const WsLayout w = decode_layout(L->d_model, L->d_ff, L->d_ff_shared, L->n_experts, L->top_k, T);
-    DecodeArgs a;
-    fill_common(a, L, T);
-    a.x = x; a.ids = ids; a.weights = weights; a.y = y; a.y32 = y32;
-    a.hdr = at<uint32_t>(ws, w.hdr);
-    a.logits = at<double>(ws, w.logits);
-    a.items = at<int32_t>(ws, w.items);
-    a.pairs = at<int32_t>(ws, w.pairs);
-    a.h_s = at<uint4>(ws, w.hs);
-    a.y_s = at<float>(ws, w.ys);
-    a.h_r = at<uint4>(ws, w.hr);
-    a.y_e = at<float>(ws, w.total);
-    a.do_group = 1;
-    a.tbi = 16;   // items of up to 16 tokens: one MFMA token tile each
-    const int P = T * a.k;
-    const int max_items = P < a.E + P / a.tbi ? P : a.E + P / a.tbi;
-    a.a_router_blocks = ((a.E + 3) / 4) * T;
-    hipError_t e = tf_launch_decode(a, STAGE_A, s);
-    if (e == hipSuccess) e = tf_launch_prefill_mfma(a, max_items, s);
+    const hipError_t e = grouped_step(L, x, T, nullptr, y, y32, ids, weights, ws, s);
     return e == hipSuccess ? TF_OK : hip_fail(e, "prefill launch");
 }
 

@@ -64,9 +64,10 @@ hipError_t tf_launch_decode(const DecodeArgs &a, int which, hipStream_t s);
 hipError_t tf_launch_group(const DecodeArgs &a, hipStream_t s);
 // Prefill combine: y = y_s + sum over ranks of y_e -> fp16.
 hipError_t tf_launch_prefill_combine(const DecodeArgs &a, hipStream_t s);
-// Prefill on the matrix cores after the router launch (items of at most 16
-// tokens): gate/up, down and the combine.
-hipError_t tf_launch_prefill_mfma(const DecodeArgs &a, int max_items, hipStream_t s);
+// Grouped steps (prefill, decode of more than one token) on the matrix cores
+// after the router launch (items of at most 16 tokens): gate/up, down and
+// the combine.
+hipError_t tf_launch_grouped(const DecodeArgs &a, int max_items, hipStream_t s);
 // Lanes per weight row used by stages A and B for these shapes (8 or 16).
 int tf_decode_lpr(const DecodeArgs &a);
 

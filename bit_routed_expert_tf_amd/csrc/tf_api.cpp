@@ -107,8 +107,8 @@ size_t grouped_ws_bytes(const tf_moe_layer *L, int T) {
 // Grouped step of T >= 2 tokens, all experts resident (shilu.ai README
 // translation, "推理引擎的工作原理": a chunk's tokens share each fetched
 // expert).  Arguments are checked by the caller.
-//   A  router rows + top-k per token, grouping into items of <= 16 tokens
-//   B  gate/up on the matrix cores: shared expert per 16 tokens, routed
+//   A  router rows + top-k per token, grouping into items of <= 4 tokens
+//   B  gate/up on the matrix cores: shared expert per 4 tokens, routed
 //      expert per item -> h_s, h_r
 //   C  down on the matrix cores -> y_s, y_e per pair
 //   D  y = y_s + sum over ranks of y_e, fp16
@@ -128,7 +128,7 @@ hipError_t grouped_step(const tf_moe_layer *L, const uint16_t *x, int T, const i
     a.h_r = at<uint4>(ws, w.hr);
     a.y_e = at<float>(ws, w.total);
     a.do_group = 1;
-    a.tbi = 16;   // items of up to 16 tokens: one MFMA tile each
+    a.tbi = 4;   // items of up to four tokens: one grouped unit each
     const int P = T * a.k;
     const int max_items = P < a.E + P / a.tbi ? P : a.E + P / a.tbi;
     a.a_router_blocks = ((a.E + 3) / 4) * T;

@@ -283,7 +283,7 @@ __device__ void topk_block(const DecodeArgs &a, int t, int tid, unsigned char *l
     int *sel = reinterpret_cast<int *>(ex + 16);             // [16]
     int *part = sel + 16;                                    // [256]
     float *lf = reinterpret_cast<float *>(part + 256);       // [E + 8], -inf padded
-    __syncthreads();
+    lds_barrier();
     for (int i = tid; i < a.E + 8; i += WG) {
         double v = -__builtin_inf();
         if (i < a.E) {
@@ -293,7 +293,7 @@ __device__ void topk_block(const DecodeArgs &a, int t, int tid, unsigned char *l
         }
         lf[i] = (float)v;
     }
-    __syncthreads();
+    lds_barrier();
     if (a.forced) {
         uint32_t fl = 0;
         if (tid < a.k) {
@@ -301,7 +301,7 @@ __device__ void topk_block(const DecodeArgs &a, int t, int tid, unsigned char *l
             if (id < 0 || id >= a.E) { fl |= TF_FLAG_ID_RANGE; id = id < 0 ? 0 : a.E - 1; }
             sel[tid] = id;
         }
-        __syncthreads();
+        lds_barrier();
         if (tid < a.k)
             for (int r = 0; r < tid; ++r)
                 if (sel[r] == sel[tid]) fl |= TF_FLAG_ID_REPEAT;
@@ -324,7 +324,7 @@ __device__ void topk_block(const DecodeArgs &a, int t, int tid, unsigned char *l
                 }
             }
             part[tid] = gt | (eq << 16);
-            __syncthreads();
+            lds_barrier();
             if (tid < 128 && i < a.E) {
                 const int p0 = part[tid], p1 = part[tid + 128];
                 int c = (p0 & 0xFFFF) + (p1 & 0xFFFF);
@@ -336,16 +336,16 @@ __device__ void topk_block(const DecodeArgs &a, int t, int tid, unsigned char *l
                 }
                 if (c < a.k) sel[c] = i;
             }
-            __syncthreads();
+            lds_barrier();
         }
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < a.k) {
         double m = l[sel[0]];
         for (int r = 1; r < a.k; ++r) m = fmax(m, l[sel[r]]);
         ex[tid] = (double)expf((float)(l[sel[tid]] - m));
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < a.k) {
         double s = 0.0;
         for (int r = 0; r < a.k; ++r) s += ex[r];
@@ -378,16 +378,16 @@ __device__ void group_block(const DecodeArgs &a, int tid, unsigned char *lds) {
     int *offs = cnt + E;                                      // [E]
     int *iidx = offs + E;                                     // [E] item index
     int *wsum = iidx + E;                                     // [4][2]
-    __syncthreads();
+    lds_barrier();
     for (int i = tid; i < E * NW; i += WG) mask[i] = 0;
     for (int p = tid; p < P; p += WG) st_dev(a.pairs + p, (int32_t)p);
-    __syncthreads();
+    lds_barrier();
     for (int p = tid; p < P; p += WG) {
         const int e = min(max((int)ld_dev(a.ids + p), 0), E - 1);
         const int t = p / a.k;
         atomicOr(&mask[e * NW + (t >> 5)], 1u << (t & 31));
     }
-    __syncthreads();
+    lds_barrier();
     // counts, and exclusive scans of the counts and of (count > 0); thread
     // tid owns experts [tid*per, tid*per + per)
     const int per = (E + WG - 1) / WG, e0 = tid * per, e1 = min(E, e0 + per);
@@ -405,7 +405,7 @@ __device__ void group_block(const DecodeArgs &a, int tid, unsigned char *lds) {
         if (lane >= o) { ic += vc; in += vn; }
     }
     if (lane == WAVE - 1) { wsum[2 * w] = ic; wsum[2 * w + 1] = in; }
-    __syncthreads();
+    lds_barrier();
     int oc = ic - sc, on = in - sn;
     for (int q = 0; q < w; ++q) { oc += wsum[2 * q]; on += wsum[2 * q + 1]; }
     for (int e = e0; e < e1; ++e) {
@@ -422,14 +422,14 @@ __device__ void group_block(const DecodeArgs &a, int tid, unsigned char *lds) {
         }
         if (tid == WG - 1) st_dev(a.g_offsets + E, (int32_t)oc);   // the total
     }
-    __syncthreads();
+    lds_barrier();
     for (int e = tid; e < E; e += WG)
         for (int q = 0; q < cnt[e]; q += a.tbi)
             st_dev(reinterpret_cast<uint4 *>(a.items + ITEM_INTS * (iidx[e] + q / a.tbi)),
                    make_uint4((uint32_t)e, (uint32_t)(offs[e] + q),
                               (uint32_t)min(a.tbi, cnt[e] - q), 0u));
     stores_done();
-    __syncthreads();   // the default positions are written before the scatter
+    lds_barrier();   // the default positions are written before the scatter
     for (int p = tid; p < P; p += WG) {
         const int e = min(max((int)ld_dev(a.ids + p), 0), E - 1);
         const int t = p / a.k;
@@ -493,7 +493,7 @@ __device__ void router_block(const DecodeArgs &a, int b, int tid, unsigned char 
             reinterpret_cast<double2 *>(xd + 16 * tid)[i] = make_double2(v[2 * i], v[2 * i + 1]);
         x16[tid] = s;
     }
-    __syncthreads();
+    lds_barrier();
     double acc = 0.0;
 #pragma unroll
     for (int j = 0; j < JR; ++j) {
@@ -515,23 +515,23 @@ __device__ void router_block(const DecodeArgs &a, int b, int tid, unsigned char 
     acc = wave_sum_f64(acc);
     if (lane == 0 && row_ok) st_dev(a.logits + (size_t)t * a.E + e, acc);
     stores_done();
-    __syncthreads();
+    lds_barrier();
     if (tid == 0) {
         const uint32_t old = atomicAdd(a.hdr + HDR_TICKET + t, 1u);
         *flag = old == (uint32_t)(nrb - 1);
     }
-    __syncthreads();
+    lds_barrier();
     if (!*flag) return;
     if (tid == 0) st_dev(a.hdr + HDR_TICKET + t, 0u);
     topk_block(a, t, tid, lds);
     if (!a.do_group || a.T == 1) return;
     stores_done();
-    __syncthreads();
+    lds_barrier();
     if (tid == 0) {
         const uint32_t old = atomicAdd(a.hdr + HDR_TICKET + a.T, 1u);
         reinterpret_cast<int *>(lds)[0] = old == (uint32_t)(a.T - 1);
     }
-    __syncthreads();
+    lds_barrier();
     if (!reinterpret_cast<int *>(lds)[0]) return;
     if (tid == 0) st_dev(a.hdr + HDR_TICKET + a.T, 0u);
     group_block(a, tid, lds);
@@ -639,7 +639,7 @@ __device__ void gateup_block(const DecodeArgs &a, int b, int tid, unsigned char 
         } else {
             for (int i = 0; i < ns; ++i) one(i);
         }
-        __syncthreads();
+        lds_barrier();
         if (tid < RWG * ns) {
             const int row = tid % RWG, i = tid / RWG;
             const int half = row / RPW, rr = row % RPW;
@@ -647,7 +647,7 @@ __device__ void gateup_block(const DecodeArgs &a, int b, int tid, unsigned char 
             const float uv = gu[((2 + half) * RPW + rr) * MAX_TB + i];
             hv[i * RWG + row] = gelu_f(gv, a.act) * uv;
         }
-        __syncthreads();
+        lds_barrier();
         if (tid < (RWG / 8) * ns) {
             const int i = tid / (RWG / 8), sub = tid % (RWG / 8);
             const float c = coef[0] * (i == 0) + coef[1] * (i == 1) + coef[2] * (i == 2) +
@@ -669,7 +669,7 @@ __device__ void gateup_block(const DecodeArgs &a, int b, int tid, unsigned char 
     tile_load_q<LPR, J>(tl, mm, row0, d, lane);
     xs_store(X, ns0, d, xst, tid);
     tile_store_sb(tl, lsb + w * RPW * G, G, lane);
-    __syncthreads();
+    lds_barrier();
     finish(ns0);
 }
 
@@ -695,7 +695,7 @@ __device__ void shared_down_block(const DecodeArgs &a, int b, int tid, unsigned 
     tile_load_q<LPR, J>(tl, dn, row0, K, lane);
     hs_store(Hs, 1, K, hst, tid);
     tile_store_sb(tl, lsb + w * RPW * G, G, lane);
-    __syncthreads();
+    lds_barrier();
     auto one = [&](int i) {
         const float v = row_sum<LPR>(tile_dot<LPR, J, true>(
             tl, lsb + w * RPW * G, G, reinterpret_cast<const uint4 *>(hst),
@@ -765,7 +765,7 @@ __global__ __launch_bounds__(256, 4) void k_stage_c(DecodeArgs a) {
         const bool va = w < np, vb = w + 4 < np;
         const int ea = a.gemv_slot ? a.gemv_slot[pa] : a.ids[pa];
         const int eb = a.gemv_slot ? a.gemv_slot[pb] : a.ids[pb];
-        if (p0 != lo) __syncthreads();   // the previous pass is done with LDS
+        if (p0 != lo) lds_barrier();   // the previous pass is done with LDS
         HStage<(JF * 8 * 8 * 8 + 255) / 256, (JF * 8 * 8 + 255) / 256> Hs;   // 8 rows
         hs_load(Hs, a.h_r + (size_t)p0 * 10 * H, np, K, tid);
         Mat ga, ua, da, gb, ub, db;
@@ -779,7 +779,7 @@ __global__ __launch_bounds__(256, 4) void k_stage_c(DecodeArgs a) {
         hs_store(Hs, np, K, hst, tid);
         tile_store_sb(ta, lsb + (w * 2) * 8 * G, G, lane);
         tile_store_sb(tb, lsb + (w * 2 + 1) * 8 * G, G, lane);
-        __syncthreads();
+        lds_barrier();
         if (va) {
             const unsigned char *st = hst + (size_t)(pa - p0) * hsb;
             acc += tile_dot<LPR, JF, true>(ta, lsb + (w * 2) * 8 * G, G,
@@ -799,7 +799,7 @@ __global__ __launch_bounds__(256, 4) void k_stage_c(DecodeArgs a) {
     }
     acc = row_sum<LPR>(acc);
     if ((lane & 7) == 0) part[w * 8 + (lane >> 3)] = acc;
-    __syncthreads();
+    lds_barrier();
     if (tid < 8) {
         const float sum = ((part[tid] + part[8 + tid]) + part[16 + tid]) + part[24 + tid];
         const size_t o = (size_t)t * a.d + row0 + tid;

@@ -116,6 +116,15 @@ __device__ __forceinline__ void stores_done() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_s_waitcnt(0);
 }
+// Workgroup barrier after this thread's LDS writes have completed.  The
+// explicit LDS-counter wait matters: without it the compiler may reach the
+// barrier with LDS stores still in flight, and a wave past the barrier has
+// been seen to read stale LDS data.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited on
+    __syncthreads();
+}
+
 // DPP lane moves (row = 16 lanes).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {

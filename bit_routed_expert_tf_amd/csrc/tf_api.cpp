@@ -11,6 +11,7 @@
 #include <string>
 
 #include "tf_internal.h"
+#include "tf_layer.h"
 #include "tf_slot.h"
 
 namespace {
@@ -65,7 +66,7 @@ tf_status check_layer(const tf_moe_layer *L) {
 
 // Decode workspace layout (offsets in bytes).
 struct WsLayout {
-    size_t hdr, logits, items, pairs, hs, ys, hr, total;
+    size_t hdr, logits, items, pairs, hs, ys, hr, xb, total;
 };
 
 WsLayout decode_layout(int d, int f, int fs, int E, int k, int T) {
@@ -78,6 +79,7 @@ WsLayout decode_layout(int d, int f, int fs, int E, int k, int T) {
     w.hs = o; o += up256(h_row_bytes(fs) * T);
     w.ys = o; o += up256((size_t)4 * T * d);
     w.hr = o; o += up256(h_row_bytes(f) * T * k);
+    w.xb = o; o += up256((size_t)16 * tfk::xb_row_u4(d) * T);
     w.total = o;
     return w;
 }
@@ -127,6 +129,7 @@ hipError_t grouped_step(const tf_moe_layer *L, const uint16_t *x, int T, const i
     a.y_s = at<float>(ws, w.ys);
     a.h_r = at<uint4>(ws, w.hr);
     a.y_e = at<float>(ws, w.total);
+    a.xb = at<uint4>(ws, w.xb);
     a.do_group = 1;
     a.tbi = 4;   // items of up to four tokens: one grouped unit each
     const int P = T * a.k;

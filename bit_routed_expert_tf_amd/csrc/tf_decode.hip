@@ -493,6 +493,17 @@ __device__ void router_block(const DecodeArgs &a, int b, int tid, unsigned char 
             reinterpret_cast<double2 *>(xd + 16 * tid)[i] = make_double2(v[2 * i], v[2 * i + 1]);
         x16[tid] = s;
     }
+    if (a.xb && b == t * nrb) {   // the token's first router workgroup: x in B-operand form
+        uint4 *row = a.xb + (size_t)t * xb_row_u4(d);
+        float X = 0.f, C = 0.f;
+        if (tid < NC) xb_produce(xv0, xv1, row, tid, X, C);
+        // a group is four word pairs: lanes 4g .. 4g+3
+        X += dpp_f<DPP_XOR1>(X);
+        C += dpp_f<DPP_XOR1>(C);
+        X += dpp_f<DPP_XOR2>(X);
+        C += dpp_f<DPP_XOR2>(C);
+        if (tid < NC && !(tid & 3)) reinterpret_cast<float2 *>(row + d / 8)[tid >> 2] = make_float2(X, C);
+    }
     lds_barrier();
     double acc = 0.0;
 #pragma unroll

@@ -51,8 +51,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int UT = 4;     // tokens per unit
-constexpr int KCH = 8;    // groups per staged K chunk (512 columns)
-constexpr int NRND = 2;   // rounds of four groups per chunk
 
 // Hidden rows between the grouped gate/up and down launches, F values:
 // word pairs (16 values) of 64 bytes [part hi: even | odd/16][part lo:
@@ -86,31 +84,24 @@ __device__ __forceinline__ half8 as_half8(uint4 v) {
 __device__ __forceinline__ f32x4 mfma(half8 a, half8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
-// An fp16 pair divided by 16 (exact unless the result is subnormal).
-__device__ __forceinline__ uint32_t div16(uint32_t p) {
-    const h2_t v = __builtin_bit_cast(h2_t, p) * h2_t{(_Float16)0.0625f, (_Float16)0.0625f};
-    return __builtin_bit_cast(uint32_t, v);
-}
-__device__ __forceinline__ float hsum2(uint32_t p) {
-    return h2f((uint16_t)(p & 0xFFFF)) + h2f((uint16_t)(p >> 16));
-}
-// Slot i of four values held as separate variables (no array, so nothing is
 // indexed through memory).
 template <typename T>
 __device__ __forceinline__ T pick4(int i, T v0, T v1, T v2, T v3) {
     return i == 0 ? v0 : i == 1 ? v1 : i == 2 ? v2 : v3;
 }
 
-template <int PARTS>
+// KC groups per staged K chunk.
+template <int PARTS, int KC>
 struct GLds {
     // the chunk's activations: [token][word pair][part][even | odd/16], one
     // 16-byte entry each; rows padded so that the tokens of a B read fall on
     // different banks
-    uint4 xs[UT][KCH * 4 * PARTS * 2 + 1];
-    float2 xc[UT][KCH + 1];     // (X, C) per token and group of the chunk
-    float2 sb[KCH][64 + 4];     // (scale, bias) per group and row of the block
+    uint4 xs[UT][KC * 4 * PARTS * 2 + 1];
+    float2 xc[UT][KC + 1];      // (X, C) per token and group of the chunk
+    float2 sb[KC][64 + 4];      // (scale, bias) per group and row of the block
     float out[2][32][UT + 1];   // gate and up sums of a unit
     uint4 zero[2 * PARTS];      // B operand of the columns a lane block does not feed
+    uint4 rec[2][3];            // item record of the next unit, by unit parity
 };
 
 // Item record as loaded (expert, begin, count, -, pairs[4], weights[4]).
@@ -119,7 +110,8 @@ struct Rec {
 };
 
 // One unit: the expert blob, routed or shared, its hidden size, the row
-// tile, and up to four (source row, destination row, coefficient) slots.
+// tile, its chunk count and up to four (source row, destination row,
+// coefficient) slots.
 struct Unit {
     const uint8_t *blob;
     int routed, F, rt, nt, nch;
@@ -129,8 +121,9 @@ struct Unit {
 };
 
 // Unit u of a launch: shared units first (token quads x row tiles), then
-// routed units (items x row tiles).
-template <bool DOWN>
+// routed units (items x row tiles).  The chunk count is even (two buffers
+// alternate; an odd count gets an empty chunk).
+template <bool DOWN, int KC, int DEPTH>
 __device__ Unit unit_of(const DecodeArgs &a, int u, const Rec &rc, int ns, int tiles_s,
                         int tiles_r) {
     Unit U;
@@ -148,7 +141,7 @@ __device__ Unit unit_of(const DecodeArgs &a, int u, const Rec &rc, int ns, int t
         U.c0 = U.c1 = U.c2 = U.c3 = 1.f;
     } else {
         const int v = u - ns, item = v / tiles_r;
-        U.blob = expert_blob(a, min((int)rc.r0.x, a.E - 1));
+        U.blob = expert_blob(a, min(max((int)rc.r0.x, 0), a.E - 1));
         U.routed = 1;
         U.F = a.f;
         U.rt = v - item * tiles_r;
@@ -169,16 +162,26 @@ __device__ Unit unit_of(const DecodeArgs &a, int u, const Rec &rc, int ns, int t
         U.c2 = __uint_as_float(rc.r2.z);
         U.c3 = __uint_as_float(rc.r2.w);
     }
-    U.nch = ((DOWN ? U.F : a.d) / 64 + KCH - 1) / KCH;
+    const int nc = ((DOWN ? U.F : a.d) / 64 + KC - 1) / KC;
+    U.nch = DEPTH == 2 ? (nc + 1) & ~1 : nc;
     return U;
 }
 
 // Persistent grouped GEMM.  DOWN = false: gate/up rows [32 rt, +32) (K = d)
 // into hidden rows h = coef * gelu(g) * u; DOWN = true: down rows [64 rt, +64)
 // (K = F) into fp32 rows (y_s per token, y_e per pair).
-template <bool DOWN>
-__device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1> &L) {
+// Pipeline: chunk c computes from LDS (staged at the end of chunk c - 1) and
+// from code ring c % 2 (loaded during chunk c - 2); it loads chunk c + 2 into
+// ring c % 2 and staging registers c % 2, and stages chunk c + 1 (loaded
+// during chunk c - 1) into LDS.  Chunk positions past a unit's end belong to
+// the next unit of this workgroup.
+template <bool DOWN, int KC, int DEPTH>
+__device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1, KC> &L) {
     constexpr int PARTS = DOWN ? 2 : 1;
+    constexpr int NR = KC / 4;        // rounds of four groups per chunk
+    constexpr int XW = KC / 8;        // gate/up staging: uint4 per lane per chunk
+    constexpr int HW = KC / 4;        // down staging: uint4 per lane per chunk
+    constexpr int SW = KC / 4;        // scale/bias entries per thread per chunk
     const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
     const int j = lane & 15, b = lane >> 4;
     const int d = a.d;
@@ -186,14 +189,14 @@ __device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1> &L) {
     const int ns = ((a.T + UT - 1) / UT) * tiles_s;
     const int n_items = (int)ld_dev(a.hdr + HDR_NITEMS);
     const int n_units = ns + n_items * tiles_r;
+    const int grid = (int)gridDim.x;
     int u = blockIdx.x;
     if (u >= n_units) return;
     if (tid < 2 * PARTS) L.zero[tid] = make_uint4(0, 0, 0, 0);
 
     // the item record of unit v (a valid record when v is not routed).  The
     // address takes an opaque zero, so the values stay in vector registers
-    // and nothing waits for them before their first use (uniform values
-    // would be moved to scalar registers right after the load).
+    // and nothing waits for them before their first use.
     auto load_rec = [&](int v) {
         int z = 0;
         asm volatile("" : "+v"(z));
@@ -205,9 +208,9 @@ __device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1> &L) {
         r.r2 = ld_dev(p + 2);
         return r;
     };
-    // A loaded record, used here: an ordered empty asm keeps what follows at
-    // this point (not hoisted next to the loads), then the fields move to
-    // scalar registers.
+    // a loaded record, used here: an ordered empty asm keeps what follows at
+    // this point (not hoisted next to the loads); then the fields move to
+    // scalar registers
     auto settle = [](Rec r) {
         asm volatile("" : "+v"(r.r0.x), "+v"(r.r0.y), "+v"(r.r0.z), "+v"(r.r0.w),
                           "+v"(r.r1.x), "+v"(r.r1.y), "+v"(r.r1.z), "+v"(r.r1.w),
@@ -219,16 +222,15 @@ __device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1> &L) {
         r.r2.z = uniform(r.r2.z); r.r2.w = uniform(r.r2.w);
         return r;
     };
-    // Per-unit streaming bases, all uniform and selected by value (a
-    // reference to one of two descriptors would put them in scratch memory):
-    // the wave's code matrix, the gate and up (or down) scale/bias arrays,
+    // Per-unit streaming bases, all uniform and selected by value: the wave's
+    // code matrix, the scale/bias arrays of block rows [0, 32) and [32, 64),
     // and the activation row of the token this wave stages (tj = wave; every
     // lane loads, non-stagers a valid row they then ignore, so that no load
-    // sits behind a branch).  Per-lane offsets are formed at each load.
+    // sits behind a branch).
     const int tj = w, li = lane;
     struct Str {
         const uint8_t *q;
-        const uint16_t *s0, *b0, *s1, *b1;   // rows [0, 32) and [32, 64) of the block
+        const uint16_t *s0, *b0, *s1, *b1;
         const uint4 *srow;
         int rt, G, nt, F;
     };
@@ -246,7 +248,7 @@ __device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1> &L) {
         S.s1 = DOWN ? md.s : mu.s;
         S.b1 = DOWN ? md.b : mu.b;
         const int src = pick4(min(tj, U.nt - 1), U.s0, U.s1, U.s2, U.s3);
-        if (!DOWN) S.srow = reinterpret_cast<const uint4 *>(a.x + (size_t)src * d);
+        if (!DOWN) S.srow = a.xb + (size_t)src * xb_row_u4(d);
         else S.srow = (U.routed ? a.h_r : a.h_s) + (size_t)src * mq_row_u4(U.F);
         return S;
     };
@@ -259,73 +261,77 @@ __device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1> &L) {
         r.rt = c ? x.rt : y.rt; r.G = c ? x.G : y.G; r.nt = c ? x.nt : y.nt; r.F = c ? x.F : y.F;
         return r;
     };
-    // this lane's codes of chunk c: groups 8c + b (round 0) and 8c + 4 + b
-    // (round 1), 32 bytes each, of row r0 + j
-    uint4 q[4];
-    auto qload = [&](const Str &S, int c, int rho) {
+    // this lane's codes of chunk c: group KC c + 4 rho + b of round rho, 32
+    // bytes each, of row r0 + j
+    auto qload = [&](uint4 (&q)[2 * NR], const Str &S, int c, int rho) {
         const int r0 = DOWN ? 64 * S.rt + 16 * w : 32 * S.rt + 16 * (w & 1);
-        const int g = min(KCH * c + 4 * rho + b, S.G - 1);
+        const int g = min(KC * c + 4 * rho + b, S.G - 1);
         const uint8_t *p = S.q + (size_t)(r0 + j) * (32 * S.G) + 32 * g;
         q[2 * rho] = *reinterpret_cast<const uint4 *>(p);
         q[2 * rho + 1] = *reinterpret_cast<const uint4 *>(p + 16);
     };
-    // staging loads of chunk c into registers
+    // staging loads of chunk c into registers (activation rows are already in
+    // B-operand form: these are copies)
     struct Pre {
-        uint4 v[PARTS];
+        uint4 v[DOWN ? HW : XW];
         float2 xc;
-        uint32_t sbw[2];
+        uint32_t sbw[SW];
     };
     auto fetch = [&](Pre &P, const Str &S, int c) {
-        if (!DOWN) {
-            P.v[0] = S.srow[min(64 * c + li, d / 8 - 1)];
-        } else {
+        if (!DOWN) {   // uint4 8 KC c + XW li + i; (X, C) of group KC c + li
+#pragma unroll
+            for (int i = 0; i < XW; ++i) P.v[i] = S.srow[min(8 * KC * c + XW * li + i, d / 8 - 1)];
+            P.xc = reinterpret_cast<const float2 *>(S.srow + d / 8)[min(KC * c + (li & (KC - 1)), S.G - 1)];
+        } else {       // uint4 16 KC c + HW li + i; (X, C) of half-group 2 KC c + li
             const int HU = S.F / 4;
 #pragma unroll
-            for (int i = 0; i < PARTS; ++i) P.v[i] = S.srow[min(128 * c + 2 * li + i, HU - 1)];
-            P.xc = reinterpret_cast<const float2 *>(S.srow + HU)[min(16 * c + (li & 15), S.F / 32 - 1)];
+            for (int i = 0; i < HW; ++i) P.v[i] = S.srow[min(16 * KC * c + HW * li + i, HU - 1)];
+            P.xc = reinterpret_cast<const float2 *>(S.srow + HU)[min(2 * KC * c + (li & (2 * KC - 1)), S.F / 32 - 1)];
         }
-        // thread stages group 8c + (tid & 7) of block rows tid >> 3 (from s0/b0)
-        // and 32 + (tid >> 3) (from s1/b1)
-        const int g = min(KCH * c + (tid & 7), S.G - 1);
-        const int row0 = (DOWN ? 64 * S.rt : 32 * S.rt) + (tid >> 3);
-        const int row1 = row0 + (DOWN ? 32 : 0);
-        P.sbw[0] = (uint32_t)S.s0[row0 * S.G + g] | ((uint32_t)S.b0[row0 * S.G + g] << 16);
-        P.sbw[1] = (uint32_t)S.s1[row1 * S.G + g] | ((uint32_t)S.b1[row1 * S.G + g] << 16);
+        // entry e = tid + 256 qq: block row e / KC, group KC c + e % KC; rows
+        // [0, 32) from s0/b0, [32, 64) from s1/b1 (down: one matrix)
+        const int g = min(KC * c + tid % KC, S.G - 1);
+#pragma unroll
+        for (int qq = 0; qq < SW; ++qq) {
+            const int rr = tid / KC + 256 / KC * qq;
+            if (DOWN || qq < SW / 2) {
+                const int row = (DOWN ? 64 * S.rt : 32 * S.rt) + rr;
+                P.sbw[qq] = (uint32_t)S.s0[row * S.G + g] | ((uint32_t)S.b0[row * S.G + g] << 16);
+            } else {
+                const int row = 32 * S.rt + rr - 32;
+                P.sbw[qq] = (uint32_t)S.s1[row * S.G + g] | ((uint32_t)S.b1[row * S.G + g] << 16);
+            }
+        }
     };
     auto store = [&](const Pre &P, const Str &S, int c) {
-        float X = 0.f, C = 0.f;
         const bool stager = tj < S.nt;   // uniform per wave
         if (!DOWN) {
-            const bool ok = 64 * c + li < d / 8;
-            const uint4 pv = pair_halves(ok ? P.v[0] : make_uint4(0, 0, 0, 0));
-            const uint2 ev = make_uint2(pv.x, pv.z), od = make_uint2(div16(pv.y), div16(pv.w));
-            X = (hsum2(pv.x) + hsum2(pv.z)) + (hsum2(pv.y) + hsum2(pv.w));
-            C = 1024.f * ((hsum2(ev.x) + hsum2(ev.y)) + (hsum2(od.x) + hsum2(od.y)));
             if (stager) {
-                reinterpret_cast<uint2 *>(&L.xs[tj][2 * (li >> 1)])[li & 1] = ev;
-                reinterpret_cast<uint2 *>(&L.xs[tj][2 * (li >> 1) + 1])[li & 1] = od;
+#pragma unroll
+                for (int i = 0; i < XW; ++i)
+                    L.xs[tj][XW * li + i] =
+                        8 * KC * c + XW * li + i < d / 8 ? P.v[i] : make_uint4(0, 0, 0, 0);
+                if (li < KC)
+                    L.xc[tj][li] = KC * c + li < S.G ? P.xc : make_float2(0.f, 0.f);
             }
-            // a group is 8 words: lanes 8g .. 8g+7
-            X = row8_sum(X);
-            C = row8_sum(C);
-            if (stager && !(li & 7)) L.xc[tj][li >> 3] = make_float2(X, C);
         } else {
             const int HU = S.F / 4;
+            float X = 0.f, C = 0.f;
             if (stager) {
 #pragma unroll
-                for (int i = 0; i < PARTS; ++i)
-                    L.xs[tj][2 * li + i] =
-                        128 * c + 2 * li + i < HU ? P.v[i] : make_uint4(0, 0, 0, 0);
+                for (int i = 0; i < HW; ++i)
+                    L.xs[tj][HW * li + i] =
+                        16 * KC * c + HW * li + i < HU ? P.v[i] : make_uint4(0, 0, 0, 0);
             }
-            if (16 * c + (li & 15) < S.F / 32) { X = P.xc.x; C = P.xc.y; }
+            if (li < 2 * KC && 2 * KC * c + li < S.F / 32) { X = P.xc.x; C = P.xc.y; }
             X += __shfl_xor(X, 1);
             C += __shfl_xor(C, 1);
-            if (stager && li < 16 && !(li & 1)) L.xc[tj][li >> 1] = make_float2(X, C);
+            if (stager && li < 2 * KC && !(li & 1)) L.xc[tj][li >> 1] = make_float2(X, C);
         }
 #pragma unroll
-        for (int qq = 0; qq < 2; ++qq) {
-            const int e = tid + 256 * qq, rr = e >> 3, gl = e & 7;
-            const uint32_t v = KCH * c + gl < S.G ? P.sbw[qq] : 0u;
+        for (int qq = 0; qq < SW; ++qq) {
+            const int rr = tid / KC + 256 / KC * qq, gl = tid % KC;
+            const uint32_t v = KC * c + gl < S.G ? P.sbw[qq] : 0u;
             L.sb[gl][rr] = make_float2(h2f((uint16_t)(v & 0xFFFF)), h2f((uint16_t)(v >> 16)));
         }
     };
@@ -333,36 +339,53 @@ __device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1> &L) {
     // this lane's column: token tc of slot sc
     const int tc = j >> 2, sc = j & 3;
     const Masks km = masks();
-    Unit cur = unit_of<DOWN>(a, u, settle(load_rec(u)), ns, tiles_s, tiles_r);
-    Str sc0 = mkstr(cur);
+    Unit cur = unit_of<DOWN, KC, DEPTH>(a, u, settle(load_rec(u)), ns, tiles_s, tiles_r);
+    Str scu = mkstr(cur);
+    uint4 qa[2 * NR], qb[DEPTH == 2 ? 2 * NR : 1];
 #pragma unroll
-    for (int rho = 0; rho < NRND; ++rho) qload(sc0, 0, rho);
-    Pre P;
-    fetch(P, sc0, 0);
-    store(P, sc0, 0);
+    for (int rho = 0; rho < NR; ++rho) qload(qa, scu, 0, rho);
+    Pre Pa, Pb;
+    fetch(Pa, scu, 0);
+    store(Pa, scu, 0);
+    if (DEPTH == 2) {
+        uint4 (&q2)[2 * NR] = *reinterpret_cast<uint4 (*)[2 * NR]>(DEPTH == 2 ? qb : qa);
+#pragma unroll
+        for (int rho = 0; rho < NR; ++rho) qload(q2, scu, 1, rho);
+        fetch(Pb, scu, 1);
+    }
+    // Records: the next unit's sits in LDS slot par (read when this unit's
+    // last two chunks start); the one after is loaded into registers a unit
+    // ahead and moved to the other slot at that same point, where a wait
+    // for it costs nothing extra.  (Copying loaded registers at the unit
+    // boundary would wait for every load in flight.)
+    int par = 0;
+    {
+        const Rec r = load_rec(u + grid);
+        if (tid == 0) L.rec[0][0] = r.r0;
+        if (tid == 1) L.rec[0][1] = r.r1;
+        if (tid == 2) L.rec[0][2] = r.r2;
+    }
+    lds_barrier();   // the slot is read before the first chunk's barrier when nch == 2
+    Rec rnn = load_rec(u + 2 * grid);
     for (;;) {
-        // the unit after this one (this one again when there is none: its
-        // loads are then cache hits that nobody uses); its record is loaded
-        // now and first used in this unit's last chunk
-        const int un = u + (int)gridDim.x;
+        const int un = u + grid;
         const bool more = un < n_units;
-        const Rec rn = load_rec(more ? un : u);
         Unit nxt = cur;
-        Str sn = sc0;
-        const bool feeds = tc < cur.nt && sc == b;
+        Str snx = scu;
         f32x4 y = {0.f, 0.f, 0.f, 0.f};
-        for (int c = 0; c < cur.nch; ++c) {
+        const bool feeds = tc < cur.nt && sc == b;
+        // One chunk: compute from LDS and ring q; load position c + DEPTH
+        // into q and Pf; stage position c + 1 from Ps (DEPTH 1: Pf is Ps,
+        // staged after its loads land).
+        auto chunk = [&](int c, uint4 (&q)[2 * NR], Pre &Pf, const Pre &Ps) {
             lds_barrier();   // chunk c is staged
-            const bool last = c + 1 == cur.nch;
-            if (last && more) {   // no loads in here
-                nxt = unit_of<DOWN>(a, un, settle(rn), ns, tiles_s, tiles_r);
-                sn = mkstr(nxt);
-            }
-            const Str s2 = sel(last, sn, sc0);
-            const int c2 = last ? 0 : c + 1;
-            fetch(P, s2, c2);
+            const bool n1 = c + 1 >= cur.nch, n2 = c + DEPTH >= cur.nch;
+            const Str s1 = sel(n1, snx, scu), s2 = sel(n2, snx, scu);
+            const int c1 = n1 ? c + 1 - cur.nch : c + 1;
+            const int c2 = n2 ? c + DEPTH - cur.nch : c + DEPTH;
+            fetch(Pf, s2, c2);
 #pragma unroll
-            for (int rho = 0; rho < NRND; ++rho) {
+            for (int rho = 0; rho < NR; ++rho) {
                 const int gc = 4 * rho + sc;   // the column's group in the chunk
                 const float2 xc = L.xc[tc][gc];
                 f32x4 D = {-xc.y, -xc.y, -xc.y, -xc.y};
@@ -379,7 +402,7 @@ __device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1> &L) {
                         D = mfma(ah, as_half8(bp[2 * p + 1]), D);
                     }
                 }
-                qload(s2, c2, rho);
+                qload(q, s2, c2, rho);
                 const float4 s01 = *reinterpret_cast<const float4 *>(&L.sb[gc][16 * w + 4 * b]);
                 const float4 s23 = *reinterpret_cast<const float4 *>(&L.sb[gc][16 * w + 4 * b + 2]);
                 y[0] = fmaf(s01.x, D[0], fmaf(s01.y, xc.x, y[0]));
@@ -391,7 +414,27 @@ __device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1> &L) {
                 asm volatile("" : "+v"(y[0]), "+v"(y[1]), "+v"(y[2]), "+v"(y[3]));
             }
             lds_barrier();   // everyone is done reading chunk c
-            store(P, s2, c2);
+            store(Ps, s1, c1);
+        };
+        for (int c = 0; c < cur.nch; c += DEPTH) {
+            if (c + DEPTH == cur.nch && more) {   // no loads in here
+                Rec rn;
+                rn.r0 = L.rec[par][0];
+                rn.r1 = L.rec[par][1];
+                rn.r2 = L.rec[par][2];
+                nxt = unit_of<DOWN, KC, DEPTH>(a, un, settle(rn), ns, tiles_s, tiles_r);
+                snx = mkstr(nxt);
+                if (tid == 0) L.rec[par ^ 1][0] = rnn.r0;
+                if (tid == 1) L.rec[par ^ 1][1] = rnn.r1;
+                if (tid == 2) L.rec[par ^ 1][2] = rnn.r2;
+            }
+            if (DEPTH == 2) {
+                uint4 (&q2)[2 * NR] = *reinterpret_cast<uint4 (*)[2 * NR]>(DEPTH == 2 ? qb : qa);
+                chunk(c, qa, Pa, Pb);
+                chunk(c + 1, q2, Pb, Pa);
+            } else {
+                chunk(c, qa, Pa, Pa);
+            }
         }
         // a token's four slot columns are neighbouring lanes: sum them
 #pragma unroll
@@ -403,8 +446,8 @@ __device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1> &L) {
         if (DOWN) {   // rows 64 rt + 16 w + 4b .. +3 of token tc
             if (owner) {
                 float *yd = cur.routed ? a.y_e : a.y_s;
-                *reinterpret_cast<float4 *>(yd + (size_t)pick4(tc, cur.d0, cur.d1, cur.d2, cur.d3) * d + 64 * cur.rt +
-                                            16 * w + 4 * b) = make_float4(y[0], y[1], y[2], y[3]);
+                *reinterpret_cast<float4 *>(yd + (size_t)pick4(tc, cur.d0, cur.d1, cur.d2, cur.d3) * d +
+                                            64 * cur.rt + 16 * w + 4 * b) = make_float4(y[0], y[1], y[2], y[3]);
             }
         } else {
             if (owner) {
@@ -441,7 +484,8 @@ __device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1> &L) {
                 C += __shfl_xor(C, 2);
                 if (ok) {
                     const int F = cur.F, wg = 4 * cur.rt + s4;   // word of the hidden row
-                    uint4 *row = (cur.routed ? a.h_r : a.h_s) + (size_t)pick4(t, cur.d0, cur.d1, cur.d2, cur.d3) * mq_row_u4(F);
+                    uint4 *row = (cur.routed ? a.h_r : a.h_s) +
+                                 (size_t)pick4(t, cur.d0, cur.d1, cur.d2, cur.d3) * mq_row_u4(F);
                     uint2 *u2 = reinterpret_cast<uint2 *>(row) + 8 * (wg >> 1) + (wg & 1);
                     u2[0] = he;
                     u2[2] = ho;
@@ -454,18 +498,23 @@ __device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1> &L) {
         if (!more) break;
         u = un;
         cur = nxt;
-        sc0 = sn;
+        scu = snx;
+        par ^= 1;
+        rnn = load_rec(u + 2 * grid);
     }
 }
 
+constexpr int KC_GU = 8, KC_DN = 8;   // groups per staged chunk
+constexpr int DEPTH = 1;              // chunks loaded ahead
+
 __global__ __launch_bounds__(256, 4) void k_gu(DecodeArgs a) {
-    __shared__ GLds<1> L;
-    grouped<false>(a, L);
+    __shared__ GLds<1, KC_GU> L;
+    grouped<false, KC_GU, DEPTH>(a, L);
 }
 
 __global__ __launch_bounds__(256, 4) void k_dn(DecodeArgs a) {
-    __shared__ GLds<2> L;
-    grouped<true>(a, L);
+    __shared__ GLds<2, KC_DN> L;
+    grouped<true, KC_DN, DEPTH>(a, L);
 }
 
 }  // namespace

@@ -63,4 +63,35 @@ __device__ __forceinline__ void hs_produce(uint4 *dst, int K, int blk, const flo
         make_float2(xe + xo, fmaf(1024.f, xe, 64.f * xo));
 }
 
+// An fp16 pair divided by 16 (exact unless the result is subnormal).
+__device__ __forceinline__ uint32_t div16(uint32_t p) {
+    const h2_t v = __builtin_bit_cast(h2_t, p) * h2_t{(_Float16)0.0625f, (_Float16)0.0625f};
+    return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float hsum2(uint32_t p) {
+    return h2f((uint16_t)(p & 0xFFFF)) + h2f((uint16_t)(p >> 16));
+}
+
+// Activation rows in the grouped kernels' B-operand form: per pair of code
+// words (16 values) the even elements and the odd elements divided by 16,
+// each as (e0,e4)(e2,e6) of both words (32 bytes), then one (X, C) float2
+// per group of 64: X = sum of the values, C = 1024 (sum of the even values +
+// sum of the odd values / 16).  Row size in uint4.
+__host__ __device__ constexpr int xb_row_u4(int d) { return (2 * d + 8 * (d / 64) + 15) / 16; }
+
+// Values 16 wp .. 16 wp + 15 (v0: the first eight) into word pair wp of an
+// activation row; X and C get their share of the group sums.
+__device__ __forceinline__ void xb_produce(uint4 v0, uint4 v1, uint4 *row, int wp, float &X,
+                                           float &C) {
+    const uint4 p0 = pair_halves(v0), p1 = pair_halves(v1);
+    const uint4 ev = make_uint4(p0.x, p0.z, p1.x, p1.z);
+    const uint4 od = make_uint4(div16(p0.y), div16(p0.w), div16(p1.y), div16(p1.w));
+    row[2 * wp] = ev;
+    row[2 * wp + 1] = od;
+    X = ((hsum2(p0.x) + hsum2(p0.z)) + (hsum2(p0.y) + hsum2(p0.w))) +
+        ((hsum2(p1.x) + hsum2(p1.z)) + (hsum2(p1.y) + hsum2(p1.w)));
+    C = 1024.f * (((hsum2(ev.x) + hsum2(ev.y)) + (hsum2(ev.z) + hsum2(ev.w))) +
+                  ((hsum2(od.x) + hsum2(od.y)) + (hsum2(od.z) + hsum2(od.w))));
+}
+
 }  // namespace tfk

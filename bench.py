@@ -17,7 +17,6 @@ from __future__ import annotations
 
 import argparse
 import ctypes
-import hashlib
 import json
 import os
 import sys
@@ -66,9 +65,10 @@ def layer_bytes(d, f, fs, E, k):
     return router + shared + routed + 2 * d + 2 * d
 
 
-def _traffic_for(kernel_name, src_path, workload):
+def _traffic_for(kernel_name, workload):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source; else None."""
+    taken on the current kernel sources; else None."""
+    from bit_routed_expert_tf_amd import profiling
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -76,10 +76,23 @@ def _traffic_for(kernel_name, src_path, workload):
         rec = json.load(open(path))[kernel_name]
     except (KeyError, ValueError):
         return None
-    sha = hashlib.sha256(open(src_path, "rb").read()).hexdigest()
-    if rec.get("source_sha256") != sha or rec.get("workload") != workload:
+    if (rec.get("source_sha256") != profiling.source_sha256(rec.get("kernel", ""))
+            or rec.get("workload") != workload):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(nbytes=256 << 20, reps=3):
+    """Plain device-to-device copies of a known size, for scaling the memory
+    counters (rocprofv3 FETCH_SIZE / WRITE_SIZE) of the same run."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
 
 
 def run_decode(args):
@@ -190,9 +203,7 @@ def run_decode(args):
     dur_b = kern["routed_gateup_shared_down"]["avg_us"] * 1e-6
     achieved = bytes_b / dur_b / 1e9
     lb = layer_bytes(d, f, fs, E, k)
-    traffic = _traffic_for("routed_gateup_shared_down",
-                           os.path.join(ROOT, "bit_routed_expert_tf_amd", "csrc", "tf_decode.hip"),
-                           wl.name)
+    traffic = _traffic_for("routed_gateup_shared_down", wl.name)
 
     out = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -534,6 +545,8 @@ def main():
     ap.add_argument("--prof-steps", type=int, default=300)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run plain 256 MiB device copies (memory-counter calibration)")
     ap.add_argument("--workload", choices=["decode", "prefill", "stack", "slot-cache"],
                     default="decode",
                     help="decode (default, the headline line); the others measure the "
@@ -544,6 +557,8 @@ def main():
               "MI355X (the multi-GPU design is expert sharding, not implemented here).",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
     if args.workload == "decode":
         out = run_decode(args)
     else:

@@ -96,9 +96,11 @@ struct GLds {
     // the chunk's activations: [token][word pair][part][even | odd/16], one
     // 16-byte entry each; rows padded so that the tokens of a B read fall on
     // different banks
-    uint4 xs[UT][KC * 4 * PARTS * 2 + 1];
-    float2 xc[UT][KC + 1];      // (X, C) per token and group of the chunk
-    float2 sb[KC][64 + 4];      // (scale, bias) per group and row of the block
+    // (two buffers: chunk c is read from buffer c % 2 while chunk c + 1 is
+    // staged into the other, so one barrier per chunk suffices)
+    uint4 xs[2][UT][KC * 4 * PARTS * 2 + 1];
+    float2 xc[2][UT][KC + 1];   // (X, C) per token and group of the chunk
+    float2 sb[2][KC][64 + 4];   // (scale, bias) per group and row of the block
     float out[2][32][UT + 1];   // gate and up sums of a unit
     uint4 zero[2 * PARTS];      // B operand of the columns a lane block does not feed
     uint4 rec[2][3];            // item record of the next unit, by unit parity
@@ -303,16 +305,16 @@ __device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1, KC> &L) {
             }
         }
     };
-    auto store = [&](const Pre &P, const Str &S, int c) {
+    auto store = [&](const Pre &P, const Str &S, int c, int nb) {
         const bool stager = tj < S.nt;   // uniform per wave
         if (!DOWN) {
             if (stager) {
 #pragma unroll
                 for (int i = 0; i < XW; ++i)
-                    L.xs[tj][XW * li + i] =
+                    L.xs[nb][tj][XW * li + i] =
                         8 * KC * c + XW * li + i < d / 8 ? P.v[i] : make_uint4(0, 0, 0, 0);
                 if (li < KC)
-                    L.xc[tj][li] = KC * c + li < S.G ? P.xc : make_float2(0.f, 0.f);
+                    L.xc[nb][tj][li] = KC * c + li < S.G ? P.xc : make_float2(0.f, 0.f);
             }
         } else {
             const int HU = S.F / 4;
@@ -320,19 +322,19 @@ __device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1, KC> &L) {
             if (stager) {
 #pragma unroll
                 for (int i = 0; i < HW; ++i)
-                    L.xs[tj][HW * li + i] =
+                    L.xs[nb][tj][HW * li + i] =
                         16 * KC * c + HW * li + i < HU ? P.v[i] : make_uint4(0, 0, 0, 0);
             }
             if (li < 2 * KC && 2 * KC * c + li < S.F / 32) { X = P.xc.x; C = P.xc.y; }
             X += __shfl_xor(X, 1);
             C += __shfl_xor(C, 1);
-            if (stager && li < 2 * KC && !(li & 1)) L.xc[tj][li >> 1] = make_float2(X, C);
+            if (stager && li < 2 * KC && !(li & 1)) L.xc[nb][tj][li >> 1] = make_float2(X, C);
         }
 #pragma unroll
         for (int qq = 0; qq < SW; ++qq) {
             const int rr = tid / KC + 256 / KC * qq, gl = tid % KC;
             const uint32_t v = KC * c + gl < S.G ? P.sbw[qq] : 0u;
-            L.sb[gl][rr] = make_float2(h2f((uint16_t)(v & 0xFFFF)), h2f((uint16_t)(v >> 16)));
+            L.sb[nb][gl][rr] = make_float2(h2f((uint16_t)(v & 0xFFFF)), h2f((uint16_t)(v >> 16)));
         }
     };
 
@@ -345,8 +347,9 @@ __device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1, KC> &L) {
 #pragma unroll
     for (int rho = 0; rho < NR; ++rho) qload(qa, scu, 0, rho);
     Pre Pa, Pb;
+    int buf = 0;   // LDS buffer the current chunk is read from
     fetch(Pa, scu, 0);
-    store(Pa, scu, 0);
+    store(Pa, scu, 0, 0);
     if (DEPTH == 2) {
         uint4 (&q2)[2 * NR] = *reinterpret_cast<uint4 (*)[2 * NR]>(DEPTH == 2 ? qb : qa);
 #pragma unroll
@@ -387,7 +390,7 @@ __device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1, KC> &L) {
 #pragma unroll
             for (int rho = 0; rho < NR; ++rho) {
                 const int gc = 4 * rho + sc;   // the column's group in the chunk
-                const float2 xc = L.xc[tc][gc];
+                const float2 xc = L.xc[buf][tc][gc];
                 f32x4 D = {-xc.y, -xc.y, -xc.y, -xc.y};
 #pragma unroll
                 for (int sg = 0; sg < 4; ++sg) {
@@ -395,7 +398,7 @@ __device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1, KC> &L) {
                     const uint32_t w0 = (sg & 1) ? v.z : v.x, w1 = (sg & 1) ? v.w : v.y;
                     const half8 al = codes_lo(km, w0, w1), ah = codes_hi(km, w0, w1);
                     const int m = 4 * (4 * rho + b) + sg;   // word pair fed by lane block b
-                    const uint4 *bp = feeds ? &L.xs[tc][m * 2 * PARTS] : L.zero;
+                    const uint4 *bp = feeds ? &L.xs[buf][tc][m * 2 * PARTS] : L.zero;
 #pragma unroll
                     for (int p = 0; p < PARTS; ++p) {
                         D = mfma(al, as_half8(bp[2 * p]), D);
@@ -403,8 +406,8 @@ __device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1, KC> &L) {
                     }
                 }
                 qload(q, s2, c2, rho);
-                const float4 s01 = *reinterpret_cast<const float4 *>(&L.sb[gc][16 * w + 4 * b]);
-                const float4 s23 = *reinterpret_cast<const float4 *>(&L.sb[gc][16 * w + 4 * b + 2]);
+                const float4 s01 = *reinterpret_cast<const float4 *>(&L.sb[buf][gc][16 * w + 4 * b]);
+                const float4 s23 = *reinterpret_cast<const float4 *>(&L.sb[buf][gc][16 * w + 4 * b + 2]);
                 y[0] = fmaf(s01.x, D[0], fmaf(s01.y, xc.x, y[0]));
                 y[1] = fmaf(s01.z, D[1], fmaf(s01.w, xc.x, y[1]));
                 y[2] = fmaf(s23.x, D[2], fmaf(s23.y, xc.x, y[2]));
@@ -413,8 +416,10 @@ __device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1, KC> &L) {
                 // reading y), so no round's D stays live to the end
                 asm volatile("" : "+v"(y[0]), "+v"(y[1]), "+v"(y[2]), "+v"(y[3]));
             }
-            lds_barrier();   // everyone is done reading chunk c
-            store(Ps, s1, c1);
+            // the other buffer: every wave finished reading it before this
+            // chunk's barrier
+            store(Ps, s1, c1, buf ^ 1);
+            buf ^= 1;
         };
         for (int c = 0; c < cur.nch; c += DEPTH) {
             if (c + DEPTH == cur.nch && more) {   // no loads in here

@@ -129,14 +129,19 @@ hipError_t grouped_step(const tf_moe_layer *L, const uint16_t *x, int T, const i
     a.y_s = at<float>(ws, w.ys);
     a.h_r = at<uint4>(ws, w.hr);
     a.y_e = at<float>(ws, w.total);
-    a.xb = at<uint4>(ws, w.xb);
     a.do_group = 1;
-    a.tbi = 4;   // items of up to four tokens: one grouped unit each
+    // decode steps (T <= 16): persistent units of up to four tokens, x staged
+    // in B-operand form by the router launch; prefill chunks: tiles of up to
+    // 16 tokens
+    const bool tiles = T > MAX_DECODE_T;
+    a.xb = tiles ? nullptr : at<uint4>(ws, w.xb);
+    a.tbi = tiles ? 16 : 4;
     const int P = T * a.k;
     const int max_items = P < a.E + P / a.tbi ? P : a.E + P / a.tbi;
     a.a_router_blocks = ((a.E + 3) / 4) * T;
     hipError_t e = tf_launch_decode(a, STAGE_A, s);
-    if (e == hipSuccess) e = tf_launch_grouped(a, max_items, s);
+    if (e == hipSuccess)
+        e = tiles ? tf_launch_prefill_tiles(a, max_items, s) : tf_launch_grouped(a, max_items, s);
     return e;
 }
 

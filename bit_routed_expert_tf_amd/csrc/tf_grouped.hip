@@ -54,8 +54,9 @@ constexpr int UT = 4;     // tokens per unit
 
 // Hidden rows between the grouped gate/up and down launches, F values:
 // word pairs (16 values) of 64 bytes [part hi: even | odd/16][part lo:
-// even | odd/16], then one (X, C) float2 per half-group (32 values).
-__host__ __device__ constexpr int mq_row_u4(int F) { return F / 4 + F / 64; }
+// even | odd/16], then one (X, C) float2 per 8-value block (the consumer adds
+// a group's eight in a fixed order).
+__host__ __device__ constexpr int mq_row_u4(int F) { return F / 4 + F / 16; }
 
 // The masks and the exponent pattern live in registers (Masks), so that each
 // value is one v_and_or_b32 (its VOP3 encoding takes no literal operands).
@@ -184,6 +185,7 @@ __device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1, KC> &L) {
     constexpr int XW = KC / 8;        // gate/up staging: uint4 per lane per chunk
     constexpr int HW = KC / 4;        // down staging: uint4 per lane per chunk
     constexpr int SW = KC / 4;        // scale/bias entries per thread per chunk
+    static_assert(!DOWN || 8 * KC <= 64, "one lane per 8-value block partial of a chunk");
     const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
     const int j = lane & 15, b = lane >> 4;
     const int d = a.d;
@@ -284,11 +286,11 @@ __device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1, KC> &L) {
 #pragma unroll
             for (int i = 0; i < XW; ++i) P.v[i] = S.srow[min(8 * KC * c + XW * li + i, d / 8 - 1)];
             P.xc = reinterpret_cast<const float2 *>(S.srow + d / 8)[min(KC * c + (li & (KC - 1)), S.G - 1)];
-        } else {       // uint4 16 KC c + HW li + i; (X, C) of half-group 2 KC c + li
+        } else {       // uint4 16 KC c + HW li + i; (X, C) of 8-value block 8 KC c + li
             const int HU = S.F / 4;
 #pragma unroll
             for (int i = 0; i < HW; ++i) P.v[i] = S.srow[min(16 * KC * c + HW * li + i, HU - 1)];
-            P.xc = reinterpret_cast<const float2 *>(S.srow + HU)[min(2 * KC * c + (li & (2 * KC - 1)), S.F / 32 - 1)];
+            P.xc = reinterpret_cast<const float2 *>(S.srow + HU)[min(8 * KC * c + (li & (8 * KC - 1)), S.F / 8 - 1)];
         }
         // entry e = tid + 256 qq: block row e / KC, group KC c + e % KC; rows
         // [0, 32) from s0/b0, [32, 64) from s1/b1 (down: one matrix)
@@ -325,10 +327,15 @@ __device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1, KC> &L) {
                     L.xs[nb][tj][HW * li + i] =
                         16 * KC * c + HW * li + i < HU ? P.v[i] : make_uint4(0, 0, 0, 0);
             }
-            if (li < 2 * KC && 2 * KC * c + li < S.F / 32) { X = P.xc.x; C = P.xc.y; }
+            if (li < 8 * KC && 8 * KC * c + li < S.F / 8) { X = P.xc.x; C = P.xc.y; }
+            // a group's eight block partials, in a fixed order
             X += __shfl_xor(X, 1);
             C += __shfl_xor(C, 1);
-            if (stager && li < 2 * KC && !(li & 1)) L.xc[nb][tj][li >> 1] = make_float2(X, C);
+            X += __shfl_xor(X, 2);
+            C += __shfl_xor(C, 2);
+            X += __shfl_xor(X, 4);
+            C += __shfl_xor(C, 4);
+            if (stager && li < 8 * KC && !(li & 7)) L.xc[nb][tj][li >> 3] = make_float2(X, C);
         }
 #pragma unroll
         for (int qq = 0; qq < SW; ++qq) {
@@ -460,44 +467,34 @@ __device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1, KC> &L) {
                 for (int r = 0; r < 4; ++r) L.out[w >> 1][16 * (w & 1) + 4 * b + r][tc] = y[r];
             }
             lds_barrier();
-            if (tid < 64) {   // thread (token, 8-row block): h = coef * gelu(g) * u
-                const int t = min(tid >> 2, UT - 1), s4 = tid & 3;
-                const bool ok = (tid >> 2) < cur.nt;
-                const float cf = pick4(t, cur.c0, cur.c1, cur.c2, cur.c3);
-                float hh[8], hl[8], X = 0.f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float e = ok ? cf * (gelu_f(L.out[0][8 * s4 + i][t], a.act) *
-                                               L.out[1][8 * s4 + i][t])
-                                       : 0.f;
-                    hh[i] = (float)(_Float16)e;
-                    hl[i] = (float)(_Float16)(e - hh[i]);
-                    X += e;
-                }
-                // even elements as they are, odd ones divided by 16, in the
-                // pair order (e0,e4)(e2,e6) | (e1,e5)(e3,e7)
-                const uint2 he = make_uint2(pack_h2(hh[0], hh[4]), pack_h2(hh[2], hh[6]));
-                const uint2 ho = make_uint2(div16(pack_h2(hh[1], hh[5])), div16(pack_h2(hh[3], hh[7])));
-                const uint2 le = make_uint2(pack_h2(hl[0], hl[4]), pack_h2(hl[2], hl[6]));
-                const uint2 lo = make_uint2(div16(pack_h2(hl[1], hl[5])), div16(pack_h2(hl[3], hl[7])));
-                float C = ((hsum2(he.x) + hsum2(he.y)) + (hsum2(ho.x) + hsum2(ho.y))) +
-                          ((hsum2(le.x) + hsum2(le.y)) + (hsum2(lo.x) + hsum2(lo.y)));
-                C *= 1024.f;
-                X += __shfl_xor(X, 1);
-                X += __shfl_xor(X, 2);
-                C += __shfl_xor(C, 1);
-                C += __shfl_xor(C, 2);
-                if (ok) {
-                    const int F = cur.F, wg = 4 * cur.rt + s4;   // word of the hidden row
-                    uint4 *row = (cur.routed ? a.h_r : a.h_s) +
-                                 (size_t)pick4(t, cur.d0, cur.d1, cur.d2, cur.d3) * mq_row_u4(F);
-                    uint2 *u2 = reinterpret_cast<uint2 *>(row) + 8 * (wg >> 1) + (wg & 1);
-                    u2[0] = he;
-                    u2[2] = ho;
-                    u2[4] = le;
-                    u2[6] = lo;
-                    if (s4 == 0) reinterpret_cast<float2 *>(row + F / 4)[cur.rt] = make_float2(X, C);
-                }
+            // wave w: 8-row block w of the unit; lane (token t, row i) of it:
+            // h = coef * gelu(g) * u, split into hi + lo fp16 parts
+            const int t = (lane >> 3) & (UT - 1), i = lane & 7;
+            const bool ok = lane < 8 * UT && t < cur.nt;
+            const float cf = pick4(t, cur.c0, cur.c1, cur.c2, cur.c3);
+            const float e = ok ? cf * (gelu_f(L.out[0][8 * w + i][t], a.act) * L.out[1][8 * w + i][t]) : 0.f;
+            const float eh = (float)(_Float16)e, el = (float)(_Float16)(e - eh);
+            // lane i < 4 packs elements (i, i + 4): even i as they are, odd i
+            // divided by 16 -- words (e0,e4)(e2,e6) | (e1,e5)(e3,e7)
+            const float ph = __shfl_xor(eh, 4), pl = __shfl_xor(el, 4);
+            uint32_t wh = pack_h2(eh, ph), wl = pack_h2(el, pl);
+            if (i & 1) { wh = div16(wh); wl = div16(wl); }
+            float C = i < 4 ? hsum2(wh) + hsum2(wl) : 0.f;
+            float X = e;
+            X += __shfl_xor(X, 1);
+            C += __shfl_xor(C, 1);
+            X += __shfl_xor(X, 2);
+            C += __shfl_xor(C, 2);
+            X += __shfl_xor(X, 4);
+            if (ok && i < 4) {
+                const int F = cur.F, wg = 4 * cur.rt + w;   // 8-value block of the hidden row
+                uint4 *row = (cur.routed ? a.h_r : a.h_s) +
+                             (size_t)pick4(t, cur.d0, cur.d1, cur.d2, cur.d3) * mq_row_u4(F);
+                uint32_t *wd = reinterpret_cast<uint32_t *>(row) + 16 * (wg >> 1) + 2 * (wg & 1) +
+                               4 * (i & 1) + (i >> 1);
+                wd[0] = wh;
+                wd[8] = wl;
+                if (i == 0) reinterpret_cast<float2 *>(row + F / 4)[wg] = make_float2(X, 1024.f * C);
             }
         }
         if (!more) break;

@@ -72,7 +72,7 @@ struct WsLayout {
 WsLayout decode_layout(int d, int f, int fs, int E, int k, int T) {
     WsLayout w{};
     size_t o = 0;
-    w.hdr = o; o += up256((size_t)4 * (HDR_TICKET + T + 1) > 256 ? (size_t)4 * (HDR_TICKET + T + 1) : 256);
+    w.hdr = o; o += up256(hdr_bytes(T));
     w.logits = o; o += up256((size_t)8 * T * E);
     w.items = o; o += up256((size_t)4 * ITEM_INTS * T * k);
     w.pairs = o; o += up256((size_t)4 * T * k);
@@ -197,7 +197,7 @@ tf_status tf_workspace_flags(void *ws, int32_t *flags_host, hipStream_t s) {
     return e == hipSuccess ? TF_OK : hip_fail(e, "clearing workspace flags");
 }
 
-static size_t router_hdr_bytes(int32_t T) { return up256((size_t)4 * (T + 3)); }
+static size_t router_hdr_bytes(int32_t T) { return up256(hdr_bytes(T)); }
 
 size_t tf_router_workspace_bytes(int32_t n_experts, int32_t T) {
     if (n_experts <= 0 || T <= 0) return 256;

@@ -267,31 +267,41 @@ __device__ __forceinline__ void hs_store(const HStage<MAXI, MAXS> &Hs, int rows,
 // softmax over the k selected logits (max-subtracted differences in fp64,
 // exponentials in fp32, normalised in fp64).  Whole WG.
 //
-// Rank of candidate i = #{j : l_j > l_i or (l_j == l_i and j < i)}.  It is
-// counted on fp32 copies of the logits: rounding to fp32 is monotone, so
-// f_j > f_i implies l_j > l_i, and only candidates whose fp32 key another
-// candidate shares need the exact fp64 comparison (a second, rare pass).
-// Two threads per candidate, each over one half of the j range, four keys
-// per LDS read.
+// Selection is exact on the fp64 logits, through 64-bit keys that order as
+// the logits do.  Candidate i goes to group i % k; the k group maxima are k
+// distinct candidates, so the k-th largest key is at least tau, the least
+// of them, and no candidate below tau can be selected.  The few candidates
+// at or above tau are ranked among themselves:
+//     rank(i) = #{j : key_j > key_i or (key_j == key_i and j < i)},
+// which is their rank among all candidates, since every other one is
+// smaller.
 __host__ __device__ constexpr int topk_lds_bytes(int E) {
-    return 8 * (E + 2) + 8 * 16 + 4 * 16 + 4 * 256 + 4 * (E + 8);
+    return 8 * E + 8 * E + 8 * 16 + 4 * 16 + 4 * E + 8 * E + 16;
+}
+
+// Unsigned key ordered as the double (NaN excluded; -0 taken as +0).
+__device__ __forceinline__ uint64_t order_key(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v == 0.0 ? 0.0 : v);
+    return (u >> 63) ? ~u : (u | (1ull << 63));
 }
 
 __device__ void topk_block(const DecodeArgs &a, int t, int tid, unsigned char *lds) {
-    double *l = reinterpret_cast<double *>(lds);            // [E] (+1 pad)
-    double *ex = l + ((a.E + 2) & ~1);                       // [16]
-    int *sel = reinterpret_cast<int *>(ex + 16);             // [16]
-    int *part = sel + 16;                                    // [256]
-    float *lf = reinterpret_cast<float *>(part + 256);       // [E + 8], -inf padded
+    const int E = a.E;
+    double *l = reinterpret_cast<double *>(lds);             // [E] logits
+    uint64_t *key = reinterpret_cast<uint64_t *>(l + E);     // [E]
+    uint64_t *gmax = key + E;                                 // [16] group maxima
+    int *sel = reinterpret_cast<int *>(gmax + 16);            // [16]
+    int *sid = sel + 16;                                      // [E] candidates >= tau
+    uint64_t *skey = reinterpret_cast<uint64_t *>(sid + ((E + 1) & ~1));  // [E] their keys
+    int *ns = reinterpret_cast<int *>(skey + E);              // their count
     lds_barrier();
-    for (int i = tid; i < a.E + 8; i += WG) {
-        double v = -__builtin_inf();
-        if (i < a.E) {
-            v = ld_dev(a.logits + (size_t)t * a.E + i);
-            if (v != v) v = -__builtin_inf();   // NaN ranks last
-            l[i] = v;
-        }
-        lf[i] = (float)v;
+    if (tid < 16) gmax[tid] = tid < a.k ? 0ull : ~0ull;   // below every key; unused groups above
+    if (tid == 0) *ns = 0;
+    for (int i = tid; i < E; i += WG) {
+        double v = ld_dev(a.logits + (size_t)t * E + i);
+        if (v != v) v = -__builtin_inf();   // NaN ranks last
+        l[i] = v;
+        key[i] = order_key(v);
     }
     lds_barrier();
     if (a.forced) {
@@ -307,50 +317,78 @@ __device__ void topk_block(const DecodeArgs &a, int t, int tid, unsigned char *l
                 if (sel[r] == sel[tid]) fl |= TF_FLAG_ID_REPEAT;
         if (fl) atomicOr(a.hdr + HDR_FLAGS, fl);
     } else {
-        const int half = tid >> 7;
-        const int E2 = ((a.E + 7) >> 3) << 2;   // half range, a multiple of 4
-        const int jb = half * E2;
-        for (int base = 0; base < a.E; base += 128) {
-            const int i = base + (tid & 127);
-            int gt = 0, eq = 0;
-            if (i < a.E) {
-                const float fi = lf[i];
-                const float4 *q = reinterpret_cast<const float4 *>(lf + jb);
-#pragma unroll 4
-                for (int j = 0; j < E2 / 4; ++j) {
-                    const float4 v = q[j];
-                    gt += (v.x > fi) + (v.y > fi) + (v.z > fi) + (v.w > fi);
-                    eq += (v.x == fi) + (v.y == fi) + (v.z == fi) + (v.w == fi);
+        for (int i = tid; i < E; i += WG) atomicMax(reinterpret_cast<unsigned long long *>(gmax + i % a.k),
+                                                    (unsigned long long)key[i]);
+        lds_barrier();
+        // all sixteen slots read at once (the unused ones hold the largest key)
+        uint64_t gm[16];
+#pragma unroll
+        for (int g = 0; g < 16; g += 2) {
+            const ulonglong2 v = *reinterpret_cast<const ulonglong2 *>(gmax + g);
+            gm[g] = v.x;
+            gm[g + 1] = v.y;
+        }
+        uint64_t tau = gm[0];
+#pragma unroll
+        for (int g = 1; g < 16; ++g) tau = min(tau, gm[g]);
+        for (int i = tid; i < E; i += WG) {
+            const uint64_t ki = key[i];
+            if (ki >= tau) {
+                const int q = atomicAdd(ns, 1);
+                sid[q] = i;
+                skey[q] = ki;
+            }
+        }
+        lds_barrier();
+        const int S = *ns;
+        for (int q = tid; q < S; q += WG) {
+            const int i = sid[q];
+            const uint64_t ki = skey[q];
+            int r = 0;
+            for (int j0 = 0; j0 < S; j0 += 8) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int jq = min(j0 + u, S - 1);
+                    const uint64_t kj = skey[jq];
+                    const int j = sid[jq];
+                    r += j0 + u < S && (kj > ki || (kj == ki && j < i));
                 }
             }
-            part[tid] = gt | (eq << 16);
-            lds_barrier();
-            if (tid < 128 && i < a.E) {
-                const int p0 = part[tid], p1 = part[tid + 128];
-                int c = (p0 & 0xFFFF) + (p1 & 0xFFFF);
-                if ((p0 >> 16) + (p1 >> 16) > 1) {   // fp32 key shared: exact order
-                    const double li = l[i];
-                    const float fi = lf[i];
-                    for (int j = 0; j < a.E; ++j)
-                        if (j != i && lf[j] == fi) c += (l[j] > li) | ((l[j] == li) & (j < i));
-                }
-                if (c < a.k) sel[c] = i;
-            }
-            lds_barrier();
+            if (r < a.k) sel[r] = i;
         }
     }
     lds_barrier();
-    if (tid < a.k) {
-        double m = l[sel[0]];
-        for (int r = 1; r < a.k; ++r) m = fmax(m, l[sel[r]]);
-        ex[tid] = (double)expf((float)(l[sel[tid]] - m));
-    }
-    lds_barrier();
-    if (tid < a.k) {
+    if (tid < WAVE) {   // lane r < k: rank r (k <= 16: one row of lanes)
+        const int r = tid, id = sel[min(r, a.k - 1)];
+        const double v = r < a.k ? l[id] : -__builtin_inf();
+        // the maximum over the row (exact in any order)
+        double m = v;
+        m = fmax(m, dpp_d<DPP_XOR1>(m));
+        m = fmax(m, dpp_d<DPP_XOR2>(m));
+        m = fmax(m, dpp_d<DPP_HALF_MIRROR>(m));
+        m = fmax(m, dpp_d<DPP_MIRROR>(m));
+        const double e = r < a.k ? (double)expf((float)(v - m)) : 0.0;
+        // the sum in rank order, every lane adding the same sequence (the
+        // values go through LDS, read back all at once)
+        double *ex = l;   // the logits are no longer read
+        if (r < 16) ex[r] = e;
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_wave_barrier();
+        double ev[16];
+#pragma unroll
+        for (int q = 0; q < 16; q += 2) {
+            const double2 v2 = *reinterpret_cast<const double2 *>(ex + q);
+            ev[q] = v2.x;
+            ev[q + 1] = v2.y;
+        }
         double s = 0.0;
-        for (int r = 0; r < a.k; ++r) s += ex[r];
-        st_dev(a.ids + (size_t)t * a.k + tid, (int32_t)sel[tid]);
-        st_dev(a.weights + (size_t)t * a.k + tid, (float)(ex[tid] / s));
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            if (q < a.k) s += ev[q];
+        if (r < a.k) {
+            st_dev(a.ids + (size_t)t * a.k + r, (int32_t)id);
+            st_dev(a.weights + (size_t)t * a.k + r, (float)(e / s));
+        }
     }
 }
 
@@ -363,10 +401,13 @@ __device__ void topk_block(const DecodeArgs &a, int t, int tid, unsigned char *l
 // in one load.  Token t's pair with expert e lands at
 // offs[e] + #{t' < t that selected e}, counted on a per-expert bit mask over
 // the tokens (T <= 128), so the order never depends on thread timing.
-// Positions start out holding their own index, so repeated ids (flagged by
-// the top-k) can never leave an out-of-range pair behind.  Whole WG.
+// The ids and weights are read once (one round trip); the sorted order is
+// built in LDS, where positions start out holding their own index, so
+// repeated ids (flagged by the top-k) can never leave an out-of-range pair
+// behind, and is written out at the end.  Whole WG.
+constexpr int GROUP_PPT = (MAX_PREFILL_T * 16 + WG - 1) / WG;   // pairs per thread, at most
 __host__ __device__ constexpr int group_lds_bytes(int E, int T) {
-    return 4 * E * ((T + 31) >> 5) + 12 * E + 8 * 4;
+    return 4 * E * ((T + 31) >> 5) + 12 * E + 8 * 4 + 4 * T * 16;
 }
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
@@ -378,18 +419,28 @@ __device__ void group_block(const DecodeArgs &a, int tid, unsigned char *lds) {
     int *offs = cnt + E;                                      // [E]
     int *iidx = offs + E;                                     // [E] item index
     int *wsum = iidx + E;                                     // [4][2]
-    lds_barrier();
-    for (int i = tid; i < E * NW; i += WG) mask[i] = 0;
-    for (int p = tid; p < P; p += WG) st_dev(a.pairs + p, (int32_t)p);
-    lds_barrier();
-    for (int p = tid; p < P; p += WG) {
-        const int e = min(max((int)ld_dev(a.ids + p), 0), E - 1);
-        const int t = p / a.k;
-        atomicOr(&mask[e * NW + (t >> 5)], 1u << (t & 31));
+    int *pl = wsum + 8;                                       // [P] sorted pair order
+    // this thread's pairs p = tid + WG j: expert and router weight
+    int pe[GROUP_PPT];
+    float pw[GROUP_PPT];
+#pragma unroll
+    for (int j = 0; j < GROUP_PPT; ++j) {
+        const int p = tid + WG * j;
+        pe[j] = p < P ? min(max((int)ld_dev(a.ids + p), 0), E - 1) : 0;
+        pw[j] = p < P && a.weights ? ld_dev(a.weights + p) : 0.f;
     }
     lds_barrier();
-    // counts, and exclusive scans of the counts and of (count > 0); thread
-    // tid owns experts [tid*per, tid*per + per)
+    for (int i = tid; i < E * NW; i += WG) mask[i] = 0;
+    for (int i = tid; i < P; i += WG) pl[i] = i;
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < GROUP_PPT; ++j) {
+        const int p = tid + WG * j, t = p / a.k;
+        if (p < P) atomicOr(&mask[pe[j] * NW + (t >> 5)], 1u << (t & 31));
+    }
+    lds_barrier();
+    // counts, and exclusive scans of the counts and of the item counts;
+    // thread tid owns experts [tid*per, tid*per + per)
     const int per = (E + WG - 1) / WG, e0 = tid * per, e1 = min(E, e0 + per);
     int sc = 0, sn = 0;
     for (int e = e0; e < e1; ++e) {
@@ -399,11 +450,7 @@ __device__ void group_block(const DecodeArgs &a, int tid, unsigned char *lds) {
         sc += c;
         sn += ceil_div(c, a.tbi);
     }
-    int ic = sc, in = sn;
-    for (int o = 1; o < WAVE; o <<= 1) {
-        const int vc = __shfl_up(ic, o), vn = __shfl_up(in, o);
-        if (lane >= o) { ic += vc; in += vn; }
-    }
+    const int ic = wave_scan_incl(sc), in = wave_scan_incl(sn);
     if (lane == WAVE - 1) { wsum[2 * w] = ic; wsum[2 * w + 1] = in; }
     lds_barrier();
     int oc = ic - sc, on = in - sn;
@@ -428,23 +475,25 @@ __device__ void group_block(const DecodeArgs &a, int tid, unsigned char *lds) {
             st_dev(reinterpret_cast<uint4 *>(a.items + ITEM_INTS * (iidx[e] + q / a.tbi)),
                    make_uint4((uint32_t)e, (uint32_t)(offs[e] + q),
                               (uint32_t)min(a.tbi, cnt[e] - q), 0u));
-    stores_done();
-    lds_barrier();   // the default positions are written before the scatter
-    for (int p = tid; p < P; p += WG) {
-        const int e = min(max((int)ld_dev(a.ids + p), 0), E - 1);
-        const int t = p / a.k;
-        int r = __popc(mask[e * NW + (t >> 5)] & ((1u << (t & 31)) - 1u));
-        for (int q = 0; q < (t >> 5); ++q) r += __popc(mask[e * NW + q]);
-        const int pos = offs[e] + r;
-        if (pos < P) st_dev(a.pairs + pos, (int32_t)p);
-        const int slot = r % a.tbi;
-        if (slot < MAX_TB) {
-            int32_t *rec = a.items + ITEM_INTS * (iidx[e] + r / a.tbi);
-            st_dev(rec + 4 + slot, (int32_t)p);
-            st_dev(reinterpret_cast<float *>(rec) + 8 + slot,
-                   a.weights ? ld_dev(a.weights + p) : 0.f);
+#pragma unroll
+    for (int j = 0; j < GROUP_PPT; ++j) {
+        const int p = tid + WG * j;
+        if (p < P) {
+            const int e = pe[j], t = p / a.k;
+            int r = __popc(mask[e * NW + (t >> 5)] & ((1u << (t & 31)) - 1u));
+            for (int q = 0; q < (t >> 5); ++q) r += __popc(mask[e * NW + q]);
+            const int pos = offs[e] + r;
+            if (pos < P) pl[pos] = p;
+            const int slot = r % a.tbi;
+            if (slot < MAX_TB) {
+                int32_t *rec = a.items + ITEM_INTS * (iidx[e] + r / a.tbi);
+                st_dev(rec + 4 + slot, (int32_t)p);
+                st_dev(reinterpret_cast<float *>(rec) + 8 + slot, pw[j]);
+            }
         }
     }
+    lds_barrier();
+    for (int i = tid; i < P; i += WG) st_dev(a.pairs + i, (int32_t)pl[i]);
 }
 
 // ------------------------------------------------------------- router
@@ -528,23 +577,23 @@ __device__ void router_block(const DecodeArgs &a, int b, int tid, unsigned char 
     stores_done();
     lds_barrier();
     if (tid == 0) {
-        const uint32_t old = atomicAdd(a.hdr + HDR_TICKET + t, 1u);
+        const uint32_t old = atomicAdd(a.hdr + hdr_ticket(t), 1u);
         *flag = old == (uint32_t)(nrb - 1);
     }
     lds_barrier();
     if (!*flag) return;
-    if (tid == 0) st_dev(a.hdr + HDR_TICKET + t, 0u);
+    if (tid == 0) st_dev(a.hdr + hdr_ticket(t), 0u);
     topk_block(a, t, tid, lds);
     if (!a.do_group || a.T == 1) return;
     stores_done();
     lds_barrier();
     if (tid == 0) {
-        const uint32_t old = atomicAdd(a.hdr + HDR_TICKET + a.T, 1u);
+        const uint32_t old = atomicAdd(a.hdr + hdr_ticket(a.T), 1u);
         reinterpret_cast<int *>(lds)[0] = old == (uint32_t)(a.T - 1);
     }
     lds_barrier();
     if (!reinterpret_cast<int *>(lds)[0]) return;
-    if (tid == 0) st_dev(a.hdr + HDR_TICKET + a.T, 0u);
+    if (tid == 0) st_dev(a.hdr + hdr_ticket(a.T), 0u);
     group_block(a, tid, lds);
 }
 

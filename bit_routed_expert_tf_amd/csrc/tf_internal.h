@@ -8,8 +8,13 @@
 
 // Workspace header words (uint32): device-side flags, the number of expert
 // work items of the current step, then one ticket per token and one for the
-// whole step (counters that return to zero at the end of every step).
-enum { HDR_FLAGS = 0, HDR_NITEMS = 1, HDR_TICKET = 2 };
+// whole step (counters that return to zero at the end of every step).  Each
+// ticket has a 128-byte line of its own: the router workgroups of all tokens
+// take theirs at the same time, and atomics on one line serialise.
+enum { HDR_FLAGS = 0, HDR_NITEMS = 1 };
+__host__ __device__ constexpr int hdr_ticket(int i) { return 32 + 32 * i; }
+// Header bytes of a step of T tokens.
+__host__ __device__ constexpr size_t hdr_bytes(int T) { return (size_t)4 * hdr_ticket(T + 1); }
 enum { STAGE_A = 1, STAGE_B = 2, STAGE_C = 4 };
 constexpr int KC_BATCH = 8;       // pairs staged per pass in the down/combine kernel
 

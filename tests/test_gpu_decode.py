@@ -265,3 +265,32 @@ def test_expert_gemv_pairs_grouped_by_token(tfa, full):
             ref = ref + coef[p] * oracle.expert_from_blob(L["pool"][slots[p]], d, f,
                                                           x[t].astype(np.float64))
         check_token32(got[t], ref)
+
+
+# ------------------------------------------------------------ top-k ties
+@pytest.mark.parametrize("E,k,pattern", [(128, 8, "all"), (128, 8, "pairs"), (128, 8, "blocks"),
+                                         (64, 8, "pairs"), (300, 16, "blocks"), (9, 8, "pairs")])
+def test_topk_exact_ties(tfa, E, k, pattern):
+    """Router rows copied between experts give exactly equal fp64 logits:
+    the selection must break them by the lower id, as the oracle does."""
+    d = 256
+    L = oracle_layer(TINY.seed + E, 0, d, E, k, 64, 64)
+    r = L["router"]
+    src = {"all": np.zeros(E, int), "pairs": np.arange(E) & ~1,
+           "blocks": (np.arange(E) // 5) * 5}[pattern]
+    for key in ("q", "scale", "bias"):
+        r[key] = np.ascontiguousarray(r[key][src])
+    D = device_layer(L)
+    x = gen.tokens(TINY.seed, 8, d)
+    xt = torch.from_numpy(x.view(np.int16)).cuda()
+    logits = torch.empty((8, E), dtype=torch.float64, device="cuda")
+    ids, w, _ = tfa.tf_router_topk(D, xt, logits=logits)
+    torch.cuda.synchronize()
+    ref_l = np.stack([oracle.qmatvec(r, x[t].astype(np.float64)) for t in range(8)])
+    ref_ids = np.stack([oracle.topk(ref_l[t], k) for t in range(8)])
+    got = ids.cpu().numpy()
+    assert np.array_equal(got, ref_ids)
+    if pattern == "all":
+        assert np.array_equal(got, np.tile(np.arange(k), (8, 1)))
+    ref_p = np.stack([oracle.softmax(ref_l[t][ref_ids[t]]) for t in range(8)])
+    assert np.max(np.abs(w.cpu().numpy() - ref_p)) <= 1e-6

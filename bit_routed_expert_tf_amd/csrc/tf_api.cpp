@@ -66,7 +66,7 @@ tf_status check_layer(const tf_moe_layer *L) {
 
 // Decode workspace layout (offsets in bytes).
 struct WsLayout {
-    size_t hdr, logits, items, pairs, hs, ys, hr, xb, total;
+    size_t hdr, logits, items, pairs, hs, ys, hr, xb, ye, ctk, total;
 };
 
 WsLayout decode_layout(int d, int f, int fs, int E, int k, int T) {
@@ -80,6 +80,8 @@ WsLayout decode_layout(int d, int f, int fs, int E, int k, int T) {
     w.ys = o; o += up256((size_t)4 * T * d);
     w.hr = o; o += up256(h_row_bytes(f) * T * k);
     w.xb = o; o += up256((size_t)16 * tfk::xb_row_u4(d) * T);
+    w.ye = o; o += up256((size_t)4 * T * k * d);           // decode: per-pair down rows
+    w.ctk = o; o += up256((size_t)128 * T * (d / 32));     // decode: down tile tickets
     w.total = o;
     return w;
 }
@@ -315,6 +317,8 @@ tf_status tf_moe_layer_fwd(const tf_moe_layer *L, const uint16_t *x, int32_t T,
     a.h_s = at<uint4>(ws, w.hs);
     a.y_s = at<float>(ws, w.ys);
     a.h_r = at<uint4>(ws, w.hr);
+    a.y_e = at<float>(ws, w.ye);
+    a.ctk = at<uint32_t>(ws, w.ctk);
     a.do_group = 1;
     // T == 1: one item per rank; else items of up to tbi pairs of one expert
     // (at most E + T*k/tbi of them)

@@ -873,6 +873,59 @@ __global__ __launch_bounds__(256, 4) void k_stage_c(DecodeArgs a) {
     }
 }
 
+// ------------------------------------------------ routed down, decode step
+// Layer decode (not the standalone GEMV): one workgroup per (pair, 32-row
+// tile), a wave per 8 rows (8 lanes per row); the pair's hidden row is
+// staged once (it already carries the router weight).  Each workgroup
+// stores its rows of y_e[pair]; the last of the token's k pairs to finish a
+// tile (a ticket) forms y = y_s + sum over ranks of y_e in rank order ->
+// fp16 (and y32).
+template <int JF>
+__global__ __launch_bounds__(256, 4) void k_stage_c1(DecodeArgs a) {
+    constexpr int LPR = 8, RPW = 64 / LPR;
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
+    const int tiles = a.d >> 5;
+    const int pair = blockIdx.x / tiles, tile = blockIdx.x - pair * tiles, t = pair / a.k;
+    const int row0 = 32 * tile + RPW * w, K = a.f, H = K >> 5, G = K >> 6;
+    uint32_t *lsb = reinterpret_cast<uint32_t *>(lds);                    // [4 waves][RPW * G]
+    unsigned char *hst = reinterpret_cast<unsigned char *>(lsb + 4 * RPW * G);
+    int *flag = reinterpret_cast<int *>(hst + hst_bytes(K));
+    HStage<(JF * 64 + 255) / 256, (JF * 8 + 255) / 256> Hs;
+    hs_load(Hs, a.h_r + (size_t)pair * 10 * H, 1, K, tid);
+    Mat g, u, dn;
+    blob_mats(expert_blob(a, a.ids[pair]), a.d, a.f, g, u, dn);
+    Tile<LPR, JF> tl;
+    tile_load_sb<LPR, JF>(tl, dn, row0, K, lane);
+    tile_load_q<LPR, JF>(tl, dn, row0, K, lane);
+    hs_store(Hs, 1, K, hst, tid);
+    tile_store_sb(tl, lsb + w * RPW * G, G, lane);
+    lds_barrier();
+    const float v = row_sum<LPR>(tile_dot<LPR, JF, true>(
+        tl, lsb + w * RPW * G, G, reinterpret_cast<const uint4 *>(hst),
+        reinterpret_cast<const uint4 *>(hst + 64 * H), reinterpret_cast<const float2 *>(hst + 128 * H),
+        H, lane));
+    if (lane % LPR == 0) st_dev(a.y_e + (size_t)pair * a.d + row0 + lane / LPR, v);
+    stores_done();
+    lds_barrier();
+    uint32_t *tk = a.ctk + 32 * (t * tiles + tile);
+    if (tid == 0) {
+        const uint32_t old = atomicAdd(tk, 1u);
+        *flag = old == (uint32_t)(a.k - 1);
+    }
+    lds_barrier();
+    if (!*flag) return;
+    if (tid == 0) st_dev(tk, 0u);
+    if (tid < 32) {
+        const size_t o = (size_t)t * a.d + 32 * tile + tid;
+        float sum = 0.f;
+        for (int r = 0; r < a.k; ++r) sum += ld_dev(a.y_e + (size_t)(t * a.k + r) * a.d + 32 * tile + tid);
+        const float y = a.y_s[o] + sum;
+        if (a.y32) a.y32[o] = y;
+        a.y[o] = f2h(y);
+    }
+}
+
 // ------------------------------------------------------ prefill combine
 // Combine: y[t] = y_s[t] + sum over ranks r of y_e[t*k + r], in rank order,
 // then fp16 round to nearest even (and the fp32 value when asked).
@@ -930,6 +983,7 @@ int lds_b(const DecodeArgs &a, int lpr) {
 int lds_c(const DecodeArgs &a) {
     return 4 * 32 + 4 * 8 * 8 * (a.f >> 6) + KC_BATCH * hst_bytes(a.f);
 }
+int lds_c1(const DecodeArgs &a) { return 4 * 4 * 8 * (a.f >> 6) + hst_bytes(a.f) + 16; }
 
 template <int LPR, int J>
 hipError_t launch_ab(const DecodeArgs &a, int which, hipStream_t s) {
@@ -950,6 +1004,11 @@ hipError_t launch_ab(const DecodeArgs &a, int which, hipStream_t s) {
 
 template <int JF>
 hipError_t launch_c(const DecodeArgs &a, hipStream_t s) {
+    if (!a.gemv_slot) {   // layer decode: per (pair, 32-row tile), last pair combines
+        const int n = a.T * a.k * (a.d >> 5);
+        if (n) TF_LAUNCH(TF_KERNEL_DOWN_COMBINE, k_stage_c1<JF>, dim3(n), dim3(WG), lds_c1(a), s, a);
+        return hipGetLastError();
+    }
     const int n = a.T * (a.d >> 3);
     if (n) TF_LAUNCH(TF_KERNEL_DOWN_COMBINE, k_stage_c<JF>, dim3(n), dim3(WG), lds_c(a), s, a);
     return hipGetLastError();

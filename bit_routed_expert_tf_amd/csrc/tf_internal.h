@@ -45,6 +45,8 @@ struct DecodeArgs {
     int32_t *pairs;              // [T*k] pair index t*k+r sorted by (expert, t, r)
     int32_t *g_counts, *g_offsets;  // grouping outputs [E], [E+1] (NULL in layer calls)
     uint4 *xb;                   // grouped steps: x rows in B-operand form (NULL otherwise)
+    uint32_t *ctk;               // decode down launch: one ticket per (token, 32-row tile),
+                                 // 32 words apart (zero between launches)
     // hidden activations as hi/lo fp16 pair rows (10*K/32 uint4 per row, see
     // tf_decode.hip): shared [T][fs], routed [T*k][f] (or [P][f])
     uint4 *h_s;

@@ -423,12 +423,16 @@ __device__ void group_block(const DecodeArgs &a, int tid, unsigned char *lds) {
     // this thread's pairs p = tid + WG j: expert and router weight
     int pe[GROUP_PPT];
     float pw[GROUP_PPT];
+    // (loads from clamped positions, all in flight at once)
+    int ev[GROUP_PPT];
 #pragma unroll
     for (int j = 0; j < GROUP_PPT; ++j) {
-        const int p = tid + WG * j;
-        pe[j] = p < P ? min(max((int)ld_dev(a.ids + p), 0), E - 1) : 0;
-        pw[j] = p < P && a.weights ? ld_dev(a.weights + p) : 0.f;
+        const int pc = min(tid + WG * j, P - 1);
+        ev[j] = (int)ld_dev(a.ids + pc);
+        pw[j] = a.weights ? ld_dev(a.weights + pc) : 0.f;
     }
+#pragma unroll
+    for (int j = 0; j < GROUP_PPT; ++j) pe[j] = min(max(ev[j], 0), E - 1);
     lds_barrier();
     for (int i = tid; i < E * NW; i += WG) mask[i] = 0;
     for (int i = tid; i < P; i += WG) pl[i] = i;
@@ -918,8 +922,15 @@ __global__ __launch_bounds__(256, 4) void k_stage_c1(DecodeArgs a) {
     if (tid == 0) st_dev(tk, 0u);
     if (tid < 32) {
         const size_t o = (size_t)t * a.d + 32 * tile + tid;
+        // every rank's value in flight at once, then added in rank order
+        float yv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            yv[r] = ld_dev(a.y_e + (size_t)(t * a.k + min(r, a.k - 1)) * a.d + 32 * tile + tid);
         float sum = 0.f;
-        for (int r = 0; r < a.k; ++r) sum += ld_dev(a.y_e + (size_t)(t * a.k + r) * a.d + 32 * tile + tid);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if (r < a.k) sum += yv[r];
         const float y = a.y_s[o] + sum;
         if (a.y32) a.y32[o] = y;
         a.y[o] = f2h(y);

@@ -140,6 +140,7 @@ hipError_t grouped_step(const tf_moe_layer *L, const uint16_t *x, int T, const i
     a.tbi = tiles ? 16 : 4;
     const int P = T * a.k;
     const int max_items = P < a.E + P / a.tbi ? P : a.E + P / a.tbi;
+    a.max_items = max_items;
     a.a_router_blocks = ((a.E + 3) / 4) * T;
     hipError_t e = tf_launch_decode(a, STAGE_A, s);
     if (e == hipSuccess)

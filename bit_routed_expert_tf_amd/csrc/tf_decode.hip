@@ -944,8 +944,14 @@ __global__ __launch_bounds__(256) void k_pf_combine(DecodeArgs a) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= (size_t)a.T * a.d) return;
     const size_t t = i / a.d, c = i - t * a.d;
+    // every rank's value in flight at once, then added in rank order
+    float yv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) yv[r] = a.y_e[(t * a.k + min(r, a.k - 1)) * a.d + c];
     float s = 0.f;
-    for (int r = 0; r < a.k; ++r) s += a.y_e[(t * a.k + r) * a.d + c];
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        if (r < a.k) s += yv[r];
     const float y = a.y_s[i] + s;
     if (a.y32) a.y32[i] = y;
     a.y[i] = f2h(y);

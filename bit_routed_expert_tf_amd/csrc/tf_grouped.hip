@@ -191,20 +191,17 @@ __device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1, KC> &L) {
     const int d = a.d;
     const int tiles_s = DOWN ? d / 64 : a.fs / 32, tiles_r = DOWN ? d / 64 : a.f / 32;
     const int ns = ((a.T + UT - 1) / UT) * tiles_s;
-    const int n_items = (int)ld_dev(a.hdr + HDR_NITEMS);
-    const int n_units = ns + n_items * tiles_r;
     const int grid = (int)gridDim.x;
     int u = blockIdx.x;
-    if (u >= n_units) return;
-    if (tid < 2 * PARTS) L.zero[tid] = make_uint4(0, 0, 0, 0);
 
-    // the item record of unit v (a valid record when v is not routed).  The
-    // address takes an opaque zero, so the values stay in vector registers
-    // and nothing waits for them before their first use.
+    // the item record of unit v (a valid record when v is not routed; past
+    // the step's items, a stale record of the workspace that no unit uses).
+    // The address takes an opaque zero, so the values stay in vector
+    // registers and nothing waits for them before their first use.
     auto load_rec = [&](int v) {
         int z = 0;
         asm volatile("" : "+v"(z));
-        const int item = min(max(v - ns, 0) / tiles_r, max(n_items - 1, 0)) + z;
+        const int item = min(max(v - ns, 0) / tiles_r, a.max_items - 1) + z;
         const uint4 *p = reinterpret_cast<const uint4 *>(a.items + ITEM_INTS * item);
         Rec r;
         r.r0 = ld_dev(p);
@@ -348,7 +345,13 @@ __device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1, KC> &L) {
     // this lane's column: token tc of slot sc
     const int tc = j >> 2, sc = j & 3;
     const Masks km = masks();
-    Unit cur = unit_of<DOWN, KC, DEPTH>(a, u, settle(load_rec(u)), ns, tiles_s, tiles_r);
+    // the first record is read together with the item count
+    const Rec rec0 = load_rec(u);
+    const int n_items = (int)ld_dev(a.hdr + HDR_NITEMS);
+    const int n_units = ns + n_items * tiles_r;
+    if (u >= n_units) return;
+    if (tid < 2 * PARTS) L.zero[tid] = make_uint4(0, 0, 0, 0);
+    Unit cur = unit_of<DOWN, KC, DEPTH>(a, u, settle(rec0), ns, tiles_s, tiles_r);
     Str scu = mkstr(cur);
     uint4 qa[2 * NR], qb[DEPTH == 2 ? 2 * NR : 1];
 #pragma unroll

@@ -60,6 +60,7 @@ struct DecodeArgs {
     int a_router_blocks, a_shared_blocks, b_routed_blocks, b_shared_blocks;
     int tbx;                     // tokens per shared gate/up block (<= MAX_TB)
     int tbi;                     // tokens per routed expert item (grouped steps)
+    int max_items;               // grouped steps: bound of the step's expert items
     int topk, do_group;
     // standalone GEMV mode (gemv_slot != NULL): pairs instead of routed items
     const int32_t *gemv_slot, *gemv_token;

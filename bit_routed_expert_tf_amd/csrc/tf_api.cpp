@@ -141,7 +141,7 @@ hipError_t grouped_step(const tf_moe_layer *L, const uint16_t *x, int T, const i
     const int P = T * a.k;
     const int max_items = P < a.E + P / a.tbi ? P : a.E + P / a.tbi;
     a.max_items = max_items;
-    a.a_router_blocks = ((a.E + 3) / 4) * T;
+    a.a_router_blocks = router_blocks(a.E, T);
     hipError_t e = tf_launch_decode(a, STAGE_A, s);
     if (e == hipSuccess)
         e = tiles ? tf_launch_prefill_tiles(a, max_items, s) : tf_launch_grouped(a, max_items, s);
@@ -229,7 +229,7 @@ tf_status tf_router_topk(const tf_qmat *router, const uint16_t *x, int32_t T, in
     a.forced = forced_ids; a.ids = ids; a.weights = weights;
     a.hdr = at<uint32_t>(ws, 0);
     a.logits = logits ? logits : at<double>(ws, router_hdr_bytes(T));
-    a.a_router_blocks = ((E + 3) / 4) * T;
+    a.a_router_blocks = router_blocks(E, T);
     a.topk = 1;
     a.do_group = 0;
     a.f = a.fs = 64;
@@ -325,7 +325,7 @@ tf_status tf_moe_layer_fwd(const tf_moe_layer *L, const uint16_t *x, int32_t T,
     // (at most E + T*k/tbi of them)
     const int max_items = T == 1 ? a.k
                           : (T * a.k < a.E + T * a.k / a.tbi ? T * a.k : a.E + T * a.k / a.tbi);
-    const int n_router = ((a.E + 3) / 4) * T;
+    const int n_router = router_blocks(a.E, T);
     // rows per workgroup: gate/up 2*RPW, shared down 4*RPW (RPW = 64 / lanes per row)
     const int rpw = 64 / tf_decode_lpr(a);
     const int n_shared_a = (a.fs / (2 * rpw)) * ((T + a.tbx - 1) / a.tbx);

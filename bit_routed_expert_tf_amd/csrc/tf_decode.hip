@@ -501,52 +501,41 @@ __device__ void group_block(const DecodeArgs &a, int tid, unsigned char *lds) {
 }
 
 // ------------------------------------------------------------- router
-// Four router rows per workgroup (one per wave).  Logit of expert e: sum
-// over 16-element chunks of s_g * sum_i q_i x_i + b_g * sum_i x_i, products
-// exact and every sum in fp64.
+// ROUTER_ROWS router rows per workgroup, two waves per row: lane r of a row
+// (0..127) takes the 16-element chunks r and r + 128, reading its codes and
+// its x straight into registers.  Logit of expert e: sum over chunks of
+// s_g * sum_i q_i x_i + b_g * sum_i x_i, products exact and every sum in
+// fp64 (per lane over its chunks, then over the wave, then the two waves).
 __device__ void router_block(const DecodeArgs &a, int b, int tid, unsigned char *lds) {
     const int lane = tid & 63, w = uniform(tid >> 6);
-    const int nrb = (a.E + 3) >> 2;
-    const int t = b / nrb, e = (b - t * nrb) * 4 + w;
+    const int nrb = (a.E + ROUTER_ROWS - 1) / ROUTER_ROWS;
+    const int t = b / nrb, e0 = (b - t * nrb) * ROUTER_ROWS, e = e0 + (w >> 1);
     const int d = a.d, NC = d >> 4, G = d >> 6;
-    constexpr int JR = 4;   // d <= 4096
+    constexpr int JR = 2;   // d <= 4096: at most 256 chunks over a row's 128 lanes
     const bool row_ok = e < a.E;
     const int er = row_ok ? e : 0;
-    // x as fp64 into LDS: thread c < NC converts 16 values (two uint4 loads)
-    uint4 xv0 = make_uint4(0, 0, 0, 0), xv1 = xv0;
-    if (tid < NC) {
-        const uint4 *xv = reinterpret_cast<const uint4 *>(a.x + (size_t)t * d);
-        xv0 = xv[2 * tid];
-        xv1 = xv[2 * tid + 1];
-    }
-    uint4 qv[JR];
-    uint32_t sbw[JR];
+    const int rl = (w & 1) * WAVE + lane;
     const uint4 *qrow = reinterpret_cast<const uint4 *>(a.rq + (size_t)er * d);
+    const uint4 *xrow = reinterpret_cast<const uint4 *>(a.x + (size_t)t * d);
+    uint4 qv[JR], x0[JR], x1[JR];
+    uint32_t sbw[JR];
 #pragma unroll
     for (int j = 0; j < JR; ++j) {
-        const int c = min(lane + WAVE * j, NC - 1);
+        const int c = min(rl + 2 * WAVE * j, NC - 1);
         qv[j] = qrow[c];
+        x0[j] = xrow[2 * c];
+        x1[j] = xrow[2 * c + 1];
         sbw[j] = (uint32_t)a.rs[(size_t)er * G + (c >> 2)] |
                  ((uint32_t)a.rb[(size_t)er * G + (c >> 2)] << 16);
     }
-    double *xd = reinterpret_cast<double *>(lds);
-    double *x16 = xd + d;
-    int *flag = reinterpret_cast<int *>(x16 + NC);
-    if (tid < NC) {
-        const uint32_t w8[8] = {xv0.x, xv0.y, xv0.z, xv0.w, xv1.x, xv1.y, xv1.z, xv1.w};
-        double v[16], s = 0.0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            v[2 * i] = (double)h2f((uint16_t)(w8[i] & 0xFFFF));
-            v[2 * i + 1] = (double)h2f((uint16_t)(w8[i] >> 16));
-            s += v[2 * i] + v[2 * i + 1];
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            reinterpret_cast<double2 *>(xd + 16 * tid)[i] = make_double2(v[2 * i], v[2 * i + 1]);
-        x16[tid] = s;
-    }
+    double *part = reinterpret_cast<double *>(lds);   // [4] wave sums
+    int *flag = reinterpret_cast<int *>(part + 4);
     if (a.xb && b == t * nrb) {   // the token's first router workgroup: x in B-operand form
+        uint4 xv0 = make_uint4(0, 0, 0, 0), xv1 = xv0;
+        if (tid < NC) {
+            xv0 = xrow[2 * tid];
+            xv1 = xrow[2 * tid + 1];
+        }
         uint4 *row = a.xb + (size_t)t * xb_row_u4(d);
         float X = 0.f, C = 0.f;
         if (tid < NC) xb_produce(xv0, xv1, row, tid, X, C);
@@ -557,27 +546,29 @@ __device__ void router_block(const DecodeArgs &a, int b, int tid, unsigned char 
         C += dpp_f<DPP_XOR2>(C);
         if (tid < NC && !(tid & 3)) reinterpret_cast<float2 *>(row + d / 8)[tid >> 2] = make_float2(X, C);
     }
-    lds_barrier();
     double acc = 0.0;
 #pragma unroll
     for (int j = 0; j < JR; ++j) {
-        const int c0 = lane + WAVE * j;
-        const int c = min(c0, NC - 1);
+        const int c0 = rl + 2 * WAVE * j;
         const uint32_t w4[4] = {qv[j].x, qv[j].y, qv[j].z, qv[j].w};
-        const double2 *xx = reinterpret_cast<const double2 *>(xd + 16 * c);
-        double D = 0.0;
+        const uint32_t w8[8] = {x0[j].x, x0[j].y, x0[j].z, x0[j].w, x1[j].x, x1[j].y, x1[j].z, x1[j].w};
+        double D = 0.0, s16 = 0.0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const double2 xp = xx[i];
-            D = fma((double)((w4[i >> 1] >> (16 * (i & 1))) & 0xFF), xp.x, D);
-            D = fma((double)((w4[i >> 1] >> (16 * (i & 1) + 8)) & 0xFF), xp.y, D);
+            const double v0 = (double)h2f((uint16_t)(w8[i] & 0xFFFF));
+            const double v1 = (double)h2f((uint16_t)(w8[i] >> 16));
+            s16 += v0 + v1;
+            D = fma((double)((w4[i >> 1] >> (16 * (i & 1))) & 0xFF), v0, D);
+            D = fma((double)((w4[i >> 1] >> (16 * (i & 1) + 8)) & 0xFF), v1, D);
         }
         const uint32_t sw = (c0 < NC && row_ok) ? sbw[j] : 0u;
-        acc = fma((double)h2f((uint16_t)(sw & 0xFFFF)), D,
-                  fma((double)h2f((uint16_t)(sw >> 16)), x16[c], acc));
+        acc = fma((double)h2f((uint16_t)(sw & 0xFFFF)), D, fma((double)h2f((uint16_t)(sw >> 16)), s16, acc));
     }
     acc = wave_sum_f64(acc);
-    if (lane == 0 && row_ok) st_dev(a.logits + (size_t)t * a.E + e, acc);
+    if (lane == 0) part[w] = acc;
+    lds_barrier();
+    if (tid < ROUTER_ROWS && e0 + tid < a.E)
+        st_dev(a.logits + (size_t)t * a.E + e0 + tid, part[2 * tid] + part[2 * tid + 1]);
     stores_done();
     lds_barrier();
     if (tid == 0) {
@@ -976,10 +967,9 @@ int gateup_lds(const DecodeArgs &a, int lpr, int rows) {
 }
 
 int lds_a(const DecodeArgs &a, int lpr) {
-    const int d = a.d, NC = d >> 4;
     int r = 0;
     if (a.a_router_blocks) {
-        const int route = 8 * d + 8 * NC + 16;
+        const int route = 8 * 4 + 16;   // wave sums and the ticket flag
         const int topk = topk_lds_bytes(a.E);
         const int group = a.do_group ? group_lds_bytes(a.E, a.T) : 0;
         r = max(route, max(topk, group));

@@ -17,6 +17,9 @@ __host__ __device__ constexpr int hdr_ticket(int i) { return 32 + 32 * i; }
 __host__ __device__ constexpr size_t hdr_bytes(int T) { return (size_t)4 * hdr_ticket(T + 1); }
 enum { STAGE_A = 1, STAGE_B = 2, STAGE_C = 4 };
 constexpr int KC_BATCH = 8;       // pairs staged per pass in the down/combine kernel
+constexpr int ROUTER_ROWS = 2;    // router rows per workgroup (two waves per row)
+// Router workgroups of a step of T tokens over E experts.
+__host__ __device__ constexpr int router_blocks(int E, int T) { return ((E + ROUTER_ROWS - 1) / ROUTER_ROWS) * T; }
 
 // Bytes of one hidden row of K values in the global hi/lo layout.
 __host__ __device__ constexpr size_t h_row_bytes(int K) { return (size_t)160 * (K >> 5); }

@@ -341,20 +341,45 @@ __device__ void topk_block(const DecodeArgs &a, int t, int tid, unsigned char *l
         }
         lds_barrier();
         const int S = *ns;
-        for (int q = tid; q < S; q += WG) {
-            const int i = sid[q];
-            const uint64_t ki = skey[q];
+        if (S <= WG / 4) {
+            // four threads per survivor, each over every fourth survivor, the
+            // four counts added by lane moves within the quad
+            const int q = tid >> 2, part = tid & 3, qc = min(q, max(S - 1, 0));
+            const int i = sid[qc];
+            const uint64_t ki = skey[qc];
             int r = 0;
-            for (int j0 = 0; j0 < S; j0 += 8) {
+            for (int j0 = part; j0 < S; j0 += 32) {
+                uint64_t kj[8];
+                int jj[8];
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
-                    const int jq = min(j0 + u, S - 1);
-                    const uint64_t kj = skey[jq];
-                    const int j = sid[jq];
-                    r += j0 + u < S && (kj > ki || (kj == ki && j < i));
+                    const int jq = min(j0 + 4 * u, S - 1);
+                    kj[u] = skey[jq];
+                    jj[u] = sid[jq];
                 }
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    r += (int)((j0 + 4 * u < S) & ((kj[u] > ki) | ((kj[u] == ki) & (jj[u] < i))));
             }
-            if (r < a.k) sel[r] = i;
+            r += __builtin_amdgcn_update_dpp(0, r, DPP_XOR1, 0xF, 0xF, false);
+            r += __builtin_amdgcn_update_dpp(0, r, DPP_XOR2, 0xF, 0xF, false);
+            if (q < S && part == 0 && r < a.k) sel[r] = i;
+        } else {
+            for (int q = tid; q < S; q += WG) {
+                const int i = sid[q];
+                const uint64_t ki = skey[q];
+                int r = 0;
+                for (int j0 = 0; j0 < S; j0 += 8) {
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const int jq = min(j0 + u, S - 1);
+                        const uint64_t kj = skey[jq];
+                        const int j = sid[jq];
+                        r += j0 + u < S && (kj > ki || (kj == ki && j < i));
+                    }
+                }
+                if (r < a.k) sel[r] = i;
+            }
         }
     }
     lds_barrier();

@@ -509,7 +509,7 @@ __device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1, KC> &L) {
     }
 }
 
-constexpr int KC_GU = 8, KC_DN = 8;   // groups per staged chunk
+constexpr int KC_GU = 8, KC_DN = 4;   // groups per staged chunk
 constexpr int DEPTH = 1;              // chunks loaded ahead
 
 __global__ __launch_bounds__(256, 4) void k_gu(DecodeArgs a) {

@@ -186,6 +186,7 @@ __device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1, KC> &L) {
     constexpr int HW = KC / 4;        // down staging: uint4 per lane per chunk
     constexpr int SW = KC / 4;        // scale/bias entries per thread per chunk
     static_assert(!DOWN || 8 * KC <= 64, "one lane per 8-value block partial of a chunk");
+    static_assert(DOWN || KC % 8 == 0, "gate/up staging copies whole uint4 per lane");
     const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
     const int j = lane & 15, b = lane >> 4;
     const int d = a.d;

@@ -499,8 +499,6 @@ def run_slot(args):
                                                               device=dev), d, f, fs, k, device=dev))
         print(f"slot: layer {l} generated ({time.time() - t0:.0f} s)", file=sys.stderr, flush=True)
     setup = time.time() - t0
-    slot_pool = torch.empty(L * S * stride, dtype=torch.uint8, device=dev)
-    cache = api.SlotCache(L, E, S, k, stride, slot_pool, host, trace_cap=ntok)
     X = torch.from_numpy(gen.tokens(wl.seed, ntok, d).view(np.int16)).to(dev)
     F = torch.from_numpy(np.stack([gen.zipf_ids(wl.seed, l, ntok, E, k) for l in range(L)])).to(dev)
     Y = torch.empty((L, ntok, d), dtype=torch.float16, device=dev)
@@ -515,25 +513,41 @@ def run_slot(args):
     torch.cuda.synchronize()
     peak = 4 * (256 << 20) / (time.perf_counter() - c0) / 1e9
     del big
-    w0 = time.perf_counter()
-    for t in range(ntok):
-        for l in range(L):
-            api.tf_moe_layer_fwd(layers[l], X[t:t + 1], forced_ids=F[l, t:t + 1],
-                                 y=Y[l, t:t + 1], cache=cache, layer_idx=l, ws=ws,
-                                 copy_stream=copy)
-        if t % 256 == 255:
-            print(f"slot: token {t + 1}", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    hits = sum(int(cache.trace(l, ntok * k)[0].sum()) for l in range(L))
-    filled = cache.bytes_filled()
-    cache.close()
-    return {"metric": "slot-cache stack decode tokens/s (30 layers, 16 slots, PCIe misses)",
-            "workload": wl.name, "tokens": ntok, "value": round(ntok / wall, 2),
-            "unit": "tokens/s", "hit_rate": round(hits / (L * ntok * k), 4),
-            "h2d_bytes": filled, "h2d_GBps": round(filled / wall / 1e9, 2),
-            "pinned_h2d_peak_GBps": round(peak, 2), "setup_s": round(setup, 1),
-            "wall_s": round(wall, 2)}
+
+    def one(n_slots, policy):
+        """One pass of the token stream through the stack with this cache."""
+        slot_pool = torch.empty(L * n_slots * stride, dtype=torch.uint8, device=dev)
+        cache = api.SlotCache(L, E, n_slots, k, stride, slot_pool, host, trace_cap=ntok,
+                              policy=policy)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        for t in range(ntok):
+            for l in range(L):
+                api.tf_moe_layer_fwd(layers[l], X[t:t + 1], forced_ids=F[l, t:t + 1],
+                                     y=Y[l, t:t + 1], cache=cache, layer_idx=l, ws=ws,
+                                     copy_stream=copy)
+            if t % 256 == 255:
+                print(f"slot: {policy} {n_slots} slots, token {t + 1}", file=sys.stderr, flush=True)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        hits = sum(int(cache.trace(l, ntok * k)[0].sum()) for l in range(L))
+        filled = cache.bytes_filled()
+        cache.close()
+        del slot_pool
+        return {"slots": n_slots, "policy": policy, "value": round(ntok / wall, 2),
+                "hit_rate": round(hits / (L * ntok * k), 4), "h2d_bytes": filled,
+                "h2d_GBps": round(filled / wall / 1e9, 2), "wall_s": round(wall, 2)}
+
+    base = one(S, "lfu")
+    out = {"metric": "slot-cache stack decode tokens/s (30 layers, 16 slots, PCIe misses)",
+           "workload": wl.name, "tokens": ntok, "value": base["value"], "unit": "tokens/s",
+           "hit_rate": base["hit_rate"], "h2d_bytes": base["h2d_bytes"],
+           "h2d_GBps": base["h2d_GBps"], "pinned_h2d_peak_GBps": round(peak, 2),
+           "setup_s": round(setup, 1), "wall_s": base["wall_s"]}
+    if args.slot_sweep:   # slot counts x policies (the LFU reading and the LRU gloss)
+        out["sweep"] = [one(n, pol) for n in (8, 16, 32) for pol in ("lfu", "lru")
+                        if not (n == S and pol == "lfu")] + [dict(base)]
+    return out
 
 
 def main():
@@ -547,6 +561,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run plain 256 MiB device copies (memory-counter calibration)")
+    ap.add_argument("--slot-sweep", action="store_true",
+                    help="slot-cache workload: also run 8, 16 and 32 slots under LFU and LRU")
     ap.add_argument("--workload", choices=["decode", "prefill", "stack", "slot-cache"],
                     default="decode",
                     help="decode (default, the headline line); the others measure the "

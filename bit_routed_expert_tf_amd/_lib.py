@@ -22,6 +22,7 @@ TF_FLAG_ID_RANGE, TF_FLAG_ID_REPEAT = 1, 2
 TF_KERNEL_ROUTER_SHARED_GATEUP, TF_KERNEL_ROUTED_GATEUP_SHARED_DOWN, TF_KERNEL_DOWN_COMBINE = 1, 2, 4
 TF_KERNEL_PREFILL_DOWN, TF_KERNEL_PREFILL_COMBINE = 8, 16
 TF_KERNEL_PREFILL_GATEUP, TF_KERNEL_GROUP = 32, 64
+TF_SLOT_LFU, TF_SLOT_LRU = 0, 1
 
 c_void_p, c_int32, c_int64, c_size_t = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 
@@ -82,6 +83,7 @@ _SIGS = {
                                       ctypes.POINTER(c_int64)]),
     "tf_slot_cache_reset": (c_int32, [c_void_p]),
     "tf_slot_cache_bytes_filled": (c_int64, [c_void_p]),
+    "tf_slot_cache_set_policy": (c_int32, [c_void_p, c_int32]),
 }
 
 _lib = None

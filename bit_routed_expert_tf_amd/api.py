@@ -227,7 +227,7 @@ class SlotCache:
     """Owning wrapper of a ``tf_slot_cache`` handle."""
 
     def __init__(self, n_layers, n_experts, n_slots, top_k, blob_stride, slot_pool, host_pool,
-                 trace_cap=0):
+                 trace_cap=0, policy="lfu"):
         self.slot_pool, self.host_pool = slot_pool, host_pool
         self.n_layers, self.n_experts, self.n_slots, self.top_k = n_layers, n_experts, n_slots, top_k
         self.blob_stride = blob_stride
@@ -236,6 +236,12 @@ class SlotCache:
                                           _p(slot_pool), _p(host_pool), trace_cap,
                                           ctypes.byref(h)))
         self.handle = h
+        self.set_policy(policy)
+
+    def set_policy(self, policy):
+        """Eviction rule of later lookups: "lfu" (default) or "lru"."""
+        code = {"lfu": _lib.TF_SLOT_LFU, "lru": _lib.TF_SLOT_LRU}[policy]
+        check(load().tf_slot_cache_set_policy(self.handle, code))
 
     def close(self):
         if self.handle:

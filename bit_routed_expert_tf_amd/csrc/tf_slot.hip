@@ -14,7 +14,9 @@
 // Policy (reading of "LFU"): a slot's count is 1 on fill and +1 per hit; the
 // token's own ids are pinned; misses are taken in rank order; the victim is
 // the lowest empty slot, else the unpinned slot with the smallest
-// (count, last-use token, slot index); every layer starts empty.
+// (count, last-use token, slot index); every layer starts empty.  The LRU
+// option (the sh.edu-sjtu.cn article's gloss, "三件事") takes the unpinned
+// slot with the smallest (last-use token, slot index) instead.
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -28,6 +30,7 @@
 // Plain device view of the tables (passed to the lookup kernel by value).
 struct SlotDev {
     int L, E, S, k;
+    int policy;                // TF_SLOT_LFU or TF_SLOT_LRU
     int64_t trace_cap;
     int32_t *slot_of;          // [L][E]  -1 = not cached
     int16_t *expert_of;        // [L][S]  -1 = empty
@@ -104,8 +107,10 @@ __global__ __launch_bounds__(64) void k_lookup(SlotDev c, int layer, const int32
         if (v < 0) {
             for (int s = 0; s < S; ++s) {
                 if ((pinned >> s) & 1u) continue;
-                if (v < 0 || count[s] < count[v] || (count[s] == count[v] && last[s] < last[v]))
-                    v = s;
+                const bool lt = c.policy == TF_SLOT_LRU
+                                    ? last[s] < last[v]
+                                    : count[s] < count[v] || (count[s] == count[v] && last[s] < last[v]);
+                if (v < 0 || lt) v = s;
             }
             slot_of[expert_of[v]] = -1;
         }
@@ -326,5 +331,12 @@ tf_status tf_slot_cache_reset(tf_slot_cache *c) {
 }
 
 int64_t tf_slot_cache_bytes_filled(const tf_slot_cache *c) { return c ? c->bytes_filled : -1; }
+
+tf_status tf_slot_cache_set_policy(tf_slot_cache *c, int32_t policy) {
+    if (!c) return fail(TF_E_ARG, "NULL cache");
+    if (policy != TF_SLOT_LFU && policy != TF_SLOT_LRU) return fail(TF_E_ARG, "unknown policy %d", policy);
+    c->d.policy = policy;
+    return TF_OK;
+}
 
 }  // extern "C"

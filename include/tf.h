@@ -246,6 +246,16 @@ tf_status tf_slot_cache_reset(tf_slot_cache *c);
 /* Total bytes copied host->device by fills since create/reset. */
 int64_t tf_slot_cache_bytes_filled(const tf_slot_cache *c);
 
+/* Eviction rule of later lookups (every layer).  TF_SLOT_LFU (the default,
+ * the pages' word): victim = unpinned slot with the smallest (count,
+ * last-use token, slot index).  TF_SLOT_LRU (the sh.edu-sjtu.cn article's
+ * gloss of the same cache, "三件事": the longest-unused slot goes): victim =
+ * unpinned slot with the smallest (last-use token, slot index).  Hits, pins
+ * and empty slots work the same in both.  Meant to be set right after create
+ * or reset; TF_E_ARG for an unknown policy. */
+typedef enum { TF_SLOT_LFU = 0, TF_SLOT_LRU = 1 } tf_slot_policy;
+tf_status tf_slot_cache_set_policy(tf_slot_cache *c, int32_t policy);
+
 #ifdef __cplusplus
 }
 #endif

@@ -291,12 +291,18 @@ def np_moe_token(layer, x16, forced=None, tanh=False):
 # --------------------------------------------------------------------------
 # Integer oracles
 # --------------------------------------------------------------------------
-def lfu_replay(ids, n_slots, n_experts=None):
-    """Replay the per-layer LFU slot cache on a stream of token id rows.
+def lfu_replay(ids, n_slots, n_experts=None, policy="lfu"):
+    """Replay the per-layer slot cache on a stream of token id rows.
 
     ``ids``: int ``[T][k]`` in rank order.  Returns (hit bool [T][k],
     slot int16 [T][k], final expert_of_slot int [S], final count [S]).
+    ``policy``: "lfu" (the pages' word; victim = least (count, last use,
+    slot)) or "lru" (the sh.edu-sjtu.cn article's gloss of it, "三件事":
+    the longest-unused slot goes; victim = least (last use, slot)).  Both
+    pin the token's own hits and fill the lowest empty slot first.
     """
+    if policy not in ("lfu", "lru"):
+        raise ValueError("policy must be 'lfu' or 'lru'")
     ids = np.asarray(ids)
     T, k = ids.shape
     S = n_slots
@@ -328,7 +334,10 @@ def lfu_replay(ids, n_slots, n_experts=None):
             if empty:
                 v = empty[0]
             else:
-                v = min((count[s], last[s], s) for s in range(S) if s not in pinned)[2]
+                if policy == "lfu":
+                    v = min((count[s], last[s], s) for s in range(S) if s not in pinned)[2]
+                else:
+                    v = min((last[s], s) for s in range(S) if s not in pinned)[1]
                 del slot_of[expert_of[v]]
             expert_of[v] = e
             count[v] = 1

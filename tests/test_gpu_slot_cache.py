@@ -46,12 +46,12 @@ def _stack(api, seed, L, d, E, k, f, fs):
     return stride, host, layers, dls
 
 
-def _run(api, seed, L, d, E, k, f, fs, S, T, check_tokens):
+def _run(api, seed, L, d, E, k, f, fs, S, T, check_tokens, policy="lfu"):
     stride, host, layers, dls = _stack(api, seed, L, d, E, k, f, fs)
     ids = np.stack([gen.zipf_ids(seed, l, T, E, k) for l in range(L)])      # [L][T][k]
     x = gen.tokens(seed, T, d)
     slot_pool = torch.empty(L * S * stride, dtype=torch.uint8, device="cuda")
-    cache = api.SlotCache(L, E, S, k, stride, slot_pool, host, trace_cap=T)
+    cache = api.SlotCache(L, E, S, k, stride, slot_pool, host, trace_cap=T, policy=policy)
     copy = torch.cuda.Stream()
     xt = torch.from_numpy(x.view(np.int16)).cuda()
     ft = torch.from_numpy(ids).cuda()
@@ -77,7 +77,7 @@ def _run(api, seed, L, d, E, k, f, fs, S, T, check_tokens):
     misses = 0
     for l in range(L):
         hit, slot = cache.trace(l, T * k)
-        h_ref, s_ref, _, _ = oracle.lfu_replay(ids[l], S, E)
+        h_ref, s_ref, _, _ = oracle.lfu_replay(ids[l], S, E, policy=policy)
         assert np.array_equal(hit.reshape(T, k), h_ref), f"layer {l}: hit sequence"
         assert np.array_equal(slot.reshape(T, k), s_ref), f"layer {l}: slot sequence"
         misses += int((~h_ref).sum())
@@ -95,7 +95,7 @@ def _run(api, seed, L, d, E, k, f, fs, S, T, check_tokens):
                              layer_idx=0, ws=ws, copy_stream=copy)
     torch.cuda.synchronize()
     hit, slot = cache.trace(0, T * k)
-    h_ref, s_ref, _, _ = oracle.lfu_replay(ids[0][:min(T, 8)], S, E)
+    h_ref, s_ref, _, _ = oracle.lfu_replay(ids[0][:min(T, 8)], S, E, policy=policy)
     assert np.array_equal(hit.reshape(-1, k), h_ref) and np.array_equal(slot.reshape(-1, k), s_ref)
     assert torch.equal(y_c[0, :min(T, 8)].view(torch.int16), y_r[0, :min(T, 8)].view(torch.int16))
     cache.close()
@@ -120,3 +120,13 @@ def test_slot_cache_full_width(tfa):
     miss = _run(tfa, 2, L=2, d=2816, E=128, k=8, f=704, fs=2816, S=16, T=48,
                 check_tokens=[0, 47])
     assert 0.2 < miss < 0.9
+
+
+@pytest.mark.parametrize("S,policy", [(8, "lru"), (4, "lfu"), (4, "lru"), (16, "lru")])
+def test_slot_cache_policies_and_sizes(tfa, S, policy):
+    """The LRU reading and other slot counts: hit/slot sequences equal the
+    oracle's replay of the same rule, cached outputs equal resident ones."""
+    print(f"slot cache: {policy} S={S} d=256 E=32 k=4 L=2 T=64", flush=True)
+    miss = _run(tfa, 5, L=2, d=256, E=32, k=4, f=128, fs=256, S=S, T=64, check_tokens=[0, 63],
+                policy=policy)
+    assert 0.0 < miss < 1.0

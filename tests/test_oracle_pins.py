@@ -296,11 +296,38 @@ def test_lfu_zipf_hit_rate_in_stated_band():
     assert all(0.45 < r < 0.75 for r in rates), rates
 
 
+def test_lru_hand_derived_sequences():
+    """The LRU reading (longest-unused slot goes): hand-derived sequences,
+    most of them where LFU decides differently."""
+    cases = json.load(open(os.path.join(GOLD, "lru_cases.json")))["cases"]
+    for c in cases:
+        hit, slot, _, _ = oracle.lfu_replay(np.array(c["ids"]), c["n_slots"], policy="lru")
+        assert hit.tolist() == c["hit"], c["name"]
+        assert slot.tolist() == c["slot"], c["name"]
+    lfu = [oracle.lfu_replay(np.array(c["ids"]), c["n_slots"])[:2] for c in cases[:2]]
+    assert any(h.tolist() != c["hit"] or s.tolist() != c["slot"] for (h, s), c in zip(lfu, cases[:2]))
+
+
+def test_lru_uniform_thrash_rate_and_zipf_band():
+    """Uniform routing: 16 of 128 slots hit about 16/128 of the time under
+    either rule; Zipf(1.1) popularity favours the count-keeping LFU."""
+    ids = gen.uniform_ids(gen.WORKLOADS[4].seed, 0, 2000, 128, 8)
+    hit, _, _, _ = oracle.lfu_replay(ids, 16, policy="lru")
+    assert abs(hit.mean() - 16 / 128) < 0.02
+    wl = gen.WORKLOADS[2]
+    z = gen.zipf_ids(wl.seed, 0, 1024, 128, 8, s=wl.zipf_s)
+    lru = oracle.lfu_replay(z, 16, policy="lru")[0].mean()
+    lfu = oracle.lfu_replay(z, 16)[0].mean()
+    assert 0.3 < lru < lfu
+
+
 def test_lfu_rejects_small_cache_and_repeats():
     with pytest.raises(ValueError):
         oracle.lfu_replay(np.array([[0, 1, 2]]), 2)
     with pytest.raises(ValueError):
         oracle.lfu_replay(np.array([[4, 4]]), 4)
+    with pytest.raises(ValueError):
+        oracle.lfu_replay(np.array([[0, 1]]), 4, policy="fifo")
 
 
 # ----------------------------------------------------- grouping by expert

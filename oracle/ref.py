@@ -17,6 +17,14 @@ Plus two integer oracles written as plain Python loops:
   in rank order; the victim is the lowest empty slot, else the unpinned slot
   with the smallest (count, last-use token, slot index); every layer starts
   empty.
+* ``sample``: the next-token choice after the stack.  The pages give the
+  knobs and their defaults (shilu.ai README translation, "向模型输入
+  prompt": temperature 0.2, Top-K 64, Top-P 0.95, temperature 0 for greedy
+  output); the order of the steps is a reading: the K largest logits (ties
+  to the lower id), their softmax at the temperature, the shortest rank
+  prefix whose cumulative probability reaches P, then the first kept rank
+  whose cumulative probability exceeds u times the kept total, u in [0, 1)
+  given by the caller.  Every sum runs sequentially in rank order.
 * ``group_by_expert``: (token, rank) pairs of a prefill chunk sorted by
   (expert, token, rank) -- the grouping that lets one fetched expert serve
   several rows (shilu.ai, "推理引擎的工作原理": prefill in chunks of at
@@ -56,7 +64,7 @@ __all__ = [
     "softmax", "expert_ffn", "expert_from_blob", "moe_token", "moe_tokens",
     "np_dequant", "np_qmatvec", "np_gelu", "np_topk", "np_softmax",
     "np_expert", "np_moe_token", "lfu_replay", "group_by_expert", "to_fp16",
-    "num_threads",
+    "num_threads", "sample",
 ]
 
 
@@ -346,6 +354,41 @@ def lfu_replay(ids, n_slots, n_experts=None, policy="lfu"):
             pinned.add(v)
             slot[t, r] = v
     return hit, slot, np.array(expert_of), np.array(count)
+
+
+def sample(logits, temperature, top_k, top_p, u):
+    """Next-token id from one row of logits (see the module docstring).
+
+    ``logits``: fp32 or fp64 ``[V]`` (NaN ranks last); ``temperature`` 0 gives
+    the greedy choice (largest logit, lowest id on ties); ``u`` in [0, 1).
+    """
+    l = np.asarray(logits, dtype=np.float64).copy()
+    l[np.isnan(l)] = -np.inf
+    V = l.size
+    if not 1 <= top_k <= V:
+        raise ValueError("need 1 <= top_k <= V")
+    order = np.lexsort((np.arange(V), -l))          # logit desc, id asc
+    if temperature == 0:
+        return int(order[0])
+    sel = order[:top_k]
+    w = [float(np.exp((l[i] - l[sel[0]]) / temperature)) for i in sel]
+    s = 0.0
+    for x in w:
+        s += x
+    cum, c = [], 0.0
+    for x in w:
+        c += x / s
+        cum.append(c)
+    keep = top_k
+    for n, c in enumerate(cum):
+        if c >= top_p:
+            keep = n + 1
+            break
+    target = u * cum[keep - 1]
+    for n in range(keep):
+        if cum[n] > target:
+            return int(sel[n])
+    return int(sel[keep - 1])
 
 
 def group_by_expert(ids, n_experts):

@@ -368,3 +368,48 @@ def test_blob_sections_round_trip():
                           ex["up"]["q"].reshape(-1))
     x = gen.tokens(0, 1, 256)[0].astype(np.float64)
     assert np.array_equal(oracle.expert_from_blob(blob, 256, 128, x), oracle.expert_ffn(ex, x))
+
+
+# ------------------------------------------------------------ sampling step
+def test_sample_hand_worked_cases():
+    cases = json.load(open(os.path.join(GOLD, "sample_cases.json")))["cases"]
+    for c in cases:
+        logits = np.array(c["logits"], dtype=np.float64)
+        k = min(c["top_k"], logits.size)
+        got = [oracle.sample(logits, c["temperature"], k, c["top_p"], u) for u in c["u"]]
+        assert got == c["ids"], c["name"]
+
+
+def test_sample_greedy_and_degenerate_knobs_are_argmax():
+    rng = np.random.default_rng(7)
+    for trial in range(50):
+        l = rng.standard_normal(1000).astype(np.float32)
+        if trial % 5 == 0:                     # a tie at the top
+            j = int(np.argmax(l))
+            l[rng.integers(0, 1000)] = l[j]
+        best = int(np.argmax(l))               # first maximum = lowest id
+        u = float(rng.random())
+        assert oracle.sample(l, 0.0, 64, 0.95, u) == best
+        assert oracle.sample(l, 0.7, 1, 0.95, u) == best
+        assert oracle.sample(l, 0.7, 64, 1e-9, u) == best
+
+
+def test_sample_frequencies_match_the_nucleus():
+    """Sweeping u over a uniform grid draws each kept id in proportion to its
+    renormalised probability; ids outside the nucleus never appear."""
+    rng = np.random.default_rng(3)
+    l = rng.standard_normal(300) * 2
+    T, K, P = 0.8, 16, 0.9
+    order = np.lexsort((np.arange(l.size), -l))[:K]
+    w = np.exp((l[order] - l[order[0]]) / T)
+    p = w / w.sum()
+    keep = int(np.searchsorted(np.cumsum(p), P) + 1)
+    q = p[:keep] / p[:keep].sum()
+    N = 20000
+    ids = [oracle.sample(l, T, K, P, (i + 0.5) / N) for i in range(N)]
+    cnt = {int(i): 0 for i in order}
+    for i in ids:
+        cnt[i] += 1
+    for r, i in enumerate(order):
+        want = q[r] if r < keep else 0.0
+        assert abs(cnt[int(i)] / N - want) <= 1.0 / N + 1e-12, (r, cnt[int(i)], want)

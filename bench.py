@@ -550,6 +550,60 @@ def run_slot(args):
     return out
 
 
+def run_sample(args):
+    """Next-token sampling over 262,144-id logits at the default knobs
+    (temperature 0.2, top-k 64, top-p 0.95), batch 1 and 16."""
+    import torch
+
+    from bit_routed_expert_tf_amd import _lib, api
+    from synth import gen
+    lib = _lib.load()
+    dev = torch.device("cuda:0")
+    V, K, TEMP, TOP_P = gen.VOCAB, 64, 0.2, 0.95
+    stream = torch.cuda.Stream(device=dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    out = {"metric": "sampled tokens/s (262,144-id logits, top-k 64, top-p 0.95, T 0.2)",
+           "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True,
+           "data": "synthetic (seeded)", "dtype": "fp32 keys, fp64 softmax",
+           "config": {"workload": "sample-v262144-k64", "vocab": V, "top_k": K,
+                      "temperature": TEMP, "top_p": TOP_P}, "batches": {}}
+    for T in (1, 16):
+        nrow = 64   # distinct logit rows cycled through
+        l, u = gen.sample_inputs(11, nrow * T, V, "lm")
+        L = torch.from_numpy(l).to(dev)
+        U = torch.from_numpy(u).to(dev)
+        ids = torch.empty(nrow * T, dtype=torch.int32, device=dev)
+        ws = api.workspace(api.tf_sample_workspace_bytes(V, T, K), dev)
+
+        def step(i):
+            j = i % nrow
+            _lib.check(lib.tf_sample(ctypes.c_void_p(L.data_ptr() + 4 * V * T * j), V, T, TEMP, K,
+                                     TOP_P, ctypes.c_void_p(U.data_ptr() + 8 * T * j),
+                                     ctypes.c_void_p(ids.data_ptr() + 4 * T * j),
+                                     ctypes.c_void_p(ws.data_ptr()), ws.numel(), sh))
+
+        with torch.cuda.stream(stream):
+            step(0)
+        torch.cuda.synchronize()
+        n = args.steps or 2000
+        graphs = _graphs(step, nrow, nrow, stream)
+        steps, ms = _timed(graphs, n, min(args.warmup, n), stream)
+        kern = _profile(lib, _hip(), {_lib.TF_KERNEL_SAMPLE_PART: "k_sample_part",
+                                      _lib.TF_KERNEL_SAMPLE_FINAL: "k_sample_final"}, step,
+                        min(args.prof_steps, 200), stream)
+        us = ms * 1e3 / steps
+        kus = kern["k_sample_part"]["avg_us"]
+        nbytes = 4 * V * T   # the logits, read once by the slice kernel
+        out["batches"][str(T)] = {
+            "us_per_call": round(us, 3), "tokens_per_s": round(T * steps / (ms / 1e3), 1),
+            "kernels": kern,
+            "roofline": {"bound": "hbm", "achieved": round(nbytes / (kus * 1e-6) / 1e9, 1),
+                         "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(nbytes / (kus * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}}
+    out["value"] = out["batches"]["16"]["tokens_per_s"]
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -563,10 +617,11 @@ def main():
                     help="first run plain 256 MiB device copies (memory-counter calibration)")
     ap.add_argument("--slot-sweep", action="store_true",
                     help="slot-cache workload: also run 8, 16 and 32 slots under LFU and LRU")
-    ap.add_argument("--workload", choices=["decode", "prefill", "stack", "slot-cache"],
+    ap.add_argument("--workload", choices=["decode", "prefill", "stack", "slot-cache", "sample"],
                     default="decode",
                     help="decode (default, the headline line); the others measure the "
-                         "prefill chunk, the 30-layer resident stack and the slot-cache stack")
+                         "prefill chunk, the 30-layer resident stack, the slot-cache stack "
+                         "and next-token sampling")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this hot path is built and measured on a single "
@@ -580,7 +635,8 @@ def main():
     else:
         if "--steps" not in sys.argv:
             args.steps = 0   # the workload's own count
-        out = {"prefill": run_prefill, "stack": run_stack, "slot-cache": run_slot}[args.workload](args)
+        out = {"prefill": run_prefill, "stack": run_stack, "slot-cache": run_slot,
+               "sample": run_sample}[args.workload](args)
     print(json.dumps(out), flush=True)
 
 

@@ -22,6 +22,7 @@ TF_FLAG_ID_RANGE, TF_FLAG_ID_REPEAT = 1, 2
 TF_KERNEL_ROUTER_SHARED_GATEUP, TF_KERNEL_ROUTED_GATEUP_SHARED_DOWN, TF_KERNEL_DOWN_COMBINE = 1, 2, 4
 TF_KERNEL_PREFILL_DOWN, TF_KERNEL_PREFILL_COMBINE = 8, 16
 TF_KERNEL_PREFILL_GATEUP, TF_KERNEL_GROUP = 32, 64
+TF_KERNEL_SAMPLE_PART, TF_KERNEL_SAMPLE_FINAL = 128, 256
 TF_SLOT_LFU, TF_SLOT_LRU = 0, 1
 
 c_void_p, c_int32, c_int64, c_size_t = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -72,6 +73,9 @@ _SIGS = {
     "tf_moe_prefill_chunk": (c_int32, [ctypes.POINTER(tf_moe_layer), c_void_p, c_int32,
                                        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                        c_void_p, c_size_t]),
+    "tf_sample_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
+    "tf_sample": (c_int32, [c_void_p, c_int32, c_int32, ctypes.c_float, c_int32, ctypes.c_float,
+                            c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "tf_profile_kernel": (c_int32, [c_int32, c_void_p, c_void_p]),
     "tf_slot_cache_create": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_size_t, c_void_p,
                                        c_void_p, c_int64, ctypes.POINTER(c_void_p)]),

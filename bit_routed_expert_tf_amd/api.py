@@ -18,7 +18,8 @@ __all__ = [
     "DeviceLayer", "workspace", "tf_expert_blob_bytes", "tf_moe_workspace_bytes",
     "tf_moe_layer_fwd", "tf_router_workspace_bytes", "tf_router_topk",
     "tf_gemv_workspace_bytes", "tf_expert_q4_gemv", "tf_prefill_workspace_bytes",
-    "tf_moe_prefill_chunk", "tf_group_workspace_bytes", "tf_group_by_expert", "tf_workspace_flags", "tf_workspace_zero", "SlotCache",
+    "tf_moe_prefill_chunk", "tf_group_workspace_bytes", "tf_group_by_expert", "tf_sample_workspace_bytes", "tf_sample",
+    "tf_workspace_flags", "tf_workspace_zero", "SlotCache",
     "pinned_host", "stream_handle",
 ]
 
@@ -211,6 +212,25 @@ def tf_group_by_expert(ids, n_experts, counts=None, offsets=None, pairs=None, ws
     check(load().tf_group_by_expert(_p(ids), T, k, n_experts, _p(counts), _p(offsets), _p(pairs),
                                     _p(ws), ws.numel(), stream_handle(stream)))
     return counts, offsets, pairs
+
+
+def tf_sample_workspace_bytes(V, T, top_k):
+    return int(load().tf_sample_workspace_bytes(V, T, top_k))
+
+
+def tf_sample(logits, temperature, top_k, top_p, u=None, ids=None, ws=None, stream=None):
+    """ids [T] int32 from logits [T][V] fp32 (u [T] fp64, NULL only when
+    temperature is 0)."""
+    T, V = logits.shape
+    dev = logits.device
+    if ids is None:
+        ids = torch.empty(T, dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = workspace(tf_sample_workspace_bytes(V, T, top_k), dev)
+    check(load().tf_sample(_p(logits), V, T, float(temperature), top_k, float(top_p),
+                           _p(u), _p(ids), _p(ws), ws.numel(),
+                           stream_handle(stream)))
+    return ids
 
 
 def tf_workspace_zero(ws, stream=None):

@@ -191,6 +191,31 @@ tf_status tf_group_by_expert(const int32_t *ids, int32_t T, int32_t top_k, int32
                              int32_t *counts, int32_t *offsets, int32_t *pairs, void *ws,
                              size_t ws_bytes, hipStream_t s);
 
+/* ------------------------------------------------------------ sampling */
+/* Next-token ids from rows of logits (shilu.ai README translation,
+ * "向模型输入 prompt": the temperature, Top-K and Top-P knobs; temperature 0
+ * gives greedy output).  Per row t:
+ *   1. the top_k largest logits, ties to the lower id, NaN ranked as -inf;
+ *   2. their softmax at `temperature`, in fp64, every sum taken
+ *      sequentially in rank order;
+ *   3. keep the shortest rank prefix whose cumulative probability is >= top_p;
+ *   4. ids[t] = the first kept rank whose cumulative probability exceeds
+ *      u[t] * (the kept cumulative probability).
+ * temperature == 0: ids[t] = the largest logit's id (u may be NULL).
+ *   logits [T][V] fp32 device, rows contiguous, 4-B aligned.
+ *   u      [T] fp64 device, each in [0, 1) (the caller's random draws).
+ *   ids    [T] int32 device out.
+ *   ws     tf_sample_workspace_bytes(V, T, top_k) bytes, 256-B aligned: 64
+ *          keys per 4096-logit slice of every row (512 * T * ceil(V / 4096)
+ *          bytes).  Calls that share a workspace must not overlap.
+ * 1 <= top_k <= 64, top_k <= V <= 262144 (TF_E_SHAPE); 0 <= T <= 4096,
+ * temperature >= 0, 0 < top_p <= 1 (TF_E_ARG).  T == 0 returns TF_OK with no
+ * launch.  Two launches, stream-ordered. */
+size_t tf_sample_workspace_bytes(int32_t V, int32_t T, int32_t top_k);
+tf_status tf_sample(const float *logits, int32_t V, int32_t T, float temperature, int32_t top_k,
+                    float top_p, const double *u, int32_t *ids, void *ws, size_t ws_bytes,
+                    hipStream_t s);
+
 /* ------------------------------------------------------------ profiling */
 /* Kernel ids of the hot path (for tf_profile_kernel). */
 enum {
@@ -200,7 +225,9 @@ enum {
     TF_KERNEL_PREFILL_DOWN = 8,              /* prefill: shared and per-item down (MFMA)  */
     TF_KERNEL_PREFILL_COMBINE = 16,          /* prefill: y_s + sum of y_e -> y            */
     TF_KERNEL_PREFILL_GATEUP = 32,           /* prefill: shared and per-item gate/up (MFMA) */
-    TF_KERNEL_GROUP = 64                     /* tf_group_by_expert                        */
+    TF_KERNEL_GROUP = 64,                    /* tf_group_by_expert                        */
+    TF_KERNEL_SAMPLE_PART = 128,             /* tf_sample: per-slice 64 largest keys      */
+    TF_KERNEL_SAMPLE_FINAL = 256             /* tf_sample: row merge, softmax, draw       */
 };
 /* Arm a one-shot timer: the next launch, by this host thread, of the named
  * kernel goes through hipExtLaunchKernel with `start` recorded when the

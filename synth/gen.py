@@ -229,3 +229,42 @@ def uniform_ids(seed, layer, n_tokens, n_experts, top_k):
     rng = _rng(seed, IDS_STREAM, layer)
     keys = rng.random((n_tokens, n_experts))
     return np.argsort(keys, axis=1, kind="stable")[:, :top_k].astype(np.int32)
+
+
+SAMPLE_STREAM = 9100
+VOCAB = 262144   # the vocabulary size taken for the sampling step (2**18)
+
+
+def sample_inputs(seed, n_rows, vocab=VOCAB, pattern="lm"):
+    """Logits ``fp32 [n_rows][vocab]`` and draws ``u fp64 [n_rows]`` in [0, 1).
+
+    ``pattern``:
+      * ``"lm"``: N(0, 2) per logit plus a head of 32 ids per row lifted by
+        Exp(mean 6), so the top 64 hold most of the mass at temperature 1;
+      * ``"ties"``: integers 0..7 (many equal logits);
+      * ``"sorted"``: the "lm" row sorted ascending (the largest logits last);
+      * ``"special"``: the "lm" row with NaN, -inf, +-0 and a row maximum
+        repeated at several ids.
+    """
+    rng = _rng(seed, SAMPLE_STREAM, n_rows, vocab)
+    if pattern == "ties":
+        l = rng.integers(0, 8, size=(n_rows, vocab)).astype(np.float32)
+    else:
+        l = rng.normal(0.0, 2.0, size=(n_rows, vocab))
+        for r in range(n_rows):
+            head = rng.choice(vocab, size=min(32, vocab), replace=False)
+            l[r, head] += rng.exponential(6.0, size=head.size)
+        l = l.astype(np.float32)
+        if pattern == "sorted":
+            l.sort(axis=1)
+        elif pattern == "special":
+            for r in range(n_rows):
+                pos = rng.choice(vocab, size=min(24, vocab), replace=False)
+                top = l[r].max()
+                l[r, pos[:6]] = np.nan
+                l[r, pos[6:12]] = -np.inf
+                l[r, pos[12:15]] = 0.0
+                l[r, pos[15:18]] = -0.0
+                l[r, pos[18:]] = top
+    u = rng.random(n_rows)
+    return l, u

@@ -138,3 +138,28 @@ def test_group_argument_errors():
     assert g(p, 4, 8, 128, p, p, p, ctypes.c_void_p((1 << 28) + 4), 1 << 30, None) == _lib.TF_E_ALIGN
     assert g(p, 128, 8, 128, p, p, p, ws, need - 1, None) == _lib.TF_E_NOMEM
     assert b"workspace" in lib.tf_last_error()
+
+
+def test_sample_argument_errors():
+    lib = tfa.load()
+    p = ctypes.c_void_p(1 << 20)
+    ws = ctypes.c_void_p(1 << 28)
+    f = lib.tf_sample
+    need = lib.tf_sample_workspace_bytes(262144, 16, 64)
+    assert need == 16 * 64 * 64 * 8 == lib.tf_sample_workspace_bytes(262144, 16, 1)
+    assert f(p, 262144, 0, 0.7, 64, 0.95, p, p, ws, need, None) == 0                 # T=0
+    assert f(p, 262144, 4097, 0.7, 64, 0.95, p, p, ws, 1 << 30, None) == _lib.TF_E_ARG
+    assert f(p, 262145, 1, 0.7, 64, 0.95, p, p, ws, 1 << 30, None) == _lib.TF_E_SHAPE  # V > 2**18
+    assert f(p, 262145, 1, 0.7, 8, 0.95, p, p, ws, 1 << 30, None) == _lib.TF_E_SHAPE
+    assert f(p, 100, 1, 0.7, 65, 0.95, p, p, ws, 1 << 30, None) == _lib.TF_E_SHAPE    # k > 64
+    assert f(p, 100, 1, 0.7, 0, 0.95, p, p, ws, 1 << 30, None) == _lib.TF_E_SHAPE     # k = 0
+    assert f(p, 7, 1, 0.7, 8, 0.95, p, p, ws, 1 << 30, None) == _lib.TF_E_SHAPE       # V < k
+    assert f(p, 100, 1, -0.5, 8, 0.95, p, p, ws, 1 << 30, None) == _lib.TF_E_ARG
+    assert f(p, 100, 1, 0.7, 8, 0.0, p, p, ws, 1 << 30, None) == _lib.TF_E_ARG
+    assert f(p, 100, 1, 0.7, 8, 1.5, p, p, ws, 1 << 30, None) == _lib.TF_E_ARG
+    assert f(p, 100, 1, 0.7, 8, 0.95, None, p, ws, 1 << 30, None) == _lib.TF_E_ARG     # u NULL
+    assert f(None, 100, 1, 0.7, 8, 0.95, p, p, ws, 1 << 30, None) == _lib.TF_E_ARG
+    assert f(ctypes.c_void_p((1 << 20) + 2), 100, 1, 0.7, 8, 0.95, p, p, ws, 1 << 30,
+             None) == _lib.TF_E_ALIGN
+    assert f(p, 262144, 16, 0.7, 64, 0.95, p, p, ws, need - 1, None) == _lib.TF_E_NOMEM
+    assert b"workspace" in lib.tf_last_error()

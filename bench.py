@@ -514,29 +514,56 @@ def run_slot(args):
     peak = 4 * (256 << 20) / (time.perf_counter() - c0) / 1e9
     del big
 
-    def one(n_slots, policy):
-        """One pass of the token stream through the stack with this cache."""
+    Fh = F.cpu().numpy()
+    prng = np.random.default_rng([wl.seed, 9200])
+    # predicted ids of (layer, token): exact, or with half of them replaced
+    pred = {"exact": Fh, "noisy": Fh.copy()}
+    for l in range(L):
+        for t in range(ntok):
+            j = prng.choice(k, size=k // 2, replace=False)
+            pred["noisy"][l, t, j] = prng.integers(0, E, size=j.size)
+
+    def one(n_slots, policy, prefetch=None, engine="kernel"):
+        """One pass of the token stream through the stack with this cache;
+        with `prefetch`, the next layer's predicted experts are copied ahead."""
         slot_pool = torch.empty(L * n_slots * stride, dtype=torch.uint8, device=dev)
         cache = api.SlotCache(L, E, n_slots, k, stride, slot_pool, host, trace_cap=ntok,
                               policy=policy)
+        cache.set_copy_engine(engine)
+        if prefetch:
+            pf_buf = torch.empty(L * k * stride, dtype=torch.uint8, device=dev)
+            cache.set_prefetch(pf_buf, k)
+            P = pred[prefetch]
         torch.cuda.synchronize()
         w0 = time.perf_counter()
+        if prefetch:
+            cache.prefetch(0, P[0, 0], copy)
         for t in range(ntok):
             for l in range(L):
                 api.tf_moe_layer_fwd(layers[l], X[t:t + 1], forced_ids=F[l, t:t + 1],
                                      y=Y[l, t:t + 1], cache=cache, layer_idx=l, ws=ws,
                                      copy_stream=copy)
+                nl, nt = (l + 1, t) if l + 1 < L else (0, t + 1)
+                if prefetch and nt < ntok:
+                    cache.prefetch(nl, P[nl, nt], copy)
             if t % 256 == 255:
-                print(f"slot: {policy} {n_slots} slots, token {t + 1}", file=sys.stderr, flush=True)
+                print(f"slot: {policy} {n_slots} slots {prefetch or ''}, token {t + 1}",
+                      file=sys.stderr, flush=True)
         torch.cuda.synchronize()
         wall = time.perf_counter() - w0
         hits = sum(int(cache.trace(l, ntok * k)[0].sum()) for l in range(L))
         filled = cache.bytes_filled()
+        pf_bytes, used, wasted = cache.prefetch_stats() if prefetch else (0, 0, 0)
         cache.close()
         del slot_pool
-        return {"slots": n_slots, "policy": policy, "value": round(ntok / wall, 2),
-                "hit_rate": round(hits / (L * ntok * k), 4), "h2d_bytes": filled,
-                "h2d_GBps": round(filled / wall / 1e9, 2), "wall_s": round(wall, 2)}
+        r = {"slots": n_slots, "policy": policy, "engine": engine, "value": round(ntok / wall, 2),
+             "hit_rate": round(hits / (L * ntok * k), 4), "h2d_bytes": filled + pf_bytes,
+             "h2d_GBps": round((filled + pf_bytes) / wall / 1e9, 2), "wall_s": round(wall, 2)}
+        if prefetch:
+            r.update({"prefetch": prefetch, "prefetch_h2d_bytes": pf_bytes,
+                      "prefetch_used": used, "prefetch_unused": wasted,
+                      "fill_h2d_bytes": filled})
+        return r
 
     base = one(S, "lfu")
     out = {"metric": "slot-cache stack decode tokens/s (30 layers, 16 slots, PCIe misses)",
@@ -544,6 +571,9 @@ def run_slot(args):
            "hit_rate": base["hit_rate"], "h2d_bytes": base["h2d_bytes"],
            "h2d_GBps": base["h2d_GBps"], "pinned_h2d_peak_GBps": round(peak, 2),
            "setup_s": round(setup, 1), "wall_s": base["wall_s"]}
+    if args.prefetch:     # speculative fill of the next layer's predicted experts
+        out["prefetch"] = [one(S, "lfu", "exact"), one(S, "lfu", "noisy"),
+                           one(S, "lfu", None, "dma"), one(S, "lfu", "exact", "dma")]
     if args.slot_sweep:   # slot counts x policies (the LFU reading and the LRU gloss)
         out["sweep"] = [one(n, pol) for n in (8, 16, 32) for pol in ("lfu", "lru")
                         if not (n == S and pol == "lfu")] + [dict(base)]
@@ -615,6 +645,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run plain 256 MiB device copies (memory-counter calibration)")
+    ap.add_argument("--prefetch", action="store_true",
+                    help="slot-cache workload: also run with the next layer's experts "
+                         "prefetched (exact predictions, and half of them wrong)")
     ap.add_argument("--slot-sweep", action="store_true",
                     help="slot-cache workload: also run 8, 16 and 32 slots under LFU and LRU")
     ap.add_argument("--workload", choices=["decode", "prefill", "stack", "slot-cache", "sample"],

@@ -24,6 +24,7 @@ TF_KERNEL_PREFILL_DOWN, TF_KERNEL_PREFILL_COMBINE = 8, 16
 TF_KERNEL_PREFILL_GATEUP, TF_KERNEL_GROUP = 32, 64
 TF_KERNEL_SAMPLE_PART, TF_KERNEL_SAMPLE_FINAL = 128, 256
 TF_SLOT_LFU, TF_SLOT_LRU = 0, 1
+TF_SLOT_COPY_DMA, TF_SLOT_COPY_KERNEL = 0, 1
 
 c_void_p, c_int32, c_int64, c_size_t = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 
@@ -88,6 +89,12 @@ _SIGS = {
     "tf_slot_cache_reset": (c_int32, [c_void_p]),
     "tf_slot_cache_bytes_filled": (c_int64, [c_void_p]),
     "tf_slot_cache_set_policy": (c_int32, [c_void_p, c_int32]),
+    "tf_slot_cache_set_prefetch": (c_int32, [c_void_p, c_void_p, c_int32]),
+    "tf_slot_cache_set_copy_engine": (c_int32, [c_void_p, c_int32]),
+    "tf_slot_cache_prefetch": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_void_p,
+                                         ctypes.POINTER(c_int32)]),
+    "tf_slot_cache_prefetch_stats": (c_int32, [c_void_p, ctypes.POINTER(c_int64),
+                                               ctypes.POINTER(c_int64), ctypes.POINTER(c_int64)]),
 }
 
 _lib = None

@@ -299,3 +299,32 @@ class SlotCache:
     def bytes_filled(self):
         return int(load().tf_slot_cache_bytes_filled(self.handle))
 
+
+    def set_copy_engine(self, engine):
+        """"kernel" (one launch per fill or prefetch reading the mapped host
+        pool, the default) or "dma" (one hipMemcpyAsync per blob)."""
+        code = {"dma": _lib.TF_SLOT_COPY_DMA, "kernel": _lib.TF_SLOT_COPY_KERNEL}[engine]
+        check(load().tf_slot_cache_set_copy_engine(self.handle, code))
+
+    def set_prefetch(self, buffers, n_buffers):
+        """Speculative fill: ``buffers`` is a device uint8 tensor of
+        n_layers * n_buffers * blob_stride bytes (kept alive here); 0 turns it off."""
+        if n_buffers and buffers.numel() < self.n_layers * n_buffers * self.blob_stride:
+            raise ValueError("prefetch buffers too small")
+        self.pf_buffers = buffers if n_buffers else None
+        check(load().tf_slot_cache_set_prefetch(self.handle, _p(self.pf_buffers), n_buffers))
+
+    def prefetch(self, layer, ids, copy_stream=None):
+        """Copy the predicted experts of ``layer`` (host ints) that are not
+        resident into free buffers; returns the number of copies issued."""
+        a = np.ascontiguousarray(np.asarray(ids, dtype=np.int32).reshape(-1))
+        n = ctypes.c_int32(0)
+        check(load().tf_slot_cache_prefetch(self.handle, layer, ctypes.c_void_p(a.ctypes.data),
+                                            a.size, stream_handle(copy_stream), ctypes.byref(n)))
+        return n.value
+
+    def prefetch_stats(self):
+        """(host->device prefetch bytes, buffers used by fills, buffers unused)."""
+        v = [ctypes.c_int64(0) for _ in range(3)]
+        check(load().tf_slot_cache_prefetch_stats(self.handle, *[ctypes.byref(x) for x in v]))
+        return tuple(int(x.value) for x in v)

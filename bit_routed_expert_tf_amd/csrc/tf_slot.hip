@@ -7,9 +7,14 @@
 // (shilu.ai README translation, "推理引擎的工作原理"; sh.edu-sjtu.cn, "三件事").
 // Here the plan runs on the GPU right after the router (one wave, no host
 // round trip), the miss list lands in mapped pinned host memory, and the host
-// turns it into one hipMemcpyAsync per miss from a pinned host pool on a copy
-// stream; the shared-expert kernels are already queued on the compute stream
-// and run meanwhile.
+// turns it into one copy launch over all the misses (a kernel reading the
+// pinned host pool through its device mapping; or one hipMemcpyAsync per
+// miss) on a copy stream; the shared-expert kernels are already queued on
+// the compute stream and run meanwhile.  Optionally the host copies the
+// experts it predicts for a layer into per-layer buffers ahead of that
+// layer's lookup (speculative fill, after the pages' read-ahead); the fill
+// then takes each predicted miss from its buffer.  Predictions never change
+// the hit/miss sequence.
 //
 // Policy (reading of "LFU"): a slot's count is 1 on fill and +1 per hit; the
 // token's own ids are pinned; misses are taken in rank order; the victim is
@@ -53,6 +58,16 @@ struct tf_slot_cache {
     std::vector<int> pending;
     hipEvent_t ev_fill;
     int64_t bytes_filled;
+    // speculative fill (tf_slot_cache_prefetch)
+    uint8_t *pf_pool = nullptr;          // device [L][P][stride] (caller-owned)
+    int P = 0;                           // buffers per layer (0 = off)
+    std::vector<int16_t> mirror;         // [L][S] expert per slot as the fills left it
+    std::vector<int32_t> pf;             // [L][P] expert in each buffer (-1 free)
+    std::vector<hipEvent_t> ev_pf;       // [L] after the layer's latest prefetch copies
+    std::vector<hipEvent_t> ev_done;     // [L] after the layer's latest fill copies
+    int64_t pf_bytes = 0, pf_used = 0, pf_wasted = 0;
+    const uint8_t *host_dev = nullptr;   // device mapping of host_pool (NULL: DMA only)
+    int engine = TF_SLOT_COPY_KERNEL;   // DMA when the host pool has no mapping
 };
 
 namespace {
@@ -61,6 +76,35 @@ __global__ void k_fill16(int16_t *p, size_t n, int16_t v) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
          i += (size_t)gridDim.x * blockDim.x)
         p[i] = v;
+}
+
+// Blob copies by a kernel: blob blockIdx.y, the x workgroups of a blob
+// striding over it in 16-byte units, four loads in flight per thread.  The
+// sources are device blobs (prefetch buffers) or blobs of the pinned host
+// pool read over PCIe through its device mapping (the kernel copy engine):
+// one launch moves all of a call's blobs, where one DMA copy per 3.3 MB blob
+// pays a fixed cost each (39 GB/s for such copies back to back, against
+// 54-56 GB/s for large ones).  On an idle GPU four workgroups per host blob
+// already reach the PCIe rate; beside the decode kernels sixteen do (fewer
+// starve, more crowd the decode kernels).
+constexpr int MAX_COPIES = 32;
+struct BlobCopies {
+    const uint4 *src[MAX_COPIES];
+    uint4 *dst[MAX_COPIES];
+};
+__global__ __launch_bounds__(256) void k_copy_blobs(BlobCopies c, size_t n16) {
+    const uint4 *src = c.src[blockIdx.y];
+    uint4 *dst = c.dst[blockIdx.y];
+    const size_t step = (size_t)gridDim.x * 256;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += 4 * step) {
+        uint4 v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (i + j * step < n16) v[j] = src[i + j * step];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (i + j * step < n16) dst[i + j * step] = v[j];
+    }
 }
 
 // One token's lookup for one layer; a single lane walks the policy so that
@@ -186,7 +230,36 @@ static tf_status reset_tables(tf_slot_cache *c) {
     memset(c->miss_host, 0, sizeof(int32_t) * c->d.L * (1 + 2 * c->d.k));
     for (auto &p : c->pending) p = 0;
     c->bytes_filled = 0;
+    c->mirror.assign((size_t)c->d.L * c->d.S, -1);
+    c->pf.assign((size_t)c->d.L * c->P, -1);
+    c->pf_bytes = c->pf_used = c->pf_wasted = 0;
     return TF_OK;
+}
+
+// Host-pool blob (layer, expert) as seen by a kernel.
+static const uint4 *host_blob_dev(const tf_slot_cache *c, int layer, int ex) {
+    if (!c->host_dev) return nullptr;
+    return reinterpret_cast<const uint4 *>(c->host_dev + ((size_t)layer * c->d.E + ex) * c->stride);
+}
+
+// One k_copy_blobs launch for n blobs (n <= MAX_COPIES) with `per_blob`
+// workgroups each.
+static hipError_t launch_copies(const tf_slot_cache *c, const BlobCopies &bc, int n, int per_blob,
+                                hipStream_t s) {
+    if (!n) return hipSuccess;
+    hipLaunchKernelGGL(k_copy_blobs, dim3(per_blob, n), dim3(256), 0, s, bc, c->stride / 16);
+    return hipGetLastError();
+}
+constexpr int HOST_WGS_PER_BLOB = 16;   // PCIe reads: about 1 MB in flight per blob
+constexpr int DEV_WGS_PER_BLOB = 64;    // HBM copies
+
+// n host-to-device DMA copies of one blob each on `copy`.
+static hipError_t dma_copies(const tf_slot_cache *c, uint8_t *const *dst, const uint8_t *const *src,
+                             int n, hipStream_t copy) {
+    hipError_t e = hipSuccess;
+    for (int j = 0; j < n && e == hipSuccess; ++j)
+        e = hipMemcpyAsync(dst[j], src[j], c->stride, hipMemcpyHostToDevice, copy);
+    return e;
 }
 
 extern "C" {
@@ -238,11 +311,20 @@ tf_status tf_slot_cache_create(int32_t n_layers, int32_t n_experts, int32_t n_sl
         return fail(TF_E_NOMEM, "pinned miss list: %s", hipGetErrorString(e));
     }
     e = hipHostGetDevicePointer(reinterpret_cast<void **>(&c->d.miss_dev), c->miss_host, 0);
+    if (e == hipSuccess) {
+        void *hd = nullptr;   // kernels read the host pool through its mapping when it has one
+        if (hipHostGetDevicePointer(&hd, const_cast<uint8_t *>(host_pool_pinned), 0) == hipSuccess)
+            c->host_dev = static_cast<const uint8_t *>(hd);
+        else
+            (void)hipGetLastError();
+        if (!c->host_dev) c->engine = TF_SLOT_COPY_DMA;
+    }
     c->ev_lookup.assign(n_layers, nullptr);
     c->pending.assign(n_layers, 0);
     for (int l = 0; l < n_layers && e == hipSuccess; ++l)
         e = hipEventCreateWithFlags(&c->ev_lookup[l], hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_fill, hipEventDisableTiming);
+
     if (e != hipSuccess) {
         tf_slot_cache_destroy(c);
         return fail(TF_E_HIP, "slot cache events: %s", hipGetErrorString(e));
@@ -258,7 +340,12 @@ void tf_slot_cache_destroy(tf_slot_cache *c) {
     (void)hipDeviceSynchronize();
     for (auto ev : c->ev_lookup)
         if (ev) (void)hipEventDestroy(ev);
+    for (auto ev : c->ev_pf)
+        if (ev) (void)hipEventDestroy(ev);
+    for (auto ev : c->ev_done)
+        if (ev) (void)hipEventDestroy(ev);
     if (c->ev_fill) (void)hipEventDestroy(c->ev_fill);
+
     if (c->miss_host) (void)hipHostFree(c->miss_host);
     if (c->dev) (void)hipFree(c->dev);
     delete c;
@@ -290,17 +377,142 @@ tf_status tf_slot_cache_fill(tf_slot_cache *c, int32_t layer, hipStream_t copy, 
     const int32_t *m = c->miss_host + (size_t)layer * (1 + 2 * c->d.k);
     const int nm = m[0];
     if (nm < 0 || nm > c->d.k) return fail(TF_E_STATE, "corrupt miss list (%d)", nm);
+    int32_t *pf = c->P ? c->pf.data() + (size_t)layer * c->P : nullptr;
+    const bool kern = c->engine == TF_SLOT_COPY_KERNEL;
+    BlobCopies dc, hc;
+    int ndc = 0, nhc = 0, nh = 0;
+    uint8_t *hdst[16];
+    const uint8_t *hsrc[16];
+    int64_t h2d = 0;
     for (int i = 0; i < nm && e == hipSuccess; ++i) {
         const int ex = m[1 + 2 * i], sl = m[2 + 2 * i];
         if (ex < 0 || ex >= c->d.E || sl < 0 || sl >= c->d.S) return fail(TF_E_STATE, "corrupt miss entry");
+        c->mirror[(size_t)layer * c->d.S + sl] = (int16_t)ex;
         uint8_t *dst = c->slot_pool + ((size_t)layer * c->d.S + sl) * c->stride;
-        const uint8_t *src = c->host_pool + ((size_t)layer * c->d.E + ex) * c->stride;
-        e = hipMemcpyAsync(dst, src, c->stride, hipMemcpyHostToDevice, copy);
+        int b = -1;
+        for (int q = 0; q < c->P; ++q)
+            if (pf[q] == ex) { b = q; break; }
+        if (b >= 0) {   // speculatively filled: a device copy from its buffer
+            dc.src[ndc] = reinterpret_cast<const uint4 *>(c->pf_pool + ((size_t)layer * c->P + b) * c->stride);
+            dc.dst[ndc] = reinterpret_cast<uint4 *>(dst);
+            ++ndc;
+            pf[b] = -2;   // used
+            ++c->pf_used;
+        } else {
+            if (kern) {
+                hc.src[nhc] = host_blob_dev(c, layer, ex);
+                hc.dst[nhc] = reinterpret_cast<uint4 *>(dst);
+                ++nhc;
+            } else {
+                hdst[nh] = dst;
+                hsrc[nh] = c->host_pool + ((size_t)layer * c->d.E + ex) * c->stride;
+                ++nh;
+            }
+            h2d += (int64_t)c->stride;
+        }
     }
+    if (e == hipSuccess) e = launch_copies(c, hc, nhc, HOST_WGS_PER_BLOB, copy);
+    if (e == hipSuccess) e = dma_copies(c, hdst, hsrc, nh, copy);
+    if (ndc && e == hipSuccess) {   // after the prefetch copies, wherever they ran
+        e = hipStreamWaitEvent(copy, c->ev_pf[layer], 0);
+        if (e == hipSuccess) e = launch_copies(c, dc, ndc, DEV_WGS_PER_BLOB, copy);
+    }
+    for (int q = 0; q < c->P; ++q) {   // buffers serve one lookup
+        if (pf[q] >= 0) ++c->pf_wasted;
+        pf[q] = -1;
+    }
+    if (e == hipSuccess && c->P) e = hipEventRecord(c->ev_done[layer], copy);
     if (e == hipSuccess && filled) e = hipEventRecord(filled, copy);
     if (e != hipSuccess) return fail(TF_E_HIP, "fill: %s", hipGetErrorString(e));
-    c->bytes_filled += (int64_t)nm * (int64_t)c->stride;
+    c->bytes_filled += h2d;
     if (n_miss_host) *n_miss_host = nm;
+    return TF_OK;
+}
+
+tf_status tf_slot_cache_set_prefetch(tf_slot_cache *c, uint8_t *buffers, int32_t n_buffers) {
+    if (!c) return fail(TF_E_ARG, "NULL cache");
+    if (n_buffers < 0 || n_buffers > 16) return fail(TF_E_ARG, "n_buffers must be in [0, 16]");
+    if (n_buffers && !buffers) return fail(TF_E_ARG, "NULL buffers");
+    if ((uintptr_t)buffers & 255) return fail(TF_E_ALIGN, "buffers 256-byte aligned");
+    hipError_t e = hipSuccess;
+    if (n_buffers && c->ev_pf.empty()) {
+        c->ev_pf.assign(c->d.L, nullptr);
+        c->ev_done.assign(c->d.L, nullptr);
+        for (int l = 0; l < c->d.L && e == hipSuccess; ++l) {
+            e = hipEventCreateWithFlags(&c->ev_pf[l], hipEventDisableTiming);
+            if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_done[l], hipEventDisableTiming);
+        }
+        if (e != hipSuccess) return fail(TF_E_HIP, "prefetch events: %s", hipGetErrorString(e));
+    }
+    e = hipDeviceSynchronize();   // no copy into the old buffers is in flight
+    if (e != hipSuccess) return fail(TF_E_HIP, "set_prefetch: %s", hipGetErrorString(e));
+    c->pf_pool = n_buffers ? buffers : nullptr;
+    c->P = n_buffers;
+    c->pf.assign((size_t)c->d.L * c->P, -1);
+    return TF_OK;
+}
+
+tf_status tf_slot_cache_prefetch(tf_slot_cache *c, int32_t layer, const int32_t *ids_host, int32_t n,
+                                 hipStream_t copy, int32_t *n_issued) {
+    if (!c) return fail(TF_E_ARG, "NULL cache");
+    if (layer < 0 || layer >= c->d.L) return fail(TF_E_ARG, "layer %d out of range", layer);
+    if (!c->P) return fail(TF_E_STATE, "no prefetch buffers (tf_slot_cache_set_prefetch)");
+    if (n < 0 || n > 1024 || (n && !ids_host)) return fail(TF_E_ARG, "need 0 <= n <= 1024 ids");
+    for (int i = 0; i < n; ++i)
+        if (ids_host[i] < 0 || ids_host[i] >= c->d.E) return fail(TF_E_ARG, "id %d out of range", ids_host[i]);
+    if (c->pending[layer]) return fail(TF_E_STATE, "layer %d: lookup not yet filled", layer);
+    // the previous fill's device copies out of these buffers come first
+    hipError_t e = hipStreamWaitEvent(copy, c->ev_done[layer], 0);
+    const int16_t *mir = c->mirror.data() + (size_t)layer * c->d.S;
+    int32_t *pf = c->pf.data() + (size_t)layer * c->P;
+    const bool kern = c->engine == TF_SLOT_COPY_KERNEL;
+    BlobCopies hc;
+    uint8_t *hdst[16];
+    const uint8_t *hsrc[16];
+    int issued = 0;
+    for (int i = 0; i < n && e == hipSuccess; ++i) {
+        const int ex = ids_host[i];
+        bool skip = false;
+        for (int s = 0; s < c->d.S && !skip; ++s) skip = mir[s] == ex;    // resident
+        for (int q = 0; q < c->P && !skip; ++q) skip = pf[q] == ex;       // already fetched
+        if (skip) continue;
+        int b = -1;
+        for (int q = 0; q < c->P; ++q)
+            if (pf[q] == -1) { b = q; break; }
+        if (b < 0) break;   // every buffer holds a prediction
+        uint8_t *dst = c->pf_pool + ((size_t)layer * c->P + b) * c->stride;
+        hc.src[issued] = host_blob_dev(c, layer, ex);
+        hc.dst[issued] = reinterpret_cast<uint4 *>(dst);
+        hdst[issued] = dst;
+        hsrc[issued] = c->host_pool + ((size_t)layer * c->d.E + ex) * c->stride;
+        pf[b] = ex;
+        c->pf_bytes += (int64_t)c->stride;
+        ++issued;
+    }
+    if (e == hipSuccess)
+        e = kern ? launch_copies(c, hc, issued, HOST_WGS_PER_BLOB, copy) : dma_copies(c, hdst, hsrc, issued, copy);
+    if (e == hipSuccess && issued) e = hipEventRecord(c->ev_pf[layer], copy);
+    if (e != hipSuccess) return fail(TF_E_HIP, "prefetch: %s", hipGetErrorString(e));
+    if (n_issued) *n_issued = issued;
+    return TF_OK;
+}
+
+tf_status tf_slot_cache_set_copy_engine(tf_slot_cache *c, int32_t engine) {
+    if (!c) return fail(TF_E_ARG, "NULL cache");
+    if (engine != TF_SLOT_COPY_DMA && engine != TF_SLOT_COPY_KERNEL)
+        return fail(TF_E_ARG, "unknown copy engine %d", engine);
+    if (engine == TF_SLOT_COPY_KERNEL && !c->host_dev)
+        return fail(TF_E_STATE, "the host pool has no device mapping");
+    c->engine = engine;
+    return TF_OK;
+}
+
+tf_status tf_slot_cache_prefetch_stats(const tf_slot_cache *c, int64_t *h2d_bytes, int64_t *used,
+                                       int64_t *wasted) {
+    if (!c) return fail(TF_E_ARG, "NULL cache");
+    if (h2d_bytes) *h2d_bytes = c->pf_bytes;
+    if (used) *used = c->pf_used;
+    if (wasted) *wasted = c->pf_wasted;
     return TF_OK;
 }
 

@@ -260,8 +260,9 @@ void tf_slot_cache_destroy(tf_slot_cache *c);
 tf_status tf_slot_cache_lookup(tf_slot_cache *c, int32_t layer, const int32_t *ids,
                                int32_t n, int32_t *slots, hipStream_t compute);
 /* [SYNC] Wait for the last lookup of `layer`, copy each missed blob from the
- * host pool into its slot on `copy` (one hipMemcpyAsync per miss), then
- * record `filled` (may be NULL) on `copy`.  *n_miss_host receives the count. */
+ * host pool (or a prefetch buffer) into its slot on `copy` (see the copy
+ * engine below), then record `filled` (may be NULL) on `copy`.
+ * *n_miss_host receives the count. */
 tf_status tf_slot_cache_fill(tf_slot_cache *c, int32_t layer, hipStream_t copy,
                              hipEvent_t filled, int32_t *n_miss_host);
 /* [SYNC] Copy `layer`'s trace (hit flag, slot per token and rank) to the host.
@@ -270,8 +271,44 @@ tf_status tf_slot_cache_trace(tf_slot_cache *c, int32_t layer, int8_t *hit_host,
                               int16_t *slot_host, int64_t cap, int64_t *len);
 /* [SYNC] Empty every layer and clear the traces. */
 tf_status tf_slot_cache_reset(tf_slot_cache *c);
-/* Total bytes copied host->device by fills since create/reset. */
+/* Total bytes copied host->device by fills since create/reset (misses served
+ * from a prefetch buffer are device copies and do not count). */
 int64_t tf_slot_cache_bytes_filled(const tf_slot_cache *c);
+
+/* Speculative fill (shengyayun.com AI newsletter of 2026-07-30, "事件与背景"
+ * item 一: read-ahead with parallel reads and a small expert cache hide the
+ * SSD latency; here host-to-device copies of predicted experts run ahead of
+ * the layer's lookup).
+ * set_prefetch: give the cache n_buffers (0..16; 0 turns prefetch off)
+ * expert-sized device buffers per layer, [n_layers][n_buffers][blob_stride]
+ * bytes, 256-B aligned, caller-owned.  Synchronises the device.
+ * prefetch: for each predicted id (host int32 [n], each in [0, n_experts))
+ * that is neither resident in `layer` (as the fills so far left it) nor
+ * already in a buffer, copy its blob from the host pool into a free buffer
+ * on `copy` (ids past the last free buffer are dropped; one launch for all
+ * of them, or one hipMemcpyAsync each, see the copy engine below).  *n_issued (may be NULL) receives the number of copies.  The
+ * layer's next fill takes each miss found in a buffer as a device copy from
+ * it (after the prefetch copies, whatever stream they ran on) and frees every
+ * buffer of the layer; predictions never change the cache's hit/miss
+ * sequence.  TF_E_STATE without buffers or between a lookup and its fill.
+ * prefetch_stats: host->device bytes of prefetch copies, buffers used by a
+ * fill, buffers freed unused (any pointer may be NULL). */
+tf_status tf_slot_cache_set_prefetch(tf_slot_cache *c, uint8_t *buffers, int32_t n_buffers);
+tf_status tf_slot_cache_prefetch(tf_slot_cache *c, int32_t layer, const int32_t *ids_host,
+                                 int32_t n, hipStream_t copy, int32_t *n_issued);
+tf_status tf_slot_cache_prefetch_stats(const tf_slot_cache *c, int64_t *h2d_bytes, int64_t *used,
+                                       int64_t *wasted);
+
+/* How fills and prefetches move blobs on the copy stream.
+ * TF_SLOT_COPY_KERNEL (the default when hipHostGetDevicePointer maps the
+ * host pool): one kernel launch per fill or prefetch reads every blob of the
+ * call over PCIe through the mapping (16 workgroups per blob).
+ * TF_SLOT_COPY_DMA (the default otherwise): one hipMemcpyAsync per blob.
+ * Device copies out of prefetch buffers always run as a
+ * kernel.  TF_E_STATE asks for the kernel engine on an unmapped pool;
+ * TF_E_ARG for an unknown engine. */
+typedef enum { TF_SLOT_COPY_DMA = 0, TF_SLOT_COPY_KERNEL = 1 } tf_slot_copy_engine;
+tf_status tf_slot_cache_set_copy_engine(tf_slot_cache *c, int32_t engine);
 
 /* Eviction rule of later lookups (every layer).  TF_SLOT_LFU (the default,
  * the pages' word): victim = unpinned slot with the smallest (count,

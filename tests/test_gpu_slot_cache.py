@@ -2,9 +2,10 @@
 
 Bars: the hit/slot sequence of every layer equals the oracle's LFU replay
 bitwise; a cached decode step is bitwise identical to the same step with all
-experts resident (the kernels read the same bytes from another pool); sampled
-tokens match the fp64 oracle within the floored 2e-3; the bytes copied equal
-misses x blob stride.  Every layer of a token consumes that token's x, and
+experts resident (the kernels read the same bytes from another pool, moved
+by the copy kernel or by DMA); sampled tokens match the fp64 oracle within
+the floored 2e-3; the bytes copied equal misses x blob stride, split between
+fills and prefetches as the predictions allow.  Every layer of a token consumes that token's x, and
 routing is forced by per-layer Zipf(1.1) popularity.
 """
 import numpy as np
@@ -46,12 +47,23 @@ def _stack(api, seed, L, d, E, k, f, fs):
     return stride, host, layers, dls
 
 
-def _run(api, seed, L, d, E, k, f, fs, S, T, check_tokens, policy="lfu"):
+def _predicted(ids, l, t, mode, rng, E):
+    """Predicted ids of layer l at token t: exact, or with half replaced."""
+    p = ids[l][t].copy()
+    if mode == "noisy":
+        j = rng.choice(p.size, size=p.size // 2, replace=False)
+        p[j] = rng.integers(0, E, size=j.size)
+    return p
+
+
+def _run(api, seed, L, d, E, k, f, fs, S, T, check_tokens, policy="lfu", prefetch=None,
+         engine="kernel"):
     stride, host, layers, dls = _stack(api, seed, L, d, E, k, f, fs)
     ids = np.stack([gen.zipf_ids(seed, l, T, E, k) for l in range(L)])      # [L][T][k]
     x = gen.tokens(seed, T, d)
     slot_pool = torch.empty(L * S * stride, dtype=torch.uint8, device="cuda")
     cache = api.SlotCache(L, E, S, k, stride, slot_pool, host, trace_cap=T, policy=policy)
+    cache.set_copy_engine(engine)
     copy = torch.cuda.Stream()
     xt = torch.from_numpy(x.view(np.int16)).cuda()
     ft = torch.from_numpy(ids).cuda()
@@ -62,11 +74,19 @@ def _run(api, seed, L, d, E, k, f, fs, S, T, check_tokens, policy="lfu"):
     id_c = torch.empty((L, T, k), dtype=torch.int32, device="cuda")
     w_c = torch.empty((L, T, k), dtype=torch.float32, device="cuda")
     id_r, w_r = torch.empty_like(id_c), torch.empty_like(w_c)
+    rng = np.random.default_rng([seed, 77])
+    if prefetch:
+        pf_buf = torch.empty(L * k * stride, dtype=torch.uint8, device="cuda")
+        cache.set_prefetch(pf_buf, k)
+        cache.prefetch(0, _predicted(ids, 0, 0, prefetch, rng, E), copy)
     for t in range(T):
         for l in range(L):
             api.tf_moe_layer_fwd(dls[l], xt[t:t + 1], forced_ids=ft[l, t:t + 1], y=y_c[l, t:t + 1],
                                  ids=id_c[l, t:t + 1], weights=w_c[l, t:t + 1], cache=cache,
                                  layer_idx=l, ws=ws, copy_stream=copy)
+            nl, nt = (l + 1, t) if l + 1 < L else (0, t + 1)
+            if prefetch and nt < T:
+                cache.prefetch(nl, _predicted(ids, nl, nt, prefetch, rng, E), copy)
             api.tf_moe_layer_fwd(dls[l], xt[t:t + 1], forced_ids=ft[l, t:t + 1], y=y_r[l, t:t + 1],
                                  ids=id_r[l, t:t + 1], weights=w_r[l, t:t + 1], ws=ws_r)
     torch.cuda.synchronize()
@@ -81,7 +101,13 @@ def _run(api, seed, L, d, E, k, f, fs, S, T, check_tokens, policy="lfu"):
         assert np.array_equal(hit.reshape(T, k), h_ref), f"layer {l}: hit sequence"
         assert np.array_equal(slot.reshape(T, k), s_ref), f"layer {l}: slot sequence"
         misses += int((~h_ref).sum())
-    assert cache.bytes_filled() == misses * stride
+    pf_bytes, used, wasted = cache.prefetch_stats()
+    assert cache.bytes_filled() + used * stride == misses * stride
+    assert pf_bytes == (used + wasted) * stride
+    if prefetch == "exact":      # every miss was predicted and nothing else fetched
+        assert cache.bytes_filled() == 0 and used == misses and wasted == 0
+    elif prefetch == "noisy":
+        assert 0 < used < misses and wasted > 0
     yc = y_c.cpu().view(torch.int16).numpy().view(np.float16)
     for l in range(L):
         ref = oracle.moe_tokens(layers[l], x[check_tokens], ids[l][check_tokens])
@@ -113,12 +139,13 @@ def test_slot_cache_ragged_shapes(tfa):
     _run(tfa, 5, L=2, d=320, E=12, k=3, f=192, fs=320, S=5, T=40, check_tokens=[0, 39])
 
 
-def test_slot_cache_full_width(tfa):
+@pytest.mark.parametrize("engine", ["dma", "kernel"])
+def test_slot_cache_full_width(tfa, engine):
     # the slot-cache workload's shapes (d=2816, 128 experts, top-8, 16 slots)
-    # on two layers and 48 tokens
-    print("slot cache: d=2816 E=128 k=8 f=704 fs=2816 S=16 L=2 T=48", flush=True)
+    # on two layers and 48 tokens, blobs moved by the copy kernel or by DMA
+    print(f"slot cache: {engine} d=2816 E=128 k=8 f=704 fs=2816 S=16 L=2 T=48", flush=True)
     miss = _run(tfa, 2, L=2, d=2816, E=128, k=8, f=704, fs=2816, S=16, T=48,
-                check_tokens=[0, 47])
+                check_tokens=[0, 47], engine=engine)
     assert 0.2 < miss < 0.9
 
 
@@ -130,3 +157,21 @@ def test_slot_cache_policies_and_sizes(tfa, S, policy):
     miss = _run(tfa, 5, L=2, d=256, E=32, k=4, f=128, fs=256, S=S, T=64, check_tokens=[0, 63],
                 policy=policy)
     assert 0.0 < miss < 1.0
+
+
+@pytest.mark.parametrize("mode,engine", [("exact", "kernel"), ("noisy", "kernel"), ("noisy", "dma")])
+def test_slot_cache_prefetch(tfa, mode, engine):
+    """Speculative fill of the next layer's predicted experts: the hit/slot
+    sequences still equal the oracle's replay and the outputs the resident
+    ones; with exact predictions every miss is served from a buffer (no
+    host->device copy at fill time), with half the predictions wrong the
+    rest go over the host path and the unused buffers are counted."""
+    print(f"slot cache: prefetch {mode} {engine} d=256 E=32 k=4 S=8 L=3 T=64", flush=True)
+    _run(tfa, 6, L=3, d=256, E=32, k=4, f=128, fs=256, S=8, T=64, check_tokens=[0, 63],
+         prefetch=mode, engine=engine)
+
+
+def test_slot_cache_prefetch_full_width(tfa):
+    print("slot cache: prefetch exact d=2816 E=128 k=8 S=16 L=2 T=24", flush=True)
+    _run(tfa, 3, L=2, d=2816, E=128, k=8, f=704, fs=2816, S=16, T=24, check_tokens=[0, 23],
+         prefetch="exact")

@@ -25,6 +25,16 @@ Plus two integer oracles written as plain Python loops:
   prefix whose cumulative probability reaches P, then the first kept rank
   whose cumulative probability exceeds u times the kept total, u in [0, 1)
   given by the caller.  Every sum runs sequentially in rank order.
+* ``attn_decode``: one decode step of attention for one new token.  The
+  pages give the store and the kind of kernel (shilu.ai README translation,
+  "状态和范围": fp16 keys and values; a bounded ring for the 25
+  sliding-window layers and linear storage for the 5 full-attention layers;
+  exact split-K/V decode attention).  Definition: per query head h, with
+  key/value head g = h // (H / G), scores s_t = scale * (q_h . k_{g,t}) over
+  the tokens t the layer sees (the last `window` tokens up to and including
+  the new one, or all of them), p = softmax(s), out_h = sum_t p_t v_{g,t}.
+  The oracle keeps every token's key and value in token order and knows
+  nothing of a ring; "exact" is read as the full softmax, no approximation.
 * ``group_by_expert``: (token, rank) pairs of a prefill chunk sorted by
   (expert, token, rank) -- the grouping that lets one fetched expert serve
   several rows (shilu.ai, "推理引擎的工作原理": prefill in chunks of at
@@ -42,7 +52,10 @@ order by one-hot columns, integer-exact GEMV, brute-force top-k with ties,
 softmax identities, GELU values (Phi(1)), the one-expert rule, closed-form
 0/1 experts, identical-expert combine, hand-derived LFU sequences, byte
 accounting against the pages' 14.3 GB / 1.35 GB, fp16 decode of all 65536
-patterns, and C-vs-NumPy agreement.  No function here is "parity unpinned".
+patterns, C-vs-NumPy agreement, hand-worked sampling rows, and for attention a
+hand-worked two-token case, the uniform-score mean, window and order
+invariances and the query-head grouping.  No function here is "parity
+unpinned".
 """
 from __future__ import annotations
 
@@ -64,7 +77,7 @@ __all__ = [
     "softmax", "expert_ffn", "expert_from_blob", "moe_token", "moe_tokens",
     "np_dequant", "np_qmatvec", "np_gelu", "np_topk", "np_softmax",
     "np_expert", "np_moe_token", "lfu_replay", "group_by_expert", "to_fp16",
-    "num_threads", "sample",
+    "num_threads", "sample", "attn_decode",
 ]
 
 
@@ -389,6 +402,33 @@ def sample(logits, temperature, top_k, top_p, u):
         if cum[n] > target:
             return int(sel[n])
     return int(sel[keep - 1])
+
+
+def attn_decode(q, k_hist, v_hist, window=None, scale=None):
+    """Attention of one new token (see the module docstring).
+
+    ``q``: [H][D] (fp16 values or floats); ``k_hist``, ``v_hist``: [N][G][D],
+    the keys and values of tokens 0..N-1 in token order, the new token last;
+    ``window``: the number of most recent tokens a sliding-window layer sees
+    (None: all N); ``scale``: default 1/sqrt(D).  Returns fp64 [H][D].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(k_hist, dtype=np.float64)
+    Vv = np.asarray(v_hist, dtype=np.float64)
+    H, D = q.shape
+    N, G, _ = K.shape
+    if H % G:
+        raise ValueError("query heads must be a multiple of key/value heads")
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    first = 0 if window is None else max(0, N - window)
+    out = np.empty((H, D))
+    for h in range(H):
+        g = h // (H // G)
+        s = scale * (K[first:, g, :] @ q[h])       # one score per seen token
+        w = np.exp(s - s.max())
+        out[h] = (w / w.sum()) @ Vv[first:, g, :]
+    return out
 
 
 def group_by_expert(ids, n_experts):

@@ -413,3 +413,60 @@ def test_sample_frequencies_match_the_nucleus():
     for r, i in enumerate(order):
         want = q[r] if r < keep else 0.0
         assert abs(cnt[int(i)] / N - want) <= 1.0 / N + 1e-12, (r, cnt[int(i)], want)
+
+
+# ------------------------------------------------------------ decode attention
+def test_attn_hand_worked_cases():
+    cases = json.load(open(os.path.join(GOLD, "attn_cases.json")))["cases"]
+    for c in cases:
+        out = oracle.attn_decode(c["q"], c["k"], c["v"], window=c["window"], scale=c["scale"])
+        assert np.allclose(out, np.array(c["out"]), rtol=0, atol=1e-12), c["name"]
+
+
+def _attn_inputs(seed, H=4, G=2, D=8, N=12):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((H, D)), rng.standard_normal((N, G, D)),
+            rng.standard_normal((N, G, D)))
+
+
+def test_attn_uniform_scores_give_the_window_mean():
+    _, K, V = _attn_inputs(1)
+    q = np.zeros((4, 8))
+    for window in (None, 1, 5, 12, 40):
+        out = oracle.attn_decode(q, K, V, window=window)
+        first = 0 if window is None else max(0, 12 - window)
+        for h in range(4):
+            assert np.allclose(out[h], V[first:, h // 2].mean(axis=0), rtol=0, atol=1e-12)
+
+
+def test_attn_window_and_order_invariances():
+    q, K, V = _attn_inputs(2)
+    full = oracle.attn_decode(q, K, V)
+    assert np.allclose(oracle.attn_decode(q, K, V, window=12), full, rtol=0, atol=1e-13)
+    assert np.allclose(oracle.attn_decode(q, K, V, window=100), full, rtol=0, atol=1e-13)
+    w5 = oracle.attn_decode(q, K, V, window=5)
+    K2, V2 = K.copy(), V.copy()
+    K2[:7] = 50.0                       # tokens outside the window change freely
+    V2[:7] = -1e3
+    assert np.array_equal(oracle.attn_decode(q, K2, V2, window=5), w5)
+    perm = np.random.default_rng(3).permutation(12)
+    assert np.allclose(oracle.attn_decode(q, K[perm], V[perm]), full, rtol=0, atol=1e-12)
+    assert not np.allclose(w5, full, atol=1e-3)
+
+
+def test_attn_query_head_grouping():
+    q, K, V = _attn_inputs(4)
+    q[1] = q[0]                         # heads 0 and 1 read k/v head 0
+    q[2] = q[0]                         # head 2 reads k/v head 1
+    out = oracle.attn_decode(q, K, V)
+    assert np.array_equal(out[0], out[1])
+    assert not np.allclose(out[0], out[2], atol=1e-3)
+    one = oracle.attn_decode(q[2:3], K[:, 1:2], V[:, 1:2])
+    assert np.allclose(out[2], one[0], rtol=0, atol=1e-14)
+
+
+def test_attn_dominant_score_selects_its_value():
+    q, K, V = _attn_inputs(5, H=1, G=1)
+    K[7, 0] = q[0] / np.dot(q[0], q[0]) * 60 * np.sqrt(8)   # score 60 against O(1) others
+    out = oracle.attn_decode(q, K, V)
+    assert np.allclose(out[0], V[7, 0], rtol=0, atol=np.abs(V).max() * 12 * np.exp(-50))

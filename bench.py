@@ -634,6 +634,67 @@ def run_sample(args):
     return out
 
 
+def run_attn(args):
+    """Decode attention of one token (16 query heads, 8 key/value heads, head
+    dim 256): a full layer at its 4,096th token and a 1,024-slot
+    sliding-window ring past its first wrap."""
+    import numpy as np
+    import torch
+
+    from bit_routed_expert_tf_amd import _lib, api
+    from synth import gen
+    lib = _lib.load()
+    dev = torch.device("cuda:0")
+    H, G, D = 16, 8, 256
+    stream = torch.cuda.Stream(device=dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    out = {"metric": "decode attention us per token (16 q heads, 8 kv heads, head dim 256)",
+           "unit": "us", "n_gpus": 1, "higher_is_better": False, "data": "synthetic (seeded)",
+           "dtype": "fp16 KV, fp32 scores and sums", "config": {"workload": "attn-decode-h16-g8-d256"},
+           "layers": {}}
+    for name, S, pos, ring in (("full-4096", 4096, 4095, 0), ("sliding-1024", 1024, 5000, 1)):
+        nq = 64   # distinct queries cycled through
+        q, k, v = gen.attn_inputs(21, nq, H, G, D)
+        kc = torch.from_numpy(np.random.default_rng(5).standard_normal((G, S, D)).astype(np.float16)
+                              .view(np.int16)).to(dev)
+        vc = torch.from_numpy(np.random.default_rng(6).standard_normal((G, S, D)).astype(np.float16)
+                              .view(np.int16)).to(dev)
+        Q = torch.from_numpy(q.view(np.int16)).to(dev)
+        Kn = torch.from_numpy(k.view(np.int16)).to(dev)
+        Vn = torch.from_numpy(v.view(np.int16)).to(dev)
+        O = torch.empty((nq, H, D), dtype=torch.float32, device=dev)
+        ws = api.workspace(api.tf_attn_workspace_bytes(H, D, S), dev)
+
+        def step(i):
+            j = i % nq
+            _lib.check(lib.tf_attn_decode(
+                ctypes.c_void_p(Q[j].data_ptr()), ctypes.c_void_p(Kn[j].data_ptr()),
+                ctypes.c_void_p(Vn[j].data_ptr()), ctypes.c_void_p(kc.data_ptr()),
+                ctypes.c_void_p(vc.data_ptr()), H, G, D, S, pos, ring, 1.0 / D ** 0.5,
+                ctypes.c_void_p(O[j].data_ptr()), ctypes.c_void_p(ws.data_ptr()), ws.numel(), sh))
+
+        with torch.cuda.stream(stream):
+            step(0)
+        torch.cuda.synchronize()
+        graphs = _graphs(step, nq, nq, stream)
+        steps, ms = _timed(graphs, args.steps or 4000, min(args.warmup, 1000), stream)
+        kern = _profile(lib, _hip(), {_lib.TF_KERNEL_ATTN_CHUNK: "k_attn_chunk",
+                                      _lib.TF_KERNEL_ATTN_COMBINE: "k_attn_combine"}, step,
+                        min(args.prof_steps, 200), stream)
+        seen = min(pos + 1, S)
+        nbytes = 2 * G * seen * D * 2   # keys and values the token sees, read once
+        kus = kern["k_attn_chunk"]["avg_us"]
+        out["layers"][name] = {
+            "us_per_call": round(ms * 1e3 / steps, 3), "kv_bytes": nbytes, "kernels": kern,
+            "roofline": {"bound": "hbm", "achieved": round(nbytes / (kus * 1e-6) / 1e9, 1),
+                         "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(nbytes / (kus * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}}
+    L = out["layers"]
+    out["value"] = round(25 * L["sliding-1024"]["us_per_call"] + 5 * L["full-4096"]["us_per_call"], 2)
+    out["per_token_30_layers"] = "25 sliding-window layers + 5 full layers"
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -650,11 +711,12 @@ def main():
                          "prefetched (exact predictions, and half of them wrong)")
     ap.add_argument("--slot-sweep", action="store_true",
                     help="slot-cache workload: also run 8, 16 and 32 slots under LFU and LRU")
-    ap.add_argument("--workload", choices=["decode", "prefill", "stack", "slot-cache", "sample"],
+    ap.add_argument("--workload", choices=["decode", "prefill", "stack", "slot-cache", "sample",
+                                           "attn"],
                     default="decode",
                     help="decode (default, the headline line); the others measure the "
                          "prefill chunk, the 30-layer resident stack, the slot-cache stack "
-                         "and next-token sampling")
+                         "next-token sampling and decode attention")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this hot path is built and measured on a single "
@@ -669,7 +731,7 @@ def main():
         if "--steps" not in sys.argv:
             args.steps = 0   # the workload's own count
         out = {"prefill": run_prefill, "stack": run_stack, "slot-cache": run_slot,
-               "sample": run_sample}[args.workload](args)
+               "sample": run_sample, "attn": run_attn}[args.workload](args)
     print(json.dumps(out), flush=True)
 
 

@@ -23,6 +23,7 @@ TF_KERNEL_ROUTER_SHARED_GATEUP, TF_KERNEL_ROUTED_GATEUP_SHARED_DOWN, TF_KERNEL_D
 TF_KERNEL_PREFILL_DOWN, TF_KERNEL_PREFILL_COMBINE = 8, 16
 TF_KERNEL_PREFILL_GATEUP, TF_KERNEL_GROUP = 32, 64
 TF_KERNEL_SAMPLE_PART, TF_KERNEL_SAMPLE_FINAL = 128, 256
+TF_KERNEL_ATTN_CHUNK, TF_KERNEL_ATTN_COMBINE = 512, 1024
 TF_SLOT_LFU, TF_SLOT_LRU = 0, 1
 TF_SLOT_COPY_DMA, TF_SLOT_COPY_KERNEL = 0, 1
 
@@ -74,6 +75,10 @@ _SIGS = {
     "tf_moe_prefill_chunk": (c_int32, [ctypes.POINTER(tf_moe_layer), c_void_p, c_int32,
                                        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                        c_void_p, c_size_t]),
+    "tf_attn_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
+    "tf_attn_decode": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
+                                 c_int32, c_int32, c_int32, c_int32, c_int32, ctypes.c_float,
+                                 c_void_p, c_void_p, c_size_t, c_void_p]),
     "tf_sample_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
     "tf_sample": (c_int32, [c_void_p, c_int32, c_int32, ctypes.c_float, c_int32, ctypes.c_float,
                             c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),

@@ -19,6 +19,7 @@ __all__ = [
     "tf_moe_layer_fwd", "tf_router_workspace_bytes", "tf_router_topk",
     "tf_gemv_workspace_bytes", "tf_expert_q4_gemv", "tf_prefill_workspace_bytes",
     "tf_moe_prefill_chunk", "tf_group_workspace_bytes", "tf_group_by_expert", "tf_sample_workspace_bytes", "tf_sample",
+    "tf_attn_workspace_bytes", "tf_attn_decode",
     "tf_workspace_flags", "tf_workspace_zero", "SlotCache",
     "pinned_host", "stream_handle",
 ]
@@ -231,6 +232,28 @@ def tf_sample(logits, temperature, top_k, top_p, u=None, ids=None, ws=None, stre
                            _p(u), _p(ids), _p(ws), ws.numel(),
                            stream_handle(stream)))
     return ids
+
+
+def tf_attn_workspace_bytes(H, D, S):
+    return int(load().tf_attn_workspace_bytes(H, D, S))
+
+
+def tf_attn_decode(q, k_new, v_new, k_cache, v_cache, pos, ring, scale=None, out=None, ws=None,
+                   stream=None):
+    """q [H][D], k_new/v_new [G][D], caches [G][S][D] (fp16 bit patterns as
+    int16 or float16 tensors); returns out [H][D] fp32."""
+    H, D = q.shape
+    G, S, _ = k_cache.shape
+    if scale is None:
+        scale = 1.0 / D ** 0.5
+    if out is None:
+        out = torch.empty((H, D), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = workspace(tf_attn_workspace_bytes(H, D, S), q.device)
+    check(load().tf_attn_decode(_p(q), _p(k_new), _p(v_new), _p(k_cache), _p(v_cache), H, G, D, S,
+                                pos, int(bool(ring)), float(scale), _p(out), _p(ws), ws.numel(),
+                                stream_handle(stream)))
+    return out
 
 
 def tf_workspace_zero(ws, stream=None):

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libtf.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["tf_api.cpp", "tf_decode.hip", "tf_slot.hip", "tf_grouped.hip", "tf_prefill.hip", "tf_sample.hip"]
+SOURCES = ["tf_api.cpp", "tf_decode.hip", "tf_slot.hip", "tf_grouped.hip", "tf_prefill.hip", "tf_sample.hip", "tf_attn.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 ops are switched off for every device pass.

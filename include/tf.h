@@ -191,6 +191,33 @@ tf_status tf_group_by_expert(const int32_t *ids, int32_t T, int32_t top_k, int32
                              int32_t *counts, int32_t *offsets, int32_t *pairs, void *ws,
                              size_t ws_bytes, hipStream_t s);
 
+/* ------------------------------------------------------------ attention */
+/* Decode attention of one new token (shilu.ai README translation, "状态和范围":
+ * fp16 key/value storage, a bounded ring for the sliding-window layers and
+ * linear storage for the full-attention layers, exact split-K/V decode
+ * attention).  Per query head h, with key/value head g = h / (H / G):
+ * scores s = scale * q_h . k over the tokens the layer sees, p = softmax(s),
+ * out_h = sum p v.  The call first stores the new token's key and value:
+ * ring != 0 keeps the last S tokens (token pos in slot pos % S; the layer
+ * sees min(pos + 1, S) tokens); ring == 0 keeps token pos in slot pos
+ * (pos < S; the layer sees pos + 1 tokens).
+ *   q            [H][D] fp16 device (already normalised and rotated).
+ *   k_new, v_new [G][D] fp16 device: the new token's key and value.
+ *   k_cache, v_cache [G][S][D] fp16 device, caller-owned; slot pos (or
+ *                pos % S) is written, the others only read.
+ *   out          [H][D] fp32 device.
+ *   ws           tf_attn_workspace_bytes(H, D, S) bytes, 256-B aligned.
+ * D in {64, 128, 256}; H = G, 2G or 4G, H <= 1024; 1 <= S <= 2^20
+ * (TF_E_SHAPE); pos >= 0, pos < S without the ring, scale > 0 (TF_E_ARG);
+ * q, k/v and the caches 16-B aligned (TF_E_ALIGN).  Two launches,
+ * stream-ordered: per (32-slot chunk, key/value head) the chunk's softmax
+ * statistics and weighted values, then their exact merge per query head. */
+size_t tf_attn_workspace_bytes(int32_t H, int32_t D, int32_t S);
+tf_status tf_attn_decode(const uint16_t *q, const uint16_t *k_new, const uint16_t *v_new,
+                         uint16_t *k_cache, uint16_t *v_cache, int32_t H, int32_t G, int32_t D,
+                         int32_t S, int32_t pos, int32_t ring, float scale, float *out, void *ws,
+                         size_t ws_bytes, hipStream_t s);
+
 /* ------------------------------------------------------------ sampling */
 /* Next-token ids from rows of logits (shilu.ai README translation,
  * "向模型输入 prompt": the temperature, Top-K and Top-P knobs; temperature 0
@@ -227,7 +254,9 @@ enum {
     TF_KERNEL_PREFILL_GATEUP = 32,           /* prefill: shared and per-item gate/up (MFMA) */
     TF_KERNEL_GROUP = 64,                    /* tf_group_by_expert                        */
     TF_KERNEL_SAMPLE_PART = 128,             /* tf_sample: per-slice 64 largest keys      */
-    TF_KERNEL_SAMPLE_FINAL = 256             /* tf_sample: row merge, softmax, draw       */
+    TF_KERNEL_SAMPLE_FINAL = 256,            /* tf_sample: row merge, softmax, draw       */
+    TF_KERNEL_ATTN_CHUNK = 512,              /* tf_attn_decode: per-chunk partials        */
+    TF_KERNEL_ATTN_COMBINE = 1024            /* tf_attn_decode: merge per query head      */
 };
 /* Arm a one-shot timer: the next launch, by this host thread, of the named
  * kernel goes through hipExtLaunchKernel with `start` recorded when the

@@ -268,3 +268,17 @@ def sample_inputs(seed, n_rows, vocab=VOCAB, pattern="lm"):
                 l[r, pos[18:]] = top
     u = rng.random(n_rows)
     return l, u
+
+
+ATTN_STREAM = 9300
+
+
+def attn_inputs(seed, n_tokens, n_heads, n_kv_heads, head_dim):
+    """Per token: q [H][D], k and v [G][D], fp16 draws of N(0, 1) (the scale
+    of per-head normalised queries and keys).  Returns three arrays
+    [n_tokens][...] of float16."""
+    rng = _rng(seed, ATTN_STREAM, n_tokens, n_heads, n_kv_heads, head_dim)
+    q = rng.standard_normal((n_tokens, n_heads, head_dim)).astype(np.float16)
+    k = rng.standard_normal((n_tokens, n_kv_heads, head_dim)).astype(np.float16)
+    v = rng.standard_normal((n_tokens, n_kv_heads, head_dim)).astype(np.float16)
+    return q, k, v

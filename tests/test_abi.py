@@ -166,3 +166,22 @@ def test_sample_argument_errors():
              None) == _lib.TF_E_ALIGN
     assert f(p, 262144, 16, 0.7, 64, 0.95, p, p, ws, need - 1, None) == _lib.TF_E_NOMEM
     assert b"workspace" in lib.tf_last_error()
+
+
+def test_attn_argument_errors():
+    lib = tfa.load()
+    p = ctypes.c_void_p(1 << 20)
+    ws = ctypes.c_void_p(1 << 28)
+    f = lib.tf_attn_decode
+    need = lib.tf_attn_workspace_bytes(16, 256, 4096)
+    assert need >= 16 * 128 * 258 * 4
+    assert f(p, p, p, p, p, 16, 8, 96, 4096, 0, 0, 0.0625, p, ws, need, None) == _lib.TF_E_SHAPE   # D
+    assert f(p, p, p, p, p, 24, 8, 256, 4096, 0, 0, 0.0625, p, ws, need, None) == _lib.TF_E_SHAPE  # H = 3G
+    assert f(p, p, p, p, p, 16, 8, 256, 0, 0, 0, 0.0625, p, ws, need, None) == _lib.TF_E_SHAPE     # S
+    assert f(p, p, p, p, p, 16, 8, 256, 4096, 4096, 0, 0.0625, p, ws, need, None) == _lib.TF_E_ARG  # linear full
+    assert f(p, p, p, p, p, 16, 8, 256, 4096, -1, 1, 0.0625, p, ws, need, None) == _lib.TF_E_ARG
+    assert f(p, p, p, p, p, 16, 8, 256, 4096, 5, 1, 0.0, p, ws, need, None) == _lib.TF_E_ARG       # scale
+    assert f(None, p, p, p, p, 16, 8, 256, 4096, 5, 1, 0.0625, p, ws, need, None) == _lib.TF_E_ARG
+    assert f(ctypes.c_void_p((1 << 20) + 8), p, p, p, p, 16, 8, 256, 4096, 5, 1, 0.0625, p, ws, need,
+             None) == _lib.TF_E_ALIGN
+    assert f(p, p, p, p, p, 16, 8, 256, 4096, 5, 1, 0.0625, p, ws, need - 1, None) == _lib.TF_E_NOMEM

@@ -185,19 +185,21 @@ __global__ __launch_bounds__(WGS) void k_attn_chunk(const uint16_t *q, const uin
 // Merge of the NC chunk results of query head h = g * R + r over 32 of its
 // columns (grid (D / 32, H)): thread (d, cg) runs an online merge over the
 // chunks c = cg, cg + 8, ... (running maximum, rescaled sum and column
-// value), then the 8 chunk groups merge through LDS:
+// value), 16 (above 64 chunks) or 4 chunks' loads at a time, then the 8
+// chunk groups merge through LDS:
 // M = max m_c, L = sum l_c e^(m_c - M), out = sum o_c e^(m_c - M) / L.
 constexpr int CMB_D = 32, CMB_G = WGS / CMB_D;
+template <int CMB_U>   // chunks per thread in flight: 16 above 64 chunks, else 4
 __global__ __launch_bounds__(WGS) void k_attn_combine(int D, int R, int NC, Parts P, float *out) {
     __shared__ float sm[CMB_G][CMB_D], sl[CMB_G][CMB_D], so[CMB_G][CMB_D];
     const int h = blockIdx.y, g = h / R, r = h % R;
     const int dl = threadIdx.x % CMB_D, cg = threadIdx.x / CMB_D;
     const int d = blockIdx.x * CMB_D + dl;
     float m = -INFINITY, l = 0.f, o = 0.f;
-    for (int c0 = cg; c0 < NC; c0 += 4 * CMB_G) {
-        float mc[4], lc[4], oc[4];
+    for (int c0 = cg; c0 < NC; c0 += CMB_U * CMB_G) {
+        float mc[CMB_U], lc[CMB_U], oc[CMB_U];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {   // four chunks' loads in flight
+        for (int u = 0; u < CMB_U; ++u) {   // CMB_U chunks' loads in flight
             const int c = c0 + u * CMB_G;
             const size_t pi = ((size_t)g * NC + (c < NC ? c : 0)) * R + r;
             mc[u] = c < NC ? P.m[pi] : -INFINITY;
@@ -205,7 +207,7 @@ __global__ __launch_bounds__(WGS) void k_attn_combine(int D, int R, int NC, Part
             oc[u] = c < NC ? P.o[pi * D + d] : 0.f;
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < CMB_U; ++u) {
             const float mn = fmaxf(m, mc[u]);
             if (mn == -INFINITY) continue;
             const float a = __expf(m - mn), b = __expf(mc[u] - mn);
@@ -294,7 +296,10 @@ tf_status tf_attn_decode(const uint16_t *q, const uint16_t *k_new, const uint16_
     default: e = launch_chunks<256>(R, grid, q, k_new, v_new, k_cache, v_cache, S, n_valid, slot, scale, NC, P, s); break;
     }
     if (e == hipSuccess) {
-        TF_LAUNCH(TF_KERNEL_ATTN_COMBINE, k_attn_combine, dim3(D / CMB_D, H), dim3(WGS), 0, s, D, R, NC, P, out);
+        if (NC > 64)
+            TF_LAUNCH(TF_KERNEL_ATTN_COMBINE, k_attn_combine<16>, dim3(D / CMB_D, H), dim3(WGS), 0, s, D, R, NC, P, out);
+        else
+            TF_LAUNCH(TF_KERNEL_ATTN_COMBINE, k_attn_combine<4>, dim3(D / CMB_D, H), dim3(WGS), 0, s, D, R, NC, P, out);
         e = hipGetLastError();
     }
     if (e != hipSuccess) return fail(TF_E_HIP, "attention launch: %s", hipGetErrorString(e));

@@ -11,9 +11,10 @@
 // their order.
 //
 // Two launches:
-//   k_attn_chunk    grid (chunks of CH slots, G): one workgroup per chunk of
-//                   one key/value head serves all R = H / G query heads of it
-//                   from one read of the chunk's keys and values.  The chunk
+//   k_attn_chunk    grid (chunks of CH slots, G; CH = 64 when the layer sees
+//                   more than 2,048 tokens, else 32): one workgroup per chunk
+//                   of one key/value head serves all R = H / G query heads of
+//                   it from one read of the chunk's keys and values.  The chunk
 //                   holding the new token's slot writes k_new / v_new there
 //                   and uses them directly.  Out: per query head the chunk's
 //                   score maximum m, sum of exp(s - m), and sum of
@@ -36,7 +37,7 @@ void tf_set_error(const char *msg);   // tf_api.cpp
 namespace {
 
 constexpr int WGS = 256;
-constexpr int CH = 32;                 // slots per chunk
+constexpr int LONG_SEEN = 2048;        // above this many seen tokens, 64-slot chunks
 
 tf_status fail(tf_status st, const char *fmt, ...) {
     char buf[256];
@@ -69,7 +70,7 @@ struct Parts {
 
 // D: head dim; R: query heads per key/value head.  Thread t holds column
 // block cb = t % CPR (8 fp16 of a row) of rows r0 + RPI * i.
-template <int D, int R>
+template <int D, int R, int CH>
 __global__ __launch_bounds__(WGS) void k_attn_chunk(const uint16_t *q, const uint16_t *k_new,
                                                     const uint16_t *v_new, uint16_t *k_cache,
                                                     uint16_t *v_cache, int S, int n_valid,
@@ -235,17 +236,18 @@ __global__ __launch_bounds__(WGS) void k_attn_combine(int D, int R, int NC, Part
     }
 }
 
-size_t chunks(int S) { return ((size_t)S + CH - 1) / CH; }
+int chunk_slots(int n_valid) { return n_valid > LONG_SEEN ? 64 : 32; }
+size_t chunks(int n, int ch) { return ((size_t)n + ch - 1) / ch; }
 size_t up256(size_t n) { return (n + 255) & ~size_t(255); }
 
-template <int D>
+template <int D, int CH>
 hipError_t launch_chunks(int R, dim3 grid, const uint16_t *q, const uint16_t *kn, const uint16_t *vn,
                          uint16_t *kc, uint16_t *vc, int S, int n_valid, int slot, float scale, int NC,
                          Parts P, hipStream_t s) {
     switch (R) {
-    case 1: TF_LAUNCH(TF_KERNEL_ATTN_CHUNK, (k_attn_chunk<D, 1>), grid, dim3(WGS), 0, s, q, kn, vn, kc, vc, S, n_valid, slot, scale, NC, P); break;
-    case 2: TF_LAUNCH(TF_KERNEL_ATTN_CHUNK, (k_attn_chunk<D, 2>), grid, dim3(WGS), 0, s, q, kn, vn, kc, vc, S, n_valid, slot, scale, NC, P); break;
-    case 4: TF_LAUNCH(TF_KERNEL_ATTN_CHUNK, (k_attn_chunk<D, 4>), grid, dim3(WGS), 0, s, q, kn, vn, kc, vc, S, n_valid, slot, scale, NC, P); break;
+    case 1: TF_LAUNCH(TF_KERNEL_ATTN_CHUNK, (k_attn_chunk<D, 1, CH>), grid, dim3(WGS), 0, s, q, kn, vn, kc, vc, S, n_valid, slot, scale, NC, P); break;
+    case 2: TF_LAUNCH(TF_KERNEL_ATTN_CHUNK, (k_attn_chunk<D, 2, CH>), grid, dim3(WGS), 0, s, q, kn, vn, kc, vc, S, n_valid, slot, scale, NC, P); break;
+    case 4: TF_LAUNCH(TF_KERNEL_ATTN_CHUNK, (k_attn_chunk<D, 4, CH>), grid, dim3(WGS), 0, s, q, kn, vn, kc, vc, S, n_valid, slot, scale, NC, P); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -257,7 +259,7 @@ extern "C" {
 
 size_t tf_attn_workspace_bytes(int32_t H, int32_t D, int32_t S) {
     if (H <= 0 || D <= 0 || S <= 0) return 256;
-    const size_t n = (size_t)H * chunks(S);
+    const size_t n = (size_t)H * chunks(S, 32);   // the most chunks a call on this store uses
     return 2 * up256(4 * n) + up256(4 * n * D);
 }
 
@@ -282,19 +284,31 @@ tf_status tf_attn_decode(const uint16_t *q, const uint16_t *k_new, const uint16_
     const int R = H / G;
     const int n_valid = pos + 1 < S ? pos + 1 : S;
     const int slot = ring ? pos % S : pos;
-    const int NC = (int)chunks(n_valid);
-    const size_t n = (size_t)H * chunks(S);
+    const int ch = chunk_slots(n_valid);
+    const int NC = (int)chunks(n_valid, ch);
+    const size_t n = (size_t)H * chunks(S, 32);
     Parts P;
     P.m = reinterpret_cast<float *>(ws);
     P.l = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(ws) + up256(4 * n));
     P.o = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(ws) + 2 * up256(4 * n));
     const dim3 grid(NC, G);
     hipError_t e;
-    switch (D) {
-    case 64: e = launch_chunks<64>(R, grid, q, k_new, v_new, k_cache, v_cache, S, n_valid, slot, scale, NC, P, s); break;
-    case 128: e = launch_chunks<128>(R, grid, q, k_new, v_new, k_cache, v_cache, S, n_valid, slot, scale, NC, P, s); break;
-    default: e = launch_chunks<256>(R, grid, q, k_new, v_new, k_cache, v_cache, S, n_valid, slot, scale, NC, P, s); break;
+#define TF_ATTN_CHUNKS(DD, CC) \
+    launch_chunks<DD, CC>(R, grid, q, k_new, v_new, k_cache, v_cache, S, n_valid, slot, scale, NC, P, s)
+    if (ch == 64) {
+        switch (D) {
+        case 64: e = TF_ATTN_CHUNKS(64, 64); break;
+        case 128: e = TF_ATTN_CHUNKS(128, 64); break;
+        default: e = TF_ATTN_CHUNKS(256, 64); break;
+        }
+    } else {
+        switch (D) {
+        case 64: e = TF_ATTN_CHUNKS(64, 32); break;
+        case 128: e = TF_ATTN_CHUNKS(128, 32); break;
+        default: e = TF_ATTN_CHUNKS(256, 32); break;
+        }
     }
+#undef TF_ATTN_CHUNKS
     if (e == hipSuccess) {
         if (NC > 64)
             TF_LAUNCH(TF_KERNEL_ATTN_COMBINE, k_attn_combine<16>, dim3(D / CMB_D, H), dim3(WGS), 0, s, D, R, NC, P, out);

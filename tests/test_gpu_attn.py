@@ -8,9 +8,10 @@ the GPU keeps a ring of S slots (token p in slot p % S) or a linear store
 new token's key and value stored bitwise in their slot.  Cases: token
 sequences that wrap a ring twice, rings and stores whose sizes are not a
 multiple of the 32-slot chunk, 1, 2 and 4 query heads per key/value head,
-head dims 64, 128 and 256, and the full-size layers (16 query heads, 8
-key/value heads, head dim 256): a 4,096-token full layer at its last
-position and a 1,024-slot ring at token 5,000.
+head dims 64, 128 and 256, stores past 2,048 seen tokens (64-slot chunks),
+and the full-size layers (16 query heads, 8 key/value heads, head dim 256):
+a 4,096-token full layer at its last position and a 1,024-slot ring at
+token 5,000.
 """
 import numpy as np
 import pytest
@@ -100,6 +101,16 @@ def test_attn_full_layer_at_4096(tfa):
 def test_attn_sliding_layer_wrapped(tfa):
     print("attn: ring S=1024 pos=5000 H=16 G=8 D=256", flush=True)
     _prefilled(tfa, 3, 1, 1024, 5000)
+
+
+@pytest.mark.parametrize("ring,S,pos,H,G,D", [
+    (0, 2200, 2100, 8, 2, 128),    # past 2,048 seen tokens: 64-slot chunks
+    (1, 3000, 4000, 4, 4, 64),     # a wrapped ring with 64-slot chunks, one head per group
+    (0, 2048, 2047, 4, 1, 256),    # exactly 2,048 seen tokens: 32-slot chunks
+])
+def test_attn_long_stores(tfa, ring, S, pos, H, G, D):
+    print(f"attn: ring={ring} S={S} pos={pos} H={H} G={G} D={D}", flush=True)
+    _prefilled(tfa, 8, ring, S, pos, H=H, G=G, D=D)
 
 
 def test_attn_first_token_and_scale(tfa):

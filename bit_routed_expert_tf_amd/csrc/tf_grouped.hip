@@ -32,9 +32,10 @@
 // the four slot columns of a token are summed (DPP), in a fixed order.
 //
 // Streaming.  A workgroup is persistent: it takes units blockIdx.x,
-// blockIdx.x + gridDim.x, ...  K goes through LDS in chunks of 8 groups
-// (activations, and scale/bias as fp32); each lane holds its codes of one
-// chunk in registers.  Loads run one chunk ahead regardless of unit
+// blockIdx.x + gridDim.x, ...  K goes through LDS in chunks of 16 groups
+// (gate/up) or 4 (down) (activations, and scale/bias as fp32); each lane
+// holds its codes of one chunk in registers.  Loads run one chunk ahead
+// regardless of unit
 // boundaries: the last chunk of a unit loads the first chunk of the next
 // (whose item record was loaded when the unit began), so a unit's start-up
 // and epilogue overlap the next unit's loads.
@@ -510,7 +511,7 @@ __device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1, KC> &L) {
     }
 }
 
-constexpr int KC_GU = 8, KC_DN = 4;   // groups per staged chunk
+constexpr int KC_GU = 16, KC_DN = 4;  // groups per staged chunk
 constexpr int DEPTH = 1;              // chunks loaded ahead
 
 __global__ __launch_bounds__(256, 4) void k_gu(DecodeArgs a) {

@@ -35,10 +35,9 @@
 // blockIdx.x + gridDim.x, ...  K goes through LDS in chunks of 16 groups
 // (gate/up) or 4 (down) (activations, and scale/bias as fp32); each lane
 // holds its codes of one chunk in registers.  Loads run one chunk ahead
-// regardless of unit
-// boundaries: the last chunk of a unit loads the first chunk of the next
-// (whose item record was loaded when the unit began), so a unit's start-up
-// and epilogue overlap the next unit's loads.
+// regardless of unit boundaries: the last chunk of a unit loads the first
+// chunk of the next (whose item record was loaded when the unit began), so a
+// unit's start-up and epilogue overlap the next unit's loads.
 #include "tf_device.h"
 #include "tf_internal.h"
 #include "tf_layer.h"

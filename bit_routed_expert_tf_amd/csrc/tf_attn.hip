@@ -30,11 +30,14 @@
 #include <cstdarg>
 #include <cstdio>
 
+#include "tf_device.h"
 #include "tf_internal.h"
 
 void tf_set_error(const char *msg);   // tf_api.cpp
 
 namespace {
+
+using namespace tfk;
 
 constexpr int WGS = 256;
 constexpr int LONG_SEEN = 2048;        // above this many seen tokens, 64-slot chunks
@@ -130,7 +133,7 @@ __global__ __launch_bounds__(WGS) void k_attn_chunk(const uint16_t *q, const uin
             for (int r = 0; r < R; ++r) sc[r][jl] = ok ? part[i][r] * scale : -INFINITY;
         }
     }
-    __syncthreads();
+    lds_barrier();
     // chunk softmax statistics: wave r handles query head r (CH <= 64 lanes)
     const int lane = tid & 63, w = tid >> 6;
     if (w < R) {
@@ -147,7 +150,7 @@ __global__ __launch_bounds__(WGS) void k_attn_chunk(const uint16_t *q, const uin
             P.l[pi] = l;
         }
     }
-    __syncthreads();
+    lds_barrier();
     // weighted values: this thread's 8 columns over its rows, then summed over
     // the RPI row groups through LDS
     float acc[R][8];
@@ -173,7 +176,7 @@ __global__ __launch_bounds__(WGS) void k_attn_chunk(const uint16_t *q, const uin
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int e = 0; e < 8; ++e) red[r0][r][cb * 8 + e] = acc[r][e];
-    __syncthreads();
+    lds_barrier();
     for (int x = tid; x < R * D; x += WGS) {
         const int r = x / D, d = x % D;
         float s = 0.f;
@@ -220,7 +223,7 @@ __global__ __launch_bounds__(WGS) void k_attn_combine(int D, int R, int NC, Part
     sm[cg][dl] = m;
     sl[cg][dl] = l;
     so[cg][dl] = o;
-    __syncthreads();
+    lds_barrier();
     if (cg == 0) {
         float M = -INFINITY;
 #pragma unroll

@@ -3,7 +3,7 @@
 // defaults 0.2 / 64 / 0.95, temperature 0 for greedy output).
 //
 // Steps (the order is a reading; the pages give only the knobs): the top_k
-// largest logits of the row, ties to the lower id and NaN last; their
+// largest logits of the row, ties to the lower id and NaN ranked as -inf; their
 // softmax at the temperature, in fp64 with every sum sequential in rank
 // order; the shortest rank prefix whose cumulative probability reaches
 // top_p; then the first kept rank whose cumulative probability exceeds u

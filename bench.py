@@ -244,10 +244,21 @@ def cpu_baseline(args, router, shared_blob, pool, X, wl):
         oracle.moe_token(L, X[n])
         n += 1
     dt = time.perf_counter() - t0
-    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
+    cores = oracle.num_threads()
+    # the same oracle on one core, over a shorter sample
+    oracle.set_num_threads(1)
+    n1, t1 = 0, time.perf_counter()
+    while n1 < 2 or (time.perf_counter() - t1 < args.cpu_seconds / 4 and n1 < wl.n_tokens):
+        oracle.moe_token(L, X[n1])
+        n1 += 1
+    dt1 = time.perf_counter() - t1
+    oracle.set_num_threads(cores)
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": cores,
             "kind": "oracle",
             "sample": f"first {n} of the {wl.n_tokens} workload tokens, one at a time "
-                      f"({dt:.1f} s, C fp64 oracle, OpenMP over rows)"}
+                      f"({dt:.1f} s, C fp64 oracle, OpenMP over rows)",
+            "one_core": {"value": round(n1 / dt1, 3), "unit": "tokens/s", "cores": 1,
+                         "sample": f"first {n1} tokens ({dt1:.1f} s)"}}
 
 
 def _profile(lib, h, kernels, step, nprof, stream):

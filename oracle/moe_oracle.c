@@ -221,3 +221,14 @@ int orc_num_threads(void)
     return 1;
 #endif
 }
+
+/* Threads of later calls (n >= 1); for timing the oracle on fewer cores. */
+void orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

@@ -77,7 +77,7 @@ __all__ = [
     "softmax", "expert_ffn", "expert_from_blob", "moe_token", "moe_tokens",
     "np_dequant", "np_qmatvec", "np_gelu", "np_topk", "np_softmax",
     "np_expert", "np_moe_token", "lfu_replay", "group_by_expert", "to_fp16",
-    "num_threads", "sample", "attn_decode",
+    "num_threads", "set_num_threads", "sample", "attn_decode",
 ]
 
 
@@ -109,6 +109,8 @@ def lib():
             L.orc_gelu.argtypes = [ctypes.c_double, i32]
             L.orc_topk.argtypes = [P, i32, i32, P]
             L.orc_softmax.argtypes = [P, i32, P]
+            L.orc_set_num_threads.argtypes = [i32]
+            L.orc_set_num_threads.restype = None
             L.orc_expert_ffn.argtypes = [P] * 9 + [i32, i32, i32, P, P, P]
             L.orc_expert_blob.argtypes = [P, i32, i32, i32, P, P, P]
             L.orc_moe_token.restype = i32
@@ -129,6 +131,11 @@ def _c(a, dtype):
 
 def num_threads():
     return lib().orc_num_threads()
+
+
+def set_num_threads(n):
+    """Threads of later C-oracle calls (timing only; results do not depend on it)."""
+    lib().orc_set_num_threads(int(n))
 
 
 # --------------------------------------------------------------------------

@@ -123,6 +123,7 @@ def test_slot_cache_create_argument_errors():
     assert lib.tf_slot_cache_set_prefetch(None, p, 8) == _lib.TF_E_ARG
     assert lib.tf_slot_cache_prefetch(None, 0, p, 8, None, None) == _lib.TF_E_ARG
     assert lib.tf_slot_cache_prefetch_stats(None, None, None, None) == _lib.TF_E_ARG
+    assert lib.tf_slot_cache_set_copy_engine(None, _lib.TF_SLOT_COPY_KERNEL) == _lib.TF_E_ARG
 
 
 def test_group_argument_errors():

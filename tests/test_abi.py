@@ -186,3 +186,17 @@ def test_attn_argument_errors():
     assert f(ctypes.c_void_p((1 << 20) + 8), p, p, p, p, 16, 8, 256, 4096, 5, 1, 0.0625, p, ws, need,
              None) == _lib.TF_E_ALIGN
     assert f(p, p, p, p, p, 16, 8, 256, 4096, 5, 1, 0.0625, p, ws, need - 1, None) == _lib.TF_E_NOMEM
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """No fallback: loading a library that is not there raises, naming the build."""
+    import subprocess
+    import sys
+    code = ("import bit_routed_expert_tf_amd._lib as L\n"
+            "try:\n"
+            f"    L.load({str(tmp_path / 'libtf.so')!r})\n"
+            "except RuntimeError as e:\n"
+            "    print('raised:', e)\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                       timeout=120)
+    assert "raised:" in r.stdout and "build()" in r.stdout, r.stdout + r.stderr

@@ -8,7 +8,7 @@ Cases: the full 262,144-id vocabulary at the default knobs (temperature
 0.2, top-k 64, top-p 0.95), greedy, top-p 1, a small top-k, top-k 1; ragged
 vocabularies (one slice, a partial last slice, top_k == V); many equal
 logits (ties go to the lower id); logits sorted ascending (the whole top in
-the last slice); NaN, -inf and signed zeros; draws at 0 and just below 1.
+the last slice); NaN, -inf and signed zeros; draws at 0 and just below 1; the largest row count (4,096) in one call.
 """
 import numpy as np
 import pytest
@@ -104,3 +104,9 @@ def test_workspace_reuse(tfa):
         t32, p32 = float(np.float32(knobs[0])), float(np.float32(knobs[2]))
         want = [oracle.sample(l[r], t32, knobs[1], p32, float(u[r])) for r in range(T)]
         assert np.array_equal(ids.cpu().numpy(), np.array(want)), (seed, T, V)
+
+
+def test_maximum_rows(tfa):
+    """4,096 rows in one call (the largest T), a 100-id vocabulary."""
+    l, u = gen.sample_inputs(10, 4096, 100, "lm")
+    _check(tfa, l, u, 0.9, 8, 0.9)

@@ -8,7 +8,8 @@ Cases: the full 262,144-id vocabulary at the default knobs (temperature
 0.2, top-k 64, top-p 0.95), greedy, top-p 1, a small top-k, top-k 1; ragged
 vocabularies (one slice, a partial last slice, top_k == V); many equal
 logits (ties go to the lower id); logits sorted ascending (the whole top in
-the last slice); NaN, -inf and signed zeros; draws at 0 and just below 1; the largest row count (4,096) in one call.
+the last slice); NaN, -inf and signed zeros; draws at 0 and just below 1;
+the largest row count (4,096) in one call.
 """
 import numpy as np
 import pytest

@@ -513,7 +513,7 @@ __device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1, KC> &L) {
 constexpr int KC_GU = 16, KC_DN = 4;  // groups per staged chunk
 constexpr int DEPTH = 1;              // chunks loaded ahead
 
-__global__ __launch_bounds__(256, 4) void k_gu(DecodeArgs a) {
+__global__ __launch_bounds__(256, 2) void k_gu(DecodeArgs a) {
     __shared__ GLds<1, KC_GU> L;
     grouped<false, KC_GU, DEPTH>(a, L);
 }
@@ -526,13 +526,15 @@ __global__ __launch_bounds__(256, 4) void k_dn(DecodeArgs a) {
 }  // namespace
 
 // After the router launch (top-k and grouping into items of at most four
-// tokens): gate/up, down, then the combine.  Persistent grids of at most
-// four workgroups per compute unit.
+// tokens): gate/up, down, then the combine.  Persistent grids of at most two
+// (gate/up) and four (down) workgroups per compute unit: gate/up measured
+// 53.5, 52.0, 49.3 and 64.6 us per 16-token layer at four, three, two and
+// one per unit, down 36.0 at four against 46.0 at two.
 hipError_t tf_launch_grouped(const DecodeArgs &a, int max_items, hipStream_t s) {
     const int quads = (a.T + UT - 1) / UT;
-    const int cap = 4 * 256;
+    const int cap_gu = 2 * 256, cap = 4 * 256;
     const int n_gu = quads * (a.fs / 32) + max_items * (a.f / 32);
-    TF_LAUNCH(TF_KERNEL_PREFILL_GATEUP, k_gu, dim3(n_gu < cap ? n_gu : cap), dim3(WG), 0, s, a);
+    TF_LAUNCH(TF_KERNEL_PREFILL_GATEUP, k_gu, dim3(n_gu < cap_gu ? n_gu : cap_gu), dim3(WG), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int n_dn = (quads + max_items) * (a.d / 64);

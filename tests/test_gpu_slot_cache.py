@@ -159,16 +159,17 @@ def test_slot_cache_policies_and_sizes(tfa, S, policy):
     assert 0.0 < miss < 1.0
 
 
-@pytest.mark.parametrize("mode,engine", [("exact", "kernel"), ("noisy", "kernel"), ("noisy", "dma")])
-def test_slot_cache_prefetch(tfa, mode, engine):
+@pytest.mark.parametrize("mode,engine,policy", [("exact", "kernel", "lfu"), ("noisy", "kernel", "lfu"),
+                                                ("noisy", "dma", "lfu"), ("noisy", "kernel", "lru")])
+def test_slot_cache_prefetch(tfa, mode, engine, policy):
     """Speculative fill of the next layer's predicted experts: the hit/slot
     sequences still equal the oracle's replay and the outputs the resident
     ones; with exact predictions every miss is served from a buffer (no
     host->device copy at fill time), with half the predictions wrong the
     rest go over the host path and the unused buffers are counted."""
-    print(f"slot cache: prefetch {mode} {engine} d=256 E=32 k=4 S=8 L=3 T=64", flush=True)
+    print(f"slot cache: prefetch {mode} {engine} {policy} d=256 E=32 k=4 S=8 L=3 T=64", flush=True)
     _run(tfa, 6, L=3, d=256, E=32, k=4, f=128, fs=256, S=8, T=64, check_tokens=[0, 63],
-         prefetch=mode, engine=engine)
+         prefetch=mode, engine=engine, policy=policy)
 
 
 def test_slot_cache_prefetch_full_width(tfa):

@@ -315,11 +315,12 @@ int64_t tf_slot_cache_bytes_filled(const tf_slot_cache *c);
  * that is neither resident in `layer` (as the fills so far left it) nor
  * already in a buffer, copy its blob from the host pool into a free buffer
  * on `copy` (ids past the last free buffer are dropped; one launch for all
- * of them, or one hipMemcpyAsync each, see the copy engine below).  *n_issued (may be NULL) receives the number of copies.  The
- * layer's next fill takes each miss found in a buffer as a device copy from
- * it (after the prefetch copies, whatever stream they ran on) and frees every
- * buffer of the layer; predictions never change the cache's hit/miss
- * sequence.  TF_E_STATE without buffers or between a lookup and its fill.
+ * of them, or one hipMemcpyAsync each, see the copy engine below).
+ * *n_issued (may be NULL) receives the number of copies.  The layer's next
+ * fill takes each miss found in a buffer as a device copy from it (after the
+ * prefetch copies, whatever stream they ran on) and frees every buffer of
+ * the layer; predictions never change the cache's hit/miss sequence.
+ * TF_E_STATE without buffers or between a lookup and its fill.
  * prefetch_stats: host->device bytes of prefetch copies, buffers used by a
  * fill, buffers freed unused (any pointer may be NULL). */
 tf_status tf_slot_cache_set_prefetch(tf_slot_cache *c, uint8_t *buffers, int32_t n_buffers);
@@ -333,9 +334,9 @@ tf_status tf_slot_cache_prefetch_stats(const tf_slot_cache *c, int64_t *h2d_byte
  * host pool): one kernel launch per fill or prefetch reads every blob of the
  * call over PCIe through the mapping (16 workgroups per blob).
  * TF_SLOT_COPY_DMA (the default otherwise): one hipMemcpyAsync per blob.
- * Device copies out of prefetch buffers always run as a
- * kernel.  TF_E_STATE asks for the kernel engine on an unmapped pool;
- * TF_E_ARG for an unknown engine. */
+ * Device copies out of prefetch buffers always run as a kernel.  TF_E_STATE
+ * asks for the kernel engine on an unmapped pool; TF_E_ARG for an unknown
+ * engine. */
 typedef enum { TF_SLOT_COPY_DMA = 0, TF_SLOT_COPY_KERNEL = 1 } tf_slot_copy_engine;
 tf_status tf_slot_cache_set_copy_engine(tf_slot_cache *c, int32_t engine);
 

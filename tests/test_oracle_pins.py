@@ -160,6 +160,31 @@ def test_p7_gelu_is_the_erf_form():
     assert np.allclose([oracle.gelu(z) for z in zs], oracle.np_gelu(zs), rtol=1e-15, atol=1e-16)
 
 
+def test_p7_gelu_tanh_branch():
+    """The tanh form 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))), pinned
+    against things the oracle does not compute: PyTorch's own fp64 tanh-GELU
+    (a library routine), the odd identity gelu(z) - gelu(-z) = z (which a
+    non-odd inner polynomial, e.g. a z^2 term, breaks), the two limits, and
+    the form's known worst deviation from the erf form (about 4.7e-4, near
+    |z| = 2.7): between 3e-4 and 5e-4 over [-6, 6]."""
+    import torch
+    zs = np.linspace(-6, 6, 241)
+    got = np.array([oracle.gelu(z, tanh=True) for z in zs])
+    ref = torch.nn.functional.gelu(torch.from_numpy(zs), approximate="tanh").numpy()
+    assert np.allclose(got, ref, rtol=1e-14, atol=1e-15)
+    ref_erf = torch.nn.functional.gelu(torch.from_numpy(zs), approximate="none").numpy()
+    assert np.allclose([oracle.gelu(z) for z in zs], ref_erf, rtol=1e-14, atol=1e-15)
+    assert oracle.gelu(1.0, tanh=True) == pytest.approx(0.8411919906082768, abs=1e-15)
+    for z in zs:
+        assert oracle.gelu(z, tanh=True) - oracle.gelu(-z, tanh=True) == pytest.approx(z, abs=1e-13)
+    dev = np.abs(got - np.array([oracle.gelu(z) for z in zs]))
+    assert 3e-4 < dev.max() < 5e-4
+    assert 2.4 < abs(zs[np.argmax(dev)]) < 3.0
+    assert oracle.gelu(-12.0, tanh=True) == pytest.approx(0.0, abs=1e-20)
+    assert oracle.gelu(12.0, tanh=True) == pytest.approx(12.0, abs=1e-14)
+    assert np.allclose(got, oracle.np_gelu(zs, tanh=True), rtol=1e-14, atol=1e-15)
+
+
 # ----------------------------------------------------- P8 closed-form expert
 def test_p8_selection_matrix_expert_closed_form():
     rng = np.random.default_rng(8)

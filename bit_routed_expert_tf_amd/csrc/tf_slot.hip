@@ -151,10 +151,11 @@ __global__ __launch_bounds__(64) void k_lookup(SlotDev c, int layer, const int32
         if (v < 0) {
             for (int s = 0; s < S; ++s) {
                 if ((pinned >> s) & 1u) continue;
+                if (v < 0) { v = s; continue; }   // the first unpinned slot
                 const bool lt = c.policy == TF_SLOT_LRU
                                     ? last[s] < last[v]
                                     : count[s] < count[v] || (count[s] == count[v] && last[s] < last[v]);
-                if (v < 0 || lt) v = s;
+                if (lt) v = s;
             }
             slot_of[expert_of[v]] = -1;
         }

@@ -64,6 +64,15 @@ tf_status check_layer(const tf_moe_layer *L) {
     return TF_OK;
 }
 
+// Counters (flags, tickets) sit at the start of every workspace, at offsets
+// that depend on nothing but the entry point: sized for the most tokens a
+// call takes and, for the decode down launch's tickets, the widest d_model.
+// Data regions never overlap them, so a workspace stays valid when it is
+// reused for another token count or another layer shape (every completed
+// call leaves its counters at zero).
+constexpr size_t kHdrBytes = (hdr_bytes(MAX_PREFILL_T) + 255) & ~size_t(255);
+constexpr size_t kCtkBytes = (size_t)128 * (4096 / 32);   // one token's down tiles
+
 // Decode workspace layout (offsets in bytes).
 struct WsLayout {
     size_t hdr, logits, items, pairs, hs, ys, hr, xb, ye, ctk, total;
@@ -72,7 +81,8 @@ struct WsLayout {
 WsLayout decode_layout(int d, int f, int fs, int E, int k, int T) {
     WsLayout w{};
     size_t o = 0;
-    w.hdr = o; o += up256(hdr_bytes(T));
+    w.hdr = o; o += kHdrBytes;
+    w.ctk = o; o += kCtkBytes;             // decode down tile tickets (one token)
     w.logits = o; o += up256((size_t)8 * T * E);
     w.items = o; o += up256((size_t)4 * ITEM_INTS * T * k);
     w.pairs = o; o += up256((size_t)4 * T * k);
@@ -81,7 +91,6 @@ WsLayout decode_layout(int d, int f, int fs, int E, int k, int T) {
     w.hr = o; o += up256(h_row_bytes(f) * T * k);
     w.xb = o; o += up256((size_t)16 * tfk::xb_row_u4(d) * T);
     w.ye = o; o += up256((size_t)4 * T * k * d);           // decode: per-pair down rows
-    w.ctk = o; o += up256((size_t)128 * T * (d / 32));     // decode: down tile tickets
     w.total = o;
     return w;
 }
@@ -200,7 +209,8 @@ tf_status tf_workspace_flags(void *ws, int32_t *flags_host, hipStream_t s) {
     return e == hipSuccess ? TF_OK : hip_fail(e, "clearing workspace flags");
 }
 
-static size_t router_hdr_bytes(int32_t T) { return up256(hdr_bytes(T)); }
+// The router's counters: sized for the largest T it takes (see kHdrBytes).
+static size_t router_hdr_bytes(int32_t) { return up256(hdr_bytes(4096)); }
 
 size_t tf_router_workspace_bytes(int32_t n_experts, int32_t T) {
     if (n_experts <= 0 || T <= 0) return 256;

@@ -232,6 +232,25 @@ def test_repeat_runs_are_bitwise_identical(tfa, full):
         assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
 
 
+def test_workspace_reused_across_token_counts(tfa, full):
+    """One workspace for steps of 16, 3, 1, 5, 1 and 16 tokens: the same
+    bits as a fresh workspace each time (the counters never share bytes with
+    data regions whose place depends on the token count)."""
+    L, D, X = full
+    ws = tfa.workspace(tfa.tf_moe_workspace_bytes(D, 16))
+    xt = torch.from_numpy(X[400:464].view(np.int16)).cuda()
+    r0 = 0
+    for T in (16, 3, 1, 5, 1, 16):
+        x = xt[r0:r0 + T]
+        a = tfa.tf_moe_layer_fwd(D, x, ws=ws, want_y32=True)
+        b = tfa.tf_moe_layer_fwd(D, x, want_y32=True)
+        torch.cuda.synchronize()
+        for u, v in zip(a, b):
+            assert torch.equal(u.view(torch.int16) if u.dtype == torch.float16 else u,
+                               v.view(torch.int16) if v.dtype == torch.float16 else v), T
+        r0 += T
+
+
 def test_router_topk_logits_fp64(tfa, full):
     L, D, X = full
     x = X[:64]

@@ -268,15 +268,17 @@ __device__ __forceinline__ void hs_store(const HStage<MAXI, MAXS> &Hs, int rows,
 // exponentials in fp32, normalised in fp64).  Whole WG.
 //
 // Selection is exact on the fp64 logits, through 64-bit keys that order as
-// the logits do.  Candidate i goes to group i % k; the k group maxima are k
-// distinct candidates, so the k-th largest key is at least tau, the least
-// of them, and no candidate below tau can be selected.  The few candidates
-// at or above tau are ranked among themselves:
-//     rank(i) = #{j : key_j > key_i or (key_j == key_i and j < i)},
-// which is their rank among all candidates, since every other one is
-// smaller.
+// the logits do (NaN taken as -inf, -0 as +0).  Every candidate counts the
+// keys above its own, g(i) = #{j : key_j > key_i}: P threads per candidate
+// each scan a contiguous share of the keys (LDS reads that every lane of the
+// wave shares), and the P counts are added by lane moves.  Without exact
+// ties the g of the k largest are 0 .. k-1, one candidate each, and g(i) is
+// the rank; each selected candidate also counts itself into its rank's slot,
+// so a tie (two candidates with the same g, a slot below k with a count
+// other than one) is seen, and then every candidate counts again by the full
+// rule rank(i) = g(i) + #{j < i : key_j == key_i}.
 __host__ __device__ constexpr int topk_lds_bytes(int E) {
-    return 8 * E + 8 * E + 8 * 16 + 4 * 16 + 4 * E + 8 * E + 16;
+    return 8 * E + 8 * E + 4 * 16 + 4 * 16 + 16;
 }
 
 // Unsigned key ordered as the double (NaN excluded; -0 taken as +0).
@@ -285,18 +287,40 @@ __device__ __forceinline__ uint64_t order_key(double v) {
     return (u >> 63) ? ~u : (u | (1ull << 63));
 }
 
+// Keys above key_i among keys [j0, j1) (pairs of keys per LDS read; j0 even);
+// with TIES, also the keys equal to key_i at positions below i.
+template <bool TIES>
+__device__ __forceinline__ int count_above(const uint64_t *key, int j0, int j1, uint64_t ki, int i) {
+    int r = 0;
+    int j = j0;
+    for (; j + 8 <= j1; j += 8) {
+        ulonglong2 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const ulonglong2 *>(key + j + 2 * u);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            r += (int)(v[u].x > ki) + (int)(v[u].y > ki);
+            if (TIES) r += (int)((v[u].x == ki) & (j + 2 * u < i)) + (int)((v[u].y == ki) & (j + 2 * u + 1 < i));
+        }
+    }
+    for (; j < j1; ++j) {
+        const uint64_t kj = key[j];
+        r += (int)(kj > ki);
+        if (TIES) r += (int)((kj == ki) & (j < i));
+    }
+    return r;
+}
+
 __device__ void topk_block(const DecodeArgs &a, int t, int tid, unsigned char *lds) {
     const int E = a.E;
-    double *l = reinterpret_cast<double *>(lds);             // [E] logits
-    uint64_t *key = reinterpret_cast<uint64_t *>(l + E);     // [E]
-    uint64_t *gmax = key + E;                                 // [16] group maxima
-    int *sel = reinterpret_cast<int *>(gmax + 16);            // [16]
-    int *sid = sel + 16;                                      // [E] candidates >= tau
-    uint64_t *skey = reinterpret_cast<uint64_t *>(sid + ((E + 1) & ~1));  // [E] their keys
-    int *ns = reinterpret_cast<int *>(skey + E);              // their count
-    lds_barrier();
-    if (tid < 16) gmax[tid] = tid < a.k ? 0ull : ~0ull;   // below every key; unused groups above
-    if (tid == 0) *ns = 0;
+    uint64_t *key = reinterpret_cast<uint64_t *>(lds);        // [E] (16-byte aligned)
+    double *l = reinterpret_cast<double *>(key + E);          // [E] logits
+    int *sel = reinterpret_cast<int *>(l + E);                // [16] id of each rank
+    int *hits = sel + 16;                                     // [16] candidates per rank
+    int *tie = hits + 16;                                     // a rank below k not held once
+    lds_barrier();   // the caller's LDS (router partial sums) is no longer read
+    if (tid < 16) { sel[tid] = 0; hits[tid] = 0; }
+    if (tid == 0) *tie = 0;
     for (int i = tid; i < E; i += WG) {
         double v = ld_dev(a.logits + (size_t)t * E + i);
         if (v != v) v = -__builtin_inf();   // NaN ranks last
@@ -317,99 +341,55 @@ __device__ void topk_block(const DecodeArgs &a, int t, int tid, unsigned char *l
                 if (sel[r] == sel[tid]) fl |= TF_FLAG_ID_REPEAT;
         if (fl) atomicOr(a.hdr + HDR_FLAGS, fl);
     } else {
-        for (int i = tid; i < E; i += WG) atomicMax(reinterpret_cast<unsigned long long *>(gmax + i % a.k),
-                                                    (unsigned long long)key[i]);
-        lds_barrier();
-        // all sixteen slots read at once (the unused ones hold the largest key)
-        uint64_t gm[16];
-#pragma unroll
-        for (int g = 0; g < 16; g += 2) {
-            const ulonglong2 v = *reinterpret_cast<const ulonglong2 *>(gmax + g);
-            gm[g] = v.x;
-            gm[g + 1] = v.y;
-        }
-        uint64_t tau = gm[0];
-#pragma unroll
-        for (int g = 1; g < 16; ++g) tau = min(tau, gm[g]);
-        for (int i = tid; i < E; i += WG) {
-            const uint64_t ki = key[i];
-            if (ki >= tau) {
-                const int q = atomicAdd(ns, 1);
-                sid[q] = i;
-                skey[q] = ki;
+        // P threads per candidate (adjacent lanes), P in {1, 2, 4}; candidates
+        // beyond WG / P are taken in further rounds
+        const int P = E <= 64 ? 4 : E <= 128 ? 2 : 1;
+        const int part = tid & (P - 1), per = ((E + P - 1) / P + 1) & ~1;
+        const int j0 = min(E, part * per), j1 = min(E, j0 + per);
+        for (int c0 = 0; c0 < E; c0 += WG / P) {
+            const int c = c0 + tid / P, cc = min(c, E - 1);
+            int g = count_above<false>(key, j0, j1, key[cc], cc);
+            if (P >= 2) g += __builtin_amdgcn_update_dpp(0, g, DPP_XOR1, 0xF, 0xF, false);
+            if (P >= 4) g += __builtin_amdgcn_update_dpp(0, g, DPP_XOR2, 0xF, 0xF, false);
+            if (c < E && part == 0 && g < a.k) {
+                sel[g] = c;
+                atomicAdd(&hits[g], 1);
             }
         }
         lds_barrier();
-        const int S = *ns;
-        if (S <= WG / 4) {
-            // four threads per survivor, each over every fourth survivor, the
-            // four counts added by lane moves within the quad
-            const int q = tid >> 2, part = tid & 3, qc = min(q, max(S - 1, 0));
-            const int i = sid[qc];
-            const uint64_t ki = skey[qc];
-            int r = 0;
-            for (int j0 = part; j0 < S; j0 += 32) {
-                uint64_t kj[8];
-                int jj[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int jq = min(j0 + 4 * u, S - 1);
-                    kj[u] = skey[jq];
-                    jj[u] = sid[jq];
-                }
-#pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    r += (int)((j0 + 4 * u < S) & ((kj[u] > ki) | ((kj[u] == ki) & (jj[u] < i))));
-            }
-            r += __builtin_amdgcn_update_dpp(0, r, DPP_XOR1, 0xF, 0xF, false);
-            r += __builtin_amdgcn_update_dpp(0, r, DPP_XOR2, 0xF, 0xF, false);
-            if (q < S && part == 0 && r < a.k) sel[r] = i;
-        } else {
-            for (int q = tid; q < S; q += WG) {
-                const int i = sid[q];
-                const uint64_t ki = skey[q];
-                int r = 0;
-                for (int j0 = 0; j0 < S; j0 += 8) {
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) {
-                        const int jq = min(j0 + u, S - 1);
-                        const uint64_t kj = skey[jq];
-                        const int j = sid[jq];
-                        r += j0 + u < S && (kj > ki || (kj == ki && j < i));
-                    }
-                }
-                if (r < a.k) sel[r] = i;
+        if (tid < a.k && hits[tid] != 1) *tie = 1;
+        lds_barrier();
+        if (*tie) {   // exact ties: rank by the full rule
+            for (int c0 = 0; c0 < E; c0 += WG / P) {
+                const int c = c0 + tid / P, cc = min(c, E - 1);
+                int r = count_above<true>(key, j0, j1, key[cc], cc);
+                if (P >= 2) r += __builtin_amdgcn_update_dpp(0, r, DPP_XOR1, 0xF, 0xF, false);
+                if (P >= 4) r += __builtin_amdgcn_update_dpp(0, r, DPP_XOR2, 0xF, 0xF, false);
+                if (c < E && part == 0 && r < a.k) sel[r] = c;
             }
         }
     }
     lds_barrier();
-    if (tid < WAVE) {   // lane r < k: rank r (k <= 16: one row of lanes)
+    if (tid < WAVE) {   // lane r < k: rank r (k <= 16)
         const int r = tid, id = sel[min(r, a.k - 1)];
-        const double v = r < a.k ? l[id] : -__builtin_inf();
-        // the maximum over the row (exact in any order)
-        double m = v;
+        const double v = l[id];
+        // the largest selected logit (rank 0 without forced ids; any order is
+        // exact for a maximum)
+        double m = r < a.k ? v : -__builtin_inf();
         m = fmax(m, dpp_d<DPP_XOR1>(m));
         m = fmax(m, dpp_d<DPP_XOR2>(m));
         m = fmax(m, dpp_d<DPP_HALF_MIRROR>(m));
         m = fmax(m, dpp_d<DPP_MIRROR>(m));
         const double e = r < a.k ? (double)expf((float)(v - m)) : 0.0;
-        // the sum in rank order, every lane adding the same sequence (the
-        // values go through LDS, read back all at once)
-        double *ex = l;   // the logits are no longer read
-        if (r < 16) ex[r] = e;
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        __builtin_amdgcn_wave_barrier();
-        double ev[16];
-#pragma unroll
-        for (int q = 0; q < 16; q += 2) {
-            const double2 v2 = *reinterpret_cast<const double2 *>(ex + q);
-            ev[q] = v2.x;
-            ev[q + 1] = v2.y;
-        }
+        // the sum in rank order, every lane adding the same sequence
+        const long long eb = __builtin_bit_cast(long long, e);
         double s = 0.0;
 #pragma unroll
-        for (int q = 0; q < 16; ++q)
-            if (q < a.k) s += ev[q];
+        for (int q = 0; q < 16; ++q) {
+            const int lo = __builtin_amdgcn_readlane((int)(eb & 0xFFFFFFFF), q);
+            const int hi = __builtin_amdgcn_readlane((int)(eb >> 32), q);
+            if (q < a.k) s += __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned)lo);
+        }
         if (r < a.k) {
             st_dev(a.ids + (size_t)t * a.k + r, (int32_t)id);
             st_dev(a.weights + (size_t)t * a.k + r, (float)(e / s));

@@ -149,12 +149,15 @@ def test_slot_cache_full_width(tfa, engine):
     assert 0.2 < miss < 0.9
 
 
-@pytest.mark.parametrize("S,policy", [(8, "lru"), (4, "lfu"), (4, "lru"), (16, "lru")])
-def test_slot_cache_policies_and_sizes(tfa, S, policy):
-    """The LRU reading and other slot counts: hit/slot sequences equal the
-    oracle's replay of the same rule, cached outputs equal resident ones."""
-    print(f"slot cache: {policy} S={S} d=256 E=32 k=4 L=2 T=64", flush=True)
-    miss = _run(tfa, 5, L=2, d=256, E=32, k=4, f=128, fs=256, S=S, T=64, check_tokens=[0, 63],
+@pytest.mark.parametrize("S,policy,E", [(8, "lru", 32), (4, "lfu", 32), (4, "lru", 32),
+                                         (16, "lru", 32), (32, "lfu", 96), (32, "lru", 96)])
+def test_slot_cache_policies_and_sizes(tfa, S, policy, E):
+    """The LRU reading and other slot counts, up to the largest (32 slots, the
+    sweep's top size, with more experts than slots so that victims are
+    chosen): hit/slot sequences equal the oracle's replay of the same rule,
+    cached outputs equal resident ones."""
+    print(f"slot cache: {policy} S={S} d=256 E={E} k=4 L=2 T=96", flush=True)
+    miss = _run(tfa, 5, L=2, d=256, E=E, k=4, f=128, fs=256, S=S, T=96, check_tokens=[0, 95],
                 policy=policy)
     assert 0.0 < miss < 1.0
 

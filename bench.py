@@ -1,17 +1,25 @@
 #!/usr/bin/env python3
 """MoE-layer decode throughput on one MI355X.
 
-Workload (default): one full-width q4 MoE layer -- d_model 2816, 128 routed
-experts (all resident in HBM), top-8, expert FFN 704, shared expert FFN 2816,
-MLX-style affine 4-bit weights (group 64) and an 8-bit router -- decoding
-10,000 seeded tokens x ~ N(0,1) one token per step.  A step is the whole hot
-path for one token: router + top-8 + softmax, shared expert, the 8 routed
-experts' gate/up/down, combine, fp16 output.
+Default workload (resident-stack-30L-e128k8-uniform): 30 MoE layers of the
+full-width shape -- d_model 2816, 128 routed experts per layer, all resident
+in HBM (12.85 GB of q4 experts), top-8, expert FFN 704, shared expert FFN
+2816, MLX-style affine 4-bit weights (group 64) and an 8-bit router --
+decoding one token per step with uniform random (forced) routing; every layer
+of a step consumes that step's token.  A step is the whole hot path for one
+token through all 30 layers: router + top-8 + softmax, shared expert, the 8
+routed experts' gate/up/down and the combine, per layer.
 
-Prints one JSON line: tokens/s over the timed steps (inputs already resident
-in HBM, steps replayed from HIP graphs), the dominant kernel's roofline
-(algorithmic bytes per launch / its average duration from hipExtLaunchKernel
-start/stop events), and the fp64 CPU oracle timed on a bounded sample.
+Prints one JSON line.  ``value`` is tokens/s over exactly --steps steps,
+replayed from HIP graphs after exactly --warmup warm-up steps, each step on a
+token (and routing) of its own, inputs already resident in HBM.  The
+roofline is that of the dominant kernel (the routed gate/up + shared down
+launch): its algorithmic bytes divided by its average duration from
+start/stop events attached to the launch (hipEventDisableSystemFence, so the
+events do not flush the caches), taken on steps after the timed ones.
+Batch 16 on the same stack and the single-layer decode workload
+(decode-layer-d2816-e128k8) are reported under their own keys, and the fp64
+CPU oracle is timed on a bounded sample of the headline workload.
 """
 from __future__ import annotations
 
@@ -27,53 +35,55 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "MoE-layer decode tokens/s + achieved HBM GB/s (% of peak), 1×MI355X"
+NO_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence
 
 
 def _hip():
     h = ctypes.CDLL("libamdhip64.so")
-    h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
     h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                       ctypes.c_void_p]
-    h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
     h.hipEventDestroy.argtypes = [ctypes.c_void_p]
     return h
 
 
 def _event(h):
     e = ctypes.c_void_p()
-    assert h.hipEventCreate(ctypes.byref(e)) == 0
+    assert h.hipEventCreateWithFlags(ctypes.byref(e), NO_SYSTEM_FENCE) == 0
     return e
 
 
 def qmat_bytes(n, k, bits=4):
-    return n * k * bits // 8 + 2 * n * (k // 64) * 2
+    """Codes plus one fp16 scale and one fp16 bias per group of 64."""
+    return n * k * bits // 8 + 4 * n * (k // 64)
 
 
-def stage_b_bytes(d, f, fs, k, T=1):
-    """Algorithmic bytes of one routed-gate/up + shared-down launch (T tokens,
-    every token's experts distinct): weights + x in, h_s in, h_r and y_s out."""
-    w = k * T * 2 * qmat_bytes(f, d) + qmat_bytes(d, fs)
-    return w + T * d * 2 + T * fs * 4 + T * k * f * 4 + T * d * 4
+def stage_b_bytes(d, f, fs, k):
+    """Algorithmic bytes of one single-token routed-gate/up + shared-down
+    launch: the k experts' gate/up and the shared down weights, x and h_s in,
+    h_r and y_s out."""
+    w = k * 2 * qmat_bytes(f, d) + qmat_bytes(d, fs)
+    return w + d * 2 + fs * 4 + k * f * 4 + d * 4
 
 
 def layer_bytes(d, f, fs, E, k):
-    """Bytes one decode token must move: the 8-bit router, the shared expert,
-    k routed experts (q4 codes + fp16 scale/bias), plus x in and y out."""
+    """Bytes one decode token must move through one layer: the 8-bit router,
+    the shared expert, k routed experts, plus x in and y out."""
     router = qmat_bytes(E, d, 8)
     shared = 2 * qmat_bytes(fs, d) + qmat_bytes(d, fs)
     routed = k * (2 * qmat_bytes(f, d) + qmat_bytes(d, f))
     return router + shared + routed + 2 * d + 2 * d
 
 
-def _traffic_for(kernel_name, workload):
+def _traffic_for(name, workload):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources; else None."""
-    from bit_routed_expert_tf_amd import profiling
+    taken on the current kernel sources and this workload; else None."""
+    import profiling
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
-        rec = json.load(open(path))[kernel_name]
+        rec = json.load(open(path))[name]
     except (KeyError, ValueError):
         return None
     if (rec.get("source_sha256") != profiling.source_sha256(rec.get("kernel", ""))
@@ -82,20 +92,242 @@ def _traffic_for(kernel_name, workload):
     return rec.get("hbm_bytes_per_launch")
 
 
-def copy_calibration(nbytes=256 << 20, reps=3):
-    """Plain device-to-device copies of a known size, for scaling the memory
-    counters (rocprofv3 FETCH_SIZE / WRITE_SIZE) of the same run."""
+def calibration(nbytes=256 << 20, reps=3):
+    """Kernels of known traffic for scaling the memory counters (rocprofv3
+    FETCH_SIZE / WRITE_SIZE) of the same run: a read-only reduction and a
+    write-only fill of nbytes each."""
     import torch
-    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    b = torch.empty_like(a)
-    a.fill_(1)
+    a = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
     for _ in range(reps):
-        b.copy_(a)
+        a.sum()
+        a.fill_(2)
     torch.cuda.synchronize()
-    del a, b
+    del a
+
+
+def _profile(lib, h, kernels, step, steps, stream):
+    """Average durations of the named kernels over eager calls step(i) for i
+    in `steps`: start/stop events attached to the launch (fence-free)."""
+    import torch
+
+    from bit_routed_expert_tf_amd import _lib
+    out = {}
+    for kid, name in kernels.items():
+        evs = [(_event(h), _event(h)) for _ in steps]
+        with torch.cuda.stream(stream):
+            for (a, b), i in zip(evs, steps):
+                _lib.check(lib.tf_profile_kernel(kid, a, b))
+                step(i)
+        torch.cuda.synchronize()
+        durs = []
+        for a, b in evs:
+            v = ctypes.c_float()
+            assert h.hipEventElapsedTime(ctypes.byref(v), a, b) == 0
+            durs.append(v.value * 1e3)
+            h.hipEventDestroy(a)
+            h.hipEventDestroy(b)
+        durs.sort()
+        out[name] = {"avg_us": round(sum(durs) / len(durs), 3),
+                     "median_us": round(durs[len(durs) // 2], 3), "min_us": round(durs[0], 3),
+                     "launches": len(durs)}
+    return out
+
+
+def _graphs(step, first, n, chunk, stream):
+    """HIP graphs of at most `chunk` consecutive steps each, covering steps
+    first .. first + n - 1 in order."""
+    import torch
+    graphs = []
+    for j in range(first, first + n, chunk):
+        g = torch.cuda.CUDAGraph()
+        m = min(first + n, j + chunk) - j
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(j, j + m):
+                step(i)
+        graphs.append((g, m))
+    torch.cuda.synchronize()
+    return graphs
+
+
+def _replay_all(graphs, stream):
+    import torch
+    with torch.cuda.stream(stream):
+        for g, _ in graphs:
+            g.replay()
+    return sum(m for _, m in graphs)
+
+
+def _timed(step, warmup, steps, chunk, stream):
+    """Warm-up steps 0 .. warmup-1, then steps warmup .. warmup+steps-1 timed
+    with events on the stream; every step exactly once.  Returns (steps, ms)."""
+    import torch
+    wg = _graphs(step, 0, warmup, chunk, stream) if warmup else []
+    tg = _graphs(step, warmup, steps, chunk, stream)
+    _replay_all(wg, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    n = _replay_all(tg, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    del wg, tg
+    return n, e0.elapsed_time(e1)
+
+
+def _stack_layers(wl, dev, keep_host=False):
+    """30 layers of the stack workload resident on the device; with
+    keep_host, also their host copies (for the oracle)."""
+    import numpy as np
+    import torch
+
+    from bit_routed_expert_tf_amd import api
+    from synth import gen
+    d, E, k, f, fs = wl.d_model, wl.n_experts, wl.top_k, wl.d_ff, wl.d_ff_shared
+    stride = gen.blob_bytes(d, f)
+    t0 = time.time()
+    layers, host_layers = [], []
+    buf = torch.empty((E, stride), dtype=torch.uint8, pin_memory=True)
+    for l in range(wl.n_layers):
+        gen.expert_pool(wl.seed, l, d, f, E, out=buf.numpy(), threads=16)
+        router, sb = gen.router(wl.seed, l, d, E), gen.shared_blob(wl.seed, l, d, fs)
+        layers.append(api.DeviceLayer.from_arrays(router, sb, buf.to(dev), d, f, fs, k, device=dev))
+        if keep_host:
+            host_layers.append({"router": router, "shared_blob": sb, "pool": np.array(buf.numpy()),
+                                "d_model": d, "d_ff": f, "d_ff_shared": fs, "top_k": k})
+        if l % 10 == 9:
+            print(f"stack: {l + 1} layers resident ({time.time() - t0:.0f} s)", file=sys.stderr,
+                  flush=True)
+    return layers, host_layers, time.time() - t0
+
+
+def run_stack_batch(args, wl, layers, B, lib, dev, roofline):
+    """Batch-B decode steps through the resident stack: exactly args.warmup
+    warm-up steps, then exactly args.steps timed ones, each step on B tokens
+    of its own; then kernel durations on further steps."""
+    import numpy as np
+    import torch
+
+    from bit_routed_expert_tf_amd import _lib, api
+    from synth import gen
+    d, E, k, f, fs, L = wl.d_model, wl.n_experts, wl.top_k, wl.d_ff, wl.d_ff_shared, wl.n_layers
+    nprof = min(args.prof_steps, 200 if B == 1 else 60)
+    nstep = args.warmup + args.steps + nprof
+    ntok = nstep * B
+    X = torch.from_numpy(gen.tokens(wl.seed, ntok, d).view(np.int16)).to(dev)
+    ids_f = np.stack([gen.uniform_ids(wl.seed, l, ntok, E, k) for l in range(L)])
+    F = torch.from_numpy(ids_f).to(dev)
+    Y = torch.empty((L, B, d), dtype=torch.int16, device=dev)
+    IDS = torch.empty((L, B, k), dtype=torch.int32, device=dev)
+    W = torch.empty((L, B, k), dtype=torch.float32, device=dev)
+    ws = api.workspace(api.tf_moe_workspace_bytes(layers[0], B), dev)
+    stream = torch.cuda.Stream(device=dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    Ls = [ctypes.byref(D.struct) for D in layers]
+    xp, fp, yp, ip, wp = X.data_ptr(), F.data_ptr(), Y.data_ptr(), IDS.data_ptr(), W.data_ptr()
+    wsp, wsn = ctypes.c_void_p(ws.data_ptr()), ws.numel()
+
+    def step(i):
+        r0 = i * B
+        for l in range(L):
+            rc = lib.tf_moe_layer_fwd(
+                Ls[l], ctypes.c_void_p(xp + 2 * d * r0), B,
+                ctypes.c_void_p(fp + 4 * k * (l * ntok + r0)), ctypes.c_void_p(yp + 2 * d * B * l),
+                None, ctypes.c_void_p(ip + 4 * k * B * l), ctypes.c_void_p(wp + 4 * k * B * l),
+                None, 0, sh, sh, wsp, wsn)
+            if rc:
+                raise RuntimeError(lib.tf_last_error().decode())
+
+    steps, ms = _timed(step, args.warmup, args.steps, args.graph_chunk, stream)
+    after = range(args.warmup + args.steps, nstep)
+    blob = 2 * qmat_bytes(f, d) + qmat_bytes(d, f)
+    core = qmat_bytes(E, d, 8) + 2 * qmat_bytes(fs, d) + qmat_bytes(d, fs)
+    used = ids_f[:, args.warmup * B:(args.warmup + args.steps) * B].reshape(L, args.steps, B * k)
+    distinct = float(np.mean([[len(np.unique(r)) for r in lay] for lay in used]))
+    step_bytes = L * (core + distinct * blob + 4 * B * d)
+    if B == 1:
+        names = {_lib.TF_KERNEL_ROUTER_SHARED_GATEUP: "k_stage_a",
+                 _lib.TF_KERNEL_ROUTED_GATEUP_SHARED_DOWN: "k_stage_b",
+                 _lib.TF_KERNEL_DOWN_COMBINE: "k_stage_c1"}
+        gemv = {"k_stage_b": stage_b_bytes(d, f, fs, k)}
+    else:
+        names = {_lib.TF_KERNEL_ROUTER_SHARED_GATEUP: "k_stage_a",
+                 _lib.TF_KERNEL_PREFILL_GATEUP: "k_gu",
+                 _lib.TF_KERNEL_PREFILL_DOWN: "k_dn",
+                 _lib.TF_KERNEL_PREFILL_COMBINE: "k_pf_combine"}
+        gemv = {"k_gu": distinct * 2 * qmat_bytes(f, d) + 2 * qmat_bytes(fs, d),
+                "k_dn": distinct * qmat_bytes(d, f) + qmat_bytes(d, fs)}
+    kern = _profile(lib, _hip(), names, step, after, stream)
+    us = ms * 1e3 / steps
+    rf = {}
+    for name, kb in gemv.items():
+        dur = kern[name]["avg_us"] * 1e-6
+        rf[name] = {"bound": "hbm", "achieved": round(kb / dur / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": round(kb / dur / 1e9 / HBM_PEAK_GBPS, 4),
+                    "traffic": _traffic_for(f"{name}_batch{B}", wl.name),
+                    "algorithmic_bytes_per_launch": int(kb),
+                    "avg_duration_us": kern[name]["avg_us"]}
+    del X, F, Y, IDS, W, ws
+    torch.cuda.synchronize()
+    return {"tokens_per_s": round(B * steps / (ms / 1e3), 1), "steps": steps, "warmup": args.warmup,
+            "ms_per_step": round(ms / steps, 5), "us_per_layer": round(us / L, 3),
+            "distinct_experts_per_layer": round(distinct, 2), "step_bytes": int(step_bytes),
+            "GBps": round(step_bytes / (us * 1e-6) / 1e9, 1),
+            "frac_of_hbm_peak": round(step_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "roofline": rf[roofline], "gemv_kernels": rf, "kernels_per_layer": kern,
+            "kernel_timing": f"launch-attached fence-free events, {len(after)} eager steps after "
+                             f"the timed ones"}
+
+
+def run_stack(args):
+    """The headline: 30 resident layers, batch 1 (and batch 16 under its own
+    key), forced uniform routing."""
+    import torch
+
+    from bit_routed_expert_tf_amd import _lib
+    from synth import gen
+    wl = gen.WORKLOADS[4]
+    lib = _lib.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    layers, host_layers, setup = _stack_layers(wl, dev, keep_host=not args.no_cpu_baseline)
+    b1 = run_stack_batch(args, wl, layers, 1, lib, dev, "k_stage_b")
+    print(f"stack batch 1: {b1['tokens_per_s']} tokens/s", file=sys.stderr, flush=True)
+    out = {
+        "metric": METRIC, "value": b1["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": b1["steps"], "warmup": args.warmup, "ms_per_step": b1["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "data": "synthetic (seeded; random-init q4 weights of the stated shapes)",
+        "config": {"workload": wl.name, "layers": wl.n_layers, "tokens_per_step": 1,
+                   "d_model": wl.d_model, "n_experts": wl.n_experts, "top_k": wl.top_k,
+                   "d_ff": wl.d_ff, "d_ff_shared": wl.d_ff_shared,
+                   "routing": "uniform random forced ids, a fresh token per step",
+                   "weights": "affine q4 group 64 (fp16 scale/bias), 8-bit router",
+                   "io": "fp16 x/y, fp32 accumulate, fp64 router sums",
+                   "experts_resident": "all 30 x 128 in HBM", "graph_chunk": args.graph_chunk},
+        "roofline": dict(b1["roofline"], kernel="k_stage_b (routed gate/up + shared down)",
+                         timing=b1["kernel_timing"]),
+        "stack": {k: b1[k] for k in ("us_per_layer", "step_bytes", "GBps", "frac_of_hbm_peak",
+                                     "distinct_experts_per_layer")},
+        "kernels_per_layer": b1["kernels_per_layer"],
+        "device": torch.cuda.get_device_name(dev), "setup_s": round(setup, 1),
+    }
+    if not args.headline_only:
+        out["batch16"] = run_stack_batch(args, wl, layers, 16, lib, dev, "k_gu")
+        print(f"stack batch 16: {out['batch16']['tokens_per_s']} tokens/s", file=sys.stderr,
+              flush=True)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_stack(args, wl, host_layers)
+    del layers
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if not args.headline_only:
+        out["decode_layer"] = run_decode(args)
+    return out
 
 
 def run_decode(args):
+    """The single-layer decode workload (decode-layer-d2816-e128k8): one
+    layer, all 128 experts resident, natural routing, one token per step."""
     import numpy as np
     import torch
 
@@ -104,24 +336,16 @@ def run_decode(args):
 
     wl = gen.WORKLOADS[1]
     d, E, k, f, fs = wl.d_model, wl.n_experts, wl.top_k, wl.d_ff, wl.d_ff_shared
-    n_tok = wl.n_tokens
     lib = _lib.load()
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-
-    t0 = time.time()
-    router = gen.router(wl.seed, 0, d, E)
-    shared_blob = gen.shared_blob(wl.seed, 0, d, fs)
-    pool = gen.expert_pool(wl.seed, 0, d, f, E)
-    X = gen.tokens(wl.seed, n_tok, d)
-    D = api.DeviceLayer.from_arrays(router, shared_blob, pool, d, f, fs, k, device=dev)
-    Xd = torch.from_numpy(X.view(np.int16)).to(dev)
-    Y = torch.empty((n_tok, d), dtype=torch.int16, device=dev)
-    IDS = torch.empty((n_tok, k), dtype=torch.int32, device=dev)
-    W = torch.empty((n_tok, k), dtype=torch.float32, device=dev)
+    D = api.DeviceLayer.from_arrays(gen.router(wl.seed, 0, d, E), gen.shared_blob(wl.seed, 0, d, fs),
+                                    gen.expert_pool(wl.seed, 0, d, f, E, threads=16), d, f, fs, k,
+                                    device=dev)
+    Xd = torch.from_numpy(gen.tokens(wl.seed, wl.n_tokens, d).view(np.int16)).to(dev)
+    Y = torch.empty((wl.n_tokens, d), dtype=torch.int16, device=dev)
+    IDS = torch.empty((wl.n_tokens, k), dtype=torch.int32, device=dev)
+    W = torch.empty((wl.n_tokens, k), dtype=torch.float32, device=dev)
     ws = api.workspace(api.tf_moe_workspace_bytes(D, 1), dev)
-    setup_s = time.time() - t0
-
     stream = torch.cuda.Stream(device=dev)
     sh = ctypes.c_void_p(stream.cuda_stream)
     Lp = ctypes.byref(D.struct)
@@ -136,195 +360,63 @@ def run_decode(args):
         if rc:
             raise RuntimeError(lib.tf_last_error().decode())
 
-    with torch.cuda.stream(stream):
-        for i in range(8):
-            step(i)
-    torch.cuda.synchronize()
-
-    chunk = args.graph_chunk
-    n_graphs = (n_tok + chunk - 1) // chunk
-    graphs = []
-    for j in range(n_graphs):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for i in range(j * chunk, min(n_tok, (j + 1) * chunk)):
-                step(i)
-        graphs.append(g)
-    torch.cuda.synchronize()
-
-    def run_steps(nsteps):
-        done, j = 0, 0
-        with torch.cuda.stream(stream):
-            while done < nsteps:
-                graphs[j % n_graphs].replay()
-                done += min(chunk, n_tok - (j % n_graphs) * chunk)
-                j += 1
-        return done
-
-    run_steps(args.warmup)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    w0 = time.perf_counter()
-    e0.record(stream)
-    steps = run_steps(args.steps)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ms = e0.elapsed_time(e1)
+    nprof = min(args.prof_steps, 200)
+    steps_t = max(1, min(args.steps, wl.n_tokens - args.warmup - nprof))
+    steps, ms = _timed(step, args.warmup, steps_t, args.graph_chunk, stream)
+    after = range(args.warmup + steps, args.warmup + steps + nprof)
+    kern = _profile(lib, _hip(), {_lib.TF_KERNEL_ROUTER_SHARED_GATEUP: "k_stage_a",
+                                  _lib.TF_KERNEL_ROUTED_GATEUP_SHARED_DOWN: "k_stage_b",
+                                  _lib.TF_KERNEL_DOWN_COMBINE: "k_stage_c1"}, step, after, stream)
     tok_s = steps / (ms / 1e3)
-
-    # Per-kernel durations: eager steps whose kernels are launched through
-    # hipExtLaunchKernel with start/stop events on the compute stream.
-    h = _hip()
-    kern = {}
-    names = {_lib.TF_KERNEL_ROUTER_SHARED_GATEUP: "router_shared_gateup",
-             _lib.TF_KERNEL_ROUTED_GATEUP_SHARED_DOWN: "routed_gateup_shared_down",
-             _lib.TF_KERNEL_DOWN_COMBINE: "down_combine"}
-    nprof = args.prof_steps
-    for kid, name in names.items():
-        evs = [(_event(h), _event(h)) for _ in range(nprof)]
-        with torch.cuda.stream(stream):
-            for i in range(nprof):
-                _lib.check(lib.tf_profile_kernel(kid, evs[i][0], evs[i][1]))
-                step((i * 37) % n_tok)
-        torch.cuda.synchronize()
-        durs = []
-        for a, b in evs:
-            v = ctypes.c_float()
-            h.hipEventElapsedTime(ctypes.byref(v), a, b)
-            durs.append(v.value * 1e3)
-            h.hipEventDestroy(a)
-            h.hipEventDestroy(b)
-        durs.sort()
-        kern[name] = {"avg_us": sum(durs) / len(durs), "median_us": durs[len(durs) // 2],
-                      "min_us": durs[0], "launches": len(durs)}
-
-    bytes_b = stage_b_bytes(d, f, fs, k)
-    dur_b = kern["routed_gateup_shared_down"]["avg_us"] * 1e-6
-    achieved = bytes_b / dur_b / 1e9
+    bb = stage_b_bytes(d, f, fs, k)
+    dur = kern["k_stage_b"]["avg_us"] * 1e-6
     lb = layer_bytes(d, f, fs, E, k)
-    traffic = _traffic_for("routed_gateup_shared_down", wl.name)
-
-    out = {
-        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": steps, "warmup": args.warmup, "ms_per_step": ms / steps,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
-        "data": "synthetic (seeded; random-init q4 weights of the stated shapes)",
-        "config": {"workload": wl.name, "d_model": d, "n_experts": E, "top_k": k, "d_ff": f,
-                   "d_ff_shared": fs, "tokens": n_tok, "tokens_per_step": 1,
-                   "weights": "affine q4 group 64 (fp16 scale/bias), 8-bit router",
-                   "io": "fp16 x/y, fp32 accumulate, fp64 router sums",
-                   "experts_resident": "all 128 in HBM", "graph_chunk": chunk},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "kernel": "routed_gateup_shared_down",
-                     "algorithmic_bytes_per_launch": bytes_b,
-                     "avg_duration_us": round(dur_b * 1e6, 3)},
-        "layer": {"bytes_per_token": lb, "GBps": round(lb * tok_s / 1e9, 1),
-                  "frac_of_hbm_peak": round(lb * tok_s / 1e9 / HBM_PEAK_GBPS, 4),
-                  "wall_s": round(wall, 4), "setup_s": round(setup_s, 1)},
-        "kernels": {n: {kk: round(v, 3) if isinstance(v, float) else v for kk, v in r.items()}
-                    for n, r in kern.items()},
-        "device": torch.cuda.get_device_name(dev),
-    }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args, router, shared_blob, pool, X, wl)
-    return out
+    return {"workload": wl.name, "tokens_per_s": round(tok_s, 1), "steps": steps,
+            "warmup": args.warmup, "us_per_token": round(ms * 1e3 / steps, 3),
+            "roofline": {"bound": "hbm", "achieved": round(bb / dur / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(bb / dur / 1e9 / HBM_PEAK_GBPS, 4),
+                         "traffic": _traffic_for("k_stage_b_decode_layer", wl.name),
+                         "kernel": "k_stage_b", "algorithmic_bytes_per_launch": bb,
+                         "avg_duration_us": kern["k_stage_b"]["avg_us"]},
+            "layer": {"bytes_per_token": lb, "GBps": round(lb * tok_s / 1e9, 1),
+                      "frac_of_hbm_peak": round(lb * tok_s / 1e9 / HBM_PEAK_GBPS, 4),
+                      "note": "one layer's 441.6 MB working set partly fits the 256 MB "
+                              "Infinity Cache, so these GB/s are not all DRAM bytes"},
+            "kernels": kern}
 
 
-def cpu_baseline(args, router, shared_blob, pool, X, wl):
-    """The fp64 oracle, as it stands, on the host cores over a bounded sample
-    of the same tokens."""
+def cpu_baseline_stack(args, wl, host_layers):
+    """The fp64 oracle, as it stands, on the host cores: whole steps of the
+    headline workload (one token through all 30 layers, the same forced ids)
+    over a bounded sample, timed on all cores and on one."""
+    import numpy as np
+
     import oracle
-    L = {"router": router, "shared_blob": shared_blob, "pool": pool, "d_model": wl.d_model,
-         "d_ff": wl.d_ff, "d_ff_shared": wl.d_ff_shared, "top_k": wl.top_k}
-    oracle.moe_token(L, X[0])             # load / first-touch
-    n, t0 = 0, time.perf_counter()
-    while n < 8 or (time.perf_counter() - t0 < args.cpu_seconds and n < wl.n_tokens):
-        oracle.moe_token(L, X[n])
-        n += 1
-    dt = time.perf_counter() - t0
+    from synth import gen
+    L, d, E, k = wl.n_layers, wl.d_model, wl.n_experts, wl.top_k
+    nmax = 200
+    X = gen.tokens(wl.seed, nmax, d)
+    F = np.stack([gen.uniform_ids(wl.seed, l, nmax, E, k) for l in range(L)])
+
+    def run(seconds, least):
+        n, t0 = 0, time.perf_counter()
+        while n < least or (time.perf_counter() - t0 < seconds and n < nmax):
+            for l in range(L):
+                oracle.moe_token(host_layers[l], X[n], F[l, n])
+            n += 1
+        return n, time.perf_counter() - t0
+
+    oracle.moe_token(host_layers[0], X[0], F[0, 0])    # load / first touch
+    n, dt = run(args.cpu_seconds, 2)
     cores = oracle.num_threads()
-    # the same oracle on one core, over a shorter sample
     oracle.set_num_threads(1)
-    n1, t1 = 0, time.perf_counter()
-    while n1 < 2 or (time.perf_counter() - t1 < args.cpu_seconds / 4 and n1 < wl.n_tokens):
-        oracle.moe_token(L, X[n1])
-        n1 += 1
-    dt1 = time.perf_counter() - t1
+    n1, dt1 = run(args.cpu_seconds / 4, 1)
     oracle.set_num_threads(cores)
-    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"first {n} of the {wl.n_tokens} workload tokens, one at a time "
-                      f"({dt:.1f} s, C fp64 oracle, OpenMP over rows)",
-            "one_core": {"value": round(n1 / dt1, 3), "unit": "tokens/s", "cores": 1,
-                         "sample": f"first {n1} tokens ({dt1:.1f} s)"}}
-
-
-def _profile(lib, h, kernels, step, nprof, stream):
-    """Average durations of the named kernels (hipExtLaunchKernel start/stop
-    events on the compute stream) over nprof eager calls of step(i)."""
-    import torch
-
-    from bit_routed_expert_tf_amd import _lib
-    out = {}
-    for kid, name in kernels.items():
-        evs = [(_event(h), _event(h)) for _ in range(nprof)]
-        with torch.cuda.stream(stream):
-            for i in range(nprof):
-                _lib.check(lib.tf_profile_kernel(kid, evs[i][0], evs[i][1]))
-                step(i)
-        torch.cuda.synchronize()
-        durs = []
-        for a, b in evs:
-            v = ctypes.c_float()
-            h.hipEventElapsedTime(ctypes.byref(v), a, b)
-            durs.append(v.value * 1e3)
-            h.hipEventDestroy(a)
-            h.hipEventDestroy(b)
-        durs.sort()
-        out[name] = {"avg_us": round(sum(durs) / len(durs), 3),
-                     "median_us": round(durs[len(durs) // 2], 3), "min_us": round(durs[0], 3),
-                     "launches": len(durs)}
-    return out
-
-
-def _graphs(step, n, chunk, stream):
-    """HIP graphs of `chunk` consecutive steps each, covering steps 0..n-1."""
-    import torch
-    graphs = []
-    for j in range(0, n, chunk):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for i in range(j, min(n, j + chunk)):
-                step(i)
-        graphs.append((g, min(n, j + chunk) - j))
-    torch.cuda.synchronize()
-    return graphs
-
-
-def _replay(graphs, nsteps, stream):
-    import torch
-    done, j = 0, 0
-    with torch.cuda.stream(stream):
-        while done < nsteps:
-            g, c = graphs[j % len(graphs)]
-            g.replay()
-            done += c
-            j += 1
-    return done
-
-
-def _timed(graphs, nsteps, warmup, stream):
-    import torch
-    _replay(graphs, warmup, stream)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    steps = _replay(graphs, nsteps, stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return steps, e0.elapsed_time(e1)
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"the first {n} steps of the workload (one token through all {L} layers "
+                      f"each, {dt:.1f} s; C fp64 oracle, OpenMP over rows)",
+            "one_core": {"value": round(n1 / dt1, 4), "unit": "tokens/s", "cores": 1,
+                         "sample": f"the first {n1} steps ({dt1:.1f} s)"}}
 
 
 def run_prefill(args):
@@ -360,11 +452,7 @@ def run_prefill(args):
             ctypes.c_void_p(W.data_ptr() + 4 * k * C * j), sh, ctypes.c_void_p(ws.data_ptr()),
             ws.numel()))
 
-    with torch.cuda.stream(stream):
-        step(0)
-    torch.cuda.synchronize()
-    graphs = _graphs(step, nch, nch, stream)
-    steps, ms = _timed(graphs, args.steps or nch, nch, stream)
+    steps, ms = _timed(step, args.warmup, args.steps, args.graph_chunk, stream)
     ids = IDS.cpu().numpy().reshape(nch, C * k)
     distinct = float(np.mean([len(np.unique(r)) for r in ids]))
     qb = lambda n, kk, bits=4: n * kk * bits // 8 + 4 * n * (kk // 64)   # noqa: E731
@@ -374,7 +462,7 @@ def run_prefill(args):
         _lib.TF_KERNEL_ROUTER_SHARED_GATEUP: "router_topk_group",
         _lib.TF_KERNEL_PREFILL_GATEUP: "gateup_mfma",
         _lib.TF_KERNEL_PREFILL_DOWN: "down_mfma",
-        _lib.TF_KERNEL_PREFILL_COMBINE: "combine"}, step, min(args.prof_steps, 64), stream)
+        _lib.TF_KERNEL_PREFILL_COMBINE: "combine"}, step, range(min(args.prof_steps, 64)), stream)
     us = ms * 1e3 / steps
     return {"metric": "prefill tokens/s (128-token chunks, one layer)",
             "value": round(C * steps / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
@@ -386,101 +474,6 @@ def run_prefill(args):
             "GBps": round(chunk_bytes / (us * 1e-6) / 1e9, 1),
             "frac_of_hbm_peak": round(chunk_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
             "kernels": kern}
-
-
-def run_stack(args):
-    """30 resident layers, batch 1 and 16 independent tokens per step, forced
-    uniform routing; every layer of a step consumes the step's x."""
-    import numpy as np
-    import torch
-
-    from bit_routed_expert_tf_amd import _lib, api
-    from synth import gen
-    wl = gen.WORKLOADS[4]
-    d, E, k, f, fs, L = wl.d_model, wl.n_experts, wl.top_k, wl.d_ff, wl.d_ff_shared, wl.n_layers
-    nsteps = args.steps or wl.n_tokens
-    warm = wl.extra.get("warmup_steps", 50)
-    lib = _lib.load()
-    dev = torch.device("cuda:0")
-    t0 = time.time()
-    stride = gen.blob_bytes(d, f)
-    layers = []
-    host = torch.empty((E, stride), dtype=torch.uint8, pin_memory=True)
-    for l in range(L):
-        gen.expert_pool(wl.seed, l, d, f, E, out=host.numpy(), threads=16)
-        pool = host.to(dev, non_blocking=False)
-        layers.append(api.DeviceLayer.from_arrays(gen.router(wl.seed, l, d, E),
-                                                  gen.shared_blob(wl.seed, l, d, fs), pool,
-                                                  d, f, fs, k, device=dev))
-        print(f"stack: layer {l} resident ({time.time() - t0:.0f} s)", file=sys.stderr, flush=True)
-    setup = time.time() - t0
-    res = {}
-    for B in wl.batches:
-        ntok = (nsteps + warm) * B
-        X = torch.from_numpy(gen.tokens(wl.seed, ntok, d).view(np.int16)).to(dev)
-        ids_f = np.stack([gen.uniform_ids(wl.seed, l, ntok, E, k) for l in range(L)])
-        F = torch.from_numpy(ids_f).to(dev)
-        Y = torch.empty((L, B, d), dtype=torch.int16, device=dev)
-        IDS = torch.empty((L, B, k), dtype=torch.int32, device=dev)
-        W = torch.empty((L, B, k), dtype=torch.float32, device=dev)
-        ws = api.workspace(api.tf_moe_workspace_bytes(layers[0], B), dev)
-        stream = torch.cuda.Stream(device=dev)
-        sh = ctypes.c_void_p(stream.cuda_stream)
-        Ls = [ctypes.byref(D.struct) for D in layers]
-
-        def step(i, B=B, X=X, F=F, Y=Y, IDS=IDS, W=W, ws=ws, sh=sh, Ls=Ls, ntok=ntok):
-            r0 = (i % (ntok // B)) * B
-            for l in range(L):
-                _lib.check(lib.tf_moe_layer_fwd(
-                    Ls[l], ctypes.c_void_p(X.data_ptr() + 2 * d * r0), B,
-                    ctypes.c_void_p(F.data_ptr() + 4 * k * (l * ntok + r0)),
-                    ctypes.c_void_p(Y.data_ptr() + 2 * d * B * l), None,
-                    ctypes.c_void_p(IDS.data_ptr() + 4 * k * B * l),
-                    ctypes.c_void_p(W.data_ptr() + 4 * k * B * l), None, 0, sh, sh,
-                    ctypes.c_void_p(ws.data_ptr()), ws.numel()))
-
-        with torch.cuda.stream(stream):
-            step(0)
-        torch.cuda.synchronize()
-        graphs = _graphs(step, nsteps + warm, 50, stream)
-        steps, ms = _timed(graphs, nsteps, warm, stream)
-        # algorithmic bytes: per layer router + shared + distinct experts of the step
-        qb = lambda n, kk, bits=4: n * kk * bits // 8 + 4 * n * (kk // 64)   # noqa: E731
-        blob = 2 * qb(f, d) + qb(d, f)
-        core = qb(E, d, 8) + 2 * qb(fs, d) + qb(d, fs)
-        rows = ids_f[:, :(nsteps + warm) * B].reshape(L, nsteps + warm, B * k)
-        distinct = float(np.mean([[len(np.unique(r)) for r in lay] for lay in rows]))
-        step_bytes = L * (core + distinct * blob + 4 * B * d)
-        nexp = B * k if B * k < distinct else distinct
-        if B == 1:   # decode kernels A, B, C; B = routed gate/up + shared down
-            names = {_lib.TF_KERNEL_ROUTER_SHARED_GATEUP: "router_shared_gateup",
-                     _lib.TF_KERNEL_ROUTED_GATEUP_SHARED_DOWN: "routed_gateup_shared_down",
-                     _lib.TF_KERNEL_DOWN_COMBINE: "down_combine"}
-            gemv = {"routed_gateup_shared_down": nexp * 2 * qb(f, d) + qb(d, fs)}
-        else:        # grouped step: router + grouping, gate/up, down, combine
-            names = {_lib.TF_KERNEL_ROUTER_SHARED_GATEUP: "router_topk_group",
-                     _lib.TF_KERNEL_PREFILL_GATEUP: "gateup_mfma",
-                     _lib.TF_KERNEL_PREFILL_DOWN: "down_mfma",
-                     _lib.TF_KERNEL_PREFILL_COMBINE: "combine"}
-            gemv = {"gateup_mfma": nexp * 2 * qb(f, d) + 2 * qb(fs, d),
-                    "down_mfma": nexp * qb(d, f) + qb(d, fs)}
-        kern = _profile(lib, _hip(), names, step, min(args.prof_steps, 100), stream)
-        us = ms * 1e3 / steps
-        gk = {}
-        for name, kb in gemv.items():
-            dur = kern[name]["avg_us"] * 1e-6
-            gk[name] = {"bytes_per_launch": int(kb), "GBps": round(kb / dur / 1e9, 1),
-                        "frac": round(kb / dur / 1e9 / HBM_PEAK_GBPS, 4)}
-        res[f"batch{B}"] = {
-            "tokens_per_s": round(B * steps / (ms / 1e3), 1), "us_per_step": round(us, 2),
-            "distinct_experts_per_layer": round(distinct, 2), "step_bytes": int(step_bytes),
-            "GBps": round(step_bytes / (us * 1e-6) / 1e9, 1),
-            "frac_of_hbm_peak": round(step_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-            "gemv_kernels": gk, "kernels_per_layer": kern}
-        del X, F, Y, IDS, W, ws, graphs
-        torch.cuda.synchronize()
-    return {"metric": "30-layer resident MoE stack decode tokens/s", "workload": wl.name,
-            "setup_s": round(setup, 1), "steps": nsteps, "warmup": warm, "results": res}
 
 
 def run_slot(args):
@@ -623,15 +616,10 @@ def run_sample(args):
                                      ctypes.c_void_p(ids.data_ptr() + 4 * T * j),
                                      ctypes.c_void_p(ws.data_ptr()), ws.numel(), sh))
 
-        with torch.cuda.stream(stream):
-            step(0)
-        torch.cuda.synchronize()
-        n = args.steps or 2000
-        graphs = _graphs(step, nrow, nrow, stream)
-        steps, ms = _timed(graphs, n, min(args.warmup, n), stream)
+        steps, ms = _timed(step, args.warmup, args.steps, args.graph_chunk, stream)
         kern = _profile(lib, _hip(), {_lib.TF_KERNEL_SAMPLE_PART: "k_sample_part",
                                       _lib.TF_KERNEL_SAMPLE_FINAL: "k_sample_final"}, step,
-                        min(args.prof_steps, 200), stream)
+                        range(min(args.prof_steps, 200)), stream)
         us = ms * 1e3 / steps
         kus = kern["k_sample_part"]["avg_us"]
         nbytes = 4 * V * T   # the logits, read once by the slice kernel
@@ -684,14 +672,10 @@ def run_attn(args):
                 ctypes.c_void_p(vc.data_ptr()), H, G, D, S, pos, ring, 1.0 / D ** 0.5,
                 ctypes.c_void_p(O[j].data_ptr()), ctypes.c_void_p(ws.data_ptr()), ws.numel(), sh))
 
-        with torch.cuda.stream(stream):
-            step(0)
-        torch.cuda.synchronize()
-        graphs = _graphs(step, nq, nq, stream)
-        steps, ms = _timed(graphs, args.steps or 4000, min(args.warmup, 1000), stream)
+        steps, ms = _timed(step, args.warmup, args.steps, args.graph_chunk, stream)
         kern = _profile(lib, _hip(), {_lib.TF_KERNEL_ATTN_CHUNK: "k_attn_chunk",
                                       _lib.TF_KERNEL_ATTN_COMBINE: "k_attn_combine"}, step,
-                        min(args.prof_steps, 200), stream)
+                        range(min(args.prof_steps, 200)), stream)
         seen = min(pos + 1, S)
         nbytes = 2 * G * seen * D * 2   # keys and values the token sees, read once
         kus = kern["k_attn_chunk"]["avg_us"]
@@ -706,42 +690,53 @@ def run_attn(args):
     return out
 
 
+# steps and warm-up steps of each workload when the flags are not given
+DEFAULT_STEPS = {"stack": (1000, 50), "decode": (1000, 50), "prefill": (64, 64),
+                 "slot-cache": (2048, 0), "sample": (2000, 200), "attn": (4000, 1000)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10000)
-    ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--graph-chunk", type=int, default=250)
-    ap.add_argument("--prof-steps", type=int, default=300)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: the workload's own count; 1000 for the stack)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps before them (default 50 for the stack)")
+    ap.add_argument("--graph-chunk", type=int, default=25, help="steps per HIP graph")
+    ap.add_argument("--prof-steps", type=int, default=200,
+                    help="eager steps whose kernels are timed, after the timed region")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="first run plain 256 MiB device copies (memory-counter calibration)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="stack workload: batch 1 only (no batch 16, no single-layer decode)")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="first run a 256 MiB read-only reduction and a 256 MiB fill "
+                         "(memory-counter calibration)")
     ap.add_argument("--prefetch", action="store_true",
                     help="slot-cache workload: also run with the next layer's experts "
                          "prefetched (exact predictions, and half of them wrong)")
     ap.add_argument("--slot-sweep", action="store_true",
                     help="slot-cache workload: also run 8, 16 and 32 slots under LFU and LRU")
-    ap.add_argument("--workload", choices=["decode", "prefill", "stack", "slot-cache", "sample",
-                                           "attn"],
-                    default="decode",
-                    help="decode (default, the headline line); the others measure the "
-                         "prefill chunk, the 30-layer resident stack, the slot-cache stack "
-                         "next-token sampling and decode attention")
+    ap.add_argument("--workload", choices=list(DEFAULT_STEPS), default="stack",
+                    help="stack (default, the headline line: 30 resident layers); decode (one "
+                         "layer); prefill (128-token chunks); slot-cache; sample; attn")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this hot path is built and measured on a single "
               "MI355X (the multi-GPU design is expert sharding, not implemented here).",
               file=sys.stderr)
         sys.exit(2)
-    if args.copy_calibration:
-        copy_calibration()
+    ds, dw = DEFAULT_STEPS[args.workload]
+    args.steps = ds if args.steps is None else args.steps
+    args.warmup = dw if args.warmup is None else args.warmup
+    if args.steps < 1 or args.warmup < 0:
+        sys.exit("--steps must be >= 1 and --warmup >= 0")
+    if args.calibrate:
+        calibration()
     if args.workload == "decode":
         out = run_decode(args)
     else:
-        if "--steps" not in sys.argv:
-            args.steps = 0   # the workload's own count
-        out = {"prefill": run_prefill, "stack": run_stack, "slot-cache": run_slot,
+        out = {"stack": run_stack, "prefill": run_prefill, "slot-cache": run_slot,
                "sample": run_sample, "attn": run_attn}[args.workload](args)
     print(json.dumps(out), flush=True)
 

@@ -41,6 +41,9 @@
  *   except tf_slot_cache_create.
  * - Workspaces must be zero-filled before first use (tf_workspace_zero);
  *   the library leaves its counters at zero after every completed call.
+ *   Counters sit at fixed offsets at the start of a workspace, apart from
+ *   the data, so one workspace may serve calls of any token count and any
+ *   layer whose workspace size it covers.
  */
 #ifndef TF_H
 #define TF_H
@@ -82,10 +85,21 @@ typedef struct {
     int32_t n, k, bits, group;   /* bits 4 or 8, group 64, k % 64 == 0 */
 } tf_qmat;
 
-/* Size in bytes of one expert blob (host-only arithmetic). */
+/* Size in bytes of one expert blob (host-only arithmetic): gate, up and down
+ * as MLX affine 4-bit matrices with group 64 and one fp16 scale and bias per
+ * group (shilu.ai README translation, "概览" table: 4-bit shared and routed
+ * experts, group 64).  The blob is the unit the expert cache moves; at the
+ * study's shapes 30 x 128 blobs plus the resident core come to about the
+ * installed size the pages give (blog.hypho.cn review, "它省的不是模型大小":
+ * 14.3 GB installed, 1.35 GB resident shared weights).  Returns 0 when
+ * d_model or d_ff is not a positive multiple of 64. */
 size_t tf_expert_blob_bytes(int32_t d_model, int32_t d_ff);
 
-/* Split a blob into its three matrix views (host-only pointer arithmetic). */
+/* Split a blob into its three matrix views (host-only pointer arithmetic; the
+ * same section layout as tf_expert_blob_bytes).  blob: any pointer, not
+ * dereferenced; gate/up/down: caller-owned structs, filled.  TF_E_ARG on a
+ * NULL argument, TF_E_SHAPE when d_model or d_ff is not a positive multiple
+ * of 64. */
 tf_status tf_expert_view(const uint8_t *blob, int32_t d_model, int32_t d_ff,
                          tf_qmat *gate, tf_qmat *up, tf_qmat *down);
 
@@ -98,6 +112,13 @@ tf_status tf_workspace_flags(void *ws, int32_t *flags_host, hipStream_t s);
 /* ---------------------------------------------------------------- router */
 /* Router matvec (8-bit affine, products exact in fp32, sums in fp64), then
  * top-k by (logit desc, id asc) and softmax over the k selected logits.
+ * The pages: an 8-bit router (shilu.ai README translation, "概览" table)
+ * computed on the GPU from resident weights at every layer, whose top-8
+ * expert ids the runtime then plans against the layer's expert cache
+ * (same page, "推理引擎的工作原理"; blog.hypho.cn review,
+ * "它省的不是模型大小": 128 routed experts, 8 chosen per token).  Softmax
+ * scope (the k selected logits) and the tie rule (lower id first) are
+ * readings; the pages do not state them.
  *   router     : 8-bit tf_qmat [n_experts][d_model]
  *   x          : fp16 [T][d_model]
  *   forced_ids : NULL, or int32 [T][top_k] ids to use instead of the top-k
@@ -115,7 +136,11 @@ tf_status tf_router_topk(const tf_qmat *router, const uint16_t *x, int32_t T,
                          hipStream_t s);
 
 /* ------------------------------------------------------ expert q4 GEMV */
-/* For each pair p (0 <= p < P):
+/* The routed expert's fused dequantise-and-multiply: gate and up GEMVs over
+ * MLX affine 4-bit weights (group 64, per-group fp16 scale and bias), the
+ * activation, then the down GEMV (sh.edu-sjtu.cn article, "三件事": 4-bit
+ * experts with group-64 scaling; shilu.ai README translation, "状态和范围":
+ * custom quantised-GEMV and MoE kernels).  For each pair p (0 <= p < P):
  *     y32[token[p]] += coef[p] * expert(pool + slot[p]*blob_stride)(x[token[p]])
  * token[] must be non-decreasing (pairs grouped by token); each token's pairs
  * are summed in pair order, so the result is deterministic.  token == NULL
@@ -145,7 +170,14 @@ typedef struct {
 /* Workspace for tf_moe_layer_fwd with up to T tokens. */
 size_t tf_moe_workspace_bytes(const tf_moe_layer *L, int32_t T);
 
-/* Decode step: T (1..16) independent tokens through one layer.
+/* Decode step: T (1..16) independent tokens through one layer, in the order
+ * the pages give for each layer (shilu.ai README translation,
+ * "推理引擎的工作原理"): the router from resident weights, its top-8 planned
+ * against the layer's 16-slot LFU cache, missed experts read in while the
+ * resident shared-expert branch runs, then the shared and routed outputs
+ * combined (blog.hypho.cn review, "它省的不是模型大小": 128 routed experts,
+ * top-8, a dense shared expert).  The combine weights (router softmax, shared
+ * branch at weight 1) are the study's layer definition, not the pages'.
  *   x [T][d_model] fp16 in; y [T][d_model] fp16 out; y32 NULL or fp32 out.
  *   ids/weights [T][top_k] out (rank order).
  *   forced_ids NULL or [T][top_k] (see tf_router_topk).
@@ -163,8 +195,15 @@ tf_status tf_moe_layer_fwd(const tf_moe_layer *L, const uint16_t *x, int32_t T,
                            void *ws, size_t ws_bytes);
 
 /* Prefill: one chunk of T (1..128) tokens through one layer, all experts
- * resident.  Tokens are grouped by expert so that each expert's weights are
- * read once per chunk.  Same outputs as T single-token calls (ids bitwise,
+ * resident (shilu.ai README translation, "推理引擎的工作原理": prompt prefill
+ * in chunks of at most 128 tokens, so that one fetched expert serves several
+ * rows).  Tokens are grouped by expert so that each expert's weights are
+ * read once per chunk.  x [T][d_model] fp16; y [T][d_model] fp16 out; y32
+ * NULL or fp32 [T][d_model] out; ids/weights [T][top_k] out, rank order.
+ * ws: tf_prefill_workspace_bytes(L, T) bytes, 256-B aligned, zero-filled
+ * before first use.  TF_E_ARG for T outside [0, 128] or a NULL pointer,
+ * TF_E_ALIGN, TF_E_NOMEM for a short workspace, TF_E_SHAPE as in
+ * tf_moe_layer_fwd; T == 0 enqueues nothing.  Same outputs as T single-token calls (ids bitwise,
  * y within fp32 rounding). */
 size_t tf_prefill_workspace_bytes(const tf_moe_layer *L, int32_t T);
 tf_status tf_moe_prefill_chunk(const tf_moe_layer *L, const uint16_t *x, int32_t T,
@@ -262,7 +301,10 @@ enum {
  * kernel goes through hipExtLaunchKernel with `start` recorded when the
  * kernel begins and `stop` when it ends, on the stream it runs on.  Events
  * must be created with timing enabled; hipEventElapsedTime(start, stop) is
- * then the kernel's own duration.  Pass kernel 0 to disarm. */
+ * then the kernel's own duration.  Create them with hipEventDisableSystemFence:
+ * a default event's system-scope cache write-back and invalidate slows the
+ * timed kernel (measured: 10.3 against 8.5 us for the routed decode kernel).
+ * Pass kernel 0 to disarm. */
 tf_status tf_profile_kernel(int32_t kernel, hipEvent_t start, hipEvent_t stop);
 
 /* ------------------------------------------------------------ slot cache */

@@ -2,16 +2,17 @@
 
 Two counter passes over the same command (``--pmc FETCH_SIZE`` and
 ``--pmc WRITE_SIZE``, both in KiB per dispatch) are scaled by what the same
-counters read for a plain device copy of known size in that run (bench.py
---copy-calibration copies 256 MiB), so the result is in bytes of HBM
-traffic.  Usage:
+counters read, in that run, for kernels of known traffic: ``bench.py
+--calibrate`` first runs a read-only reduction over 256 MiB (torch ``sum``,
+16-byte loads per lane, like the GEMVs' code loads) and a write-only fill of
+256 MiB.  The result is in bytes of HBM traffic.  Usage:
 
-    python3 -m bit_routed_expert_tf_amd.profiling traffic \\
-        --fetch F.csv --write W.csv --kernel k_stage_b \\
-        --name routed_gateup_shared_down --workload decode-layer-d2816-e128k8
+    python3 profiling.py traffic --fetch F.csv --write W.csv --kernel k_stage_b \\
+        --name routed_gateup_shared_down --workload resident-stack-30L-e128k8-uniform
 
 prints a Markdown summary and records the figure in profiles/traffic.json,
-keyed by kernel name, with the hash of the kernel sources it was taken on.
+keyed by name, with the hash of the kernel sources it was taken on (bench.py
+reports it only while that hash still matches).
 """
 import argparse
 import csv
@@ -20,9 +21,9 @@ import json
 import os
 import sys
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "bit_routed_expert_tf_amd", "csrc")
-COPY_BYTES = 256 << 20
+CAL_BYTES = 256 << 20
 # device sources each measured kernel is built from
 SOURCES = {
     "k_stage": ["tf_decode.hip", "tf_device.h", "tf_layer.h", "tf_internal.h"],
@@ -50,23 +51,25 @@ def _per_dispatch(path, counter, match):
 
 
 def traffic(args):
-    is_copy = lambda n: "copyBuffer" in n   # noqa: E731
-    is_kern = lambda n: args.kernel in n    # noqa: E731
+    is_read = lambda n: "reduce_kernel" in n   # noqa: E731  torch sum: reads CAL_BYTES
+    is_fill = lambda n: "FillFunctor" in n     # noqa: E731  torch fill_: writes CAL_BYTES
+    is_kern = lambda n: args.kernel in n       # noqa: E731
     kf = _per_dispatch(args.fetch, "FETCH_SIZE", is_kern)
     kw = _per_dispatch(args.write, "WRITE_SIZE", is_kern)
-    cf = _per_dispatch(args.fetch, "FETCH_SIZE", is_copy)
-    cw = _per_dispatch(args.write, "WRITE_SIZE", is_copy)
+    cf = _per_dispatch(args.fetch, "FETCH_SIZE", is_read)
+    cw = _per_dispatch(args.write, "WRITE_SIZE", is_fill)
     if not (kf and kw and cf and cw):
-        sys.exit("missing dispatches: kernel %d/%d, copy %d/%d" % (len(kf), len(kw), len(cf), len(cw)))
-    # the largest copies are the calibration ones
+        sys.exit("missing dispatches: kernel %d/%d, calibration %d/%d" % (len(kf), len(kw), len(cf), len(cw)))
+    # the largest calibration dispatches are the 256 MiB ones
     cfk, cwk = max(cf), max(cw)
-    sf, sw = COPY_BYTES / (cfk * 1024), COPY_BYTES / (cwk * 1024)
+    sf, sw = CAL_BYTES / (cfk * 1024), CAL_BYTES / (cwk * 1024)
     fetch = sum(kf) / len(kf) * 1024 * sf
     write = sum(kw) / len(kw) * 1024 * sw
     rec = {"workload": args.workload, "kernel": args.kernel, "source_sha256": source_sha256(args.kernel),
            "fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write),
            "hbm_bytes_per_launch": round(fetch + write), "fetch_scale": round(sf, 4),
-           "write_scale": round(sw, 4), "dispatches": [len(kf), len(kw)]}
+           "write_scale": round(sw, 4), "dispatches": [len(kf), len(kw)],
+           "calibration": "read-only torch sum and write-only torch fill_ of 256 MiB, same run"}
     path = os.path.join(ROOT, "profiles", "traffic.json")
     data = json.load(open(path)) if os.path.exists(path) else {}
     data[args.name] = rec
@@ -74,8 +77,8 @@ def traffic(args):
         json.dump(data, f, indent=1, sort_keys=True)
     print(f"| kernel | dispatches | FETCH_SIZE KiB (avg) | WRITE_SIZE KiB (avg) |\n|---|---|---|---|\n"
           f"| `{args.kernel}` | {len(kf)} / {len(kw)} | {sum(kf) / len(kf):.1f} | {sum(kw) / len(kw):.1f} |\n"
-          f"| copy of {COPY_BYTES >> 20} MiB | {len(cf)} / {len(cw)} | {cfk:.1f} | {cwk:.1f} |\n\n"
-          f"Scale factors (copy bytes / counter bytes): fetch {sf:.4f}, write {sw:.4f}.\n"
+          f"| 256 MiB read (sum) / write (fill) | {len(cf)} / {len(cw)} | {cfk:.1f} | {cwk:.1f} |\n\n"
+          f"Scale factors (known bytes / counter bytes): fetch {sf:.4f}, write {sw:.4f}.\n"
           f"HBM traffic per launch: fetch {fetch / 1e6:.3f} MB + write {write / 1e6:.3f} MB "
           f"= {(fetch + write) / 1e6:.3f} MB.")
 

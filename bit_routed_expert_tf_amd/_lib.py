@@ -68,6 +68,9 @@ _SIGS = {
     "tf_moe_layer_fwd": (c_int32, [ctypes.POINTER(tf_moe_layer), c_void_p, c_int32, c_void_p,
                                    c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                                    c_void_p, c_void_p, c_void_p, c_size_t]),
+    "tf_moe_layer_fwd_noalloc": (c_int32, [ctypes.POINTER(tf_moe_layer), c_void_p, c_int32,
+                                           c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                           c_void_p]),
     "tf_prefill_workspace_bytes": (c_size_t, [ctypes.POINTER(tf_moe_layer), c_int32]),
     "tf_group_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
     "tf_group_by_expert": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p,

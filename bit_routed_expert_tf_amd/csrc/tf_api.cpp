@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "tf_internal.h"
@@ -376,6 +377,77 @@ tf_status tf_moe_layer_fwd(const tf_moe_layer *L, const uint16_t *x, int32_t T,
     a.b_shared_blocks = 0;
     e = tf_launch_decode(a, STAGE_B | STAGE_C, compute);
     return e == hipSuccess ? TF_OK : hip_fail(e, "routed launch");
+}
+
+}  // extern "C"
+
+// ------------------------------------------------ allocation-free decode
+// Scratch of tf_moe_layer_fwd_noalloc: a file-scope device array, one copy
+// per GPU for the life of the process.  Host code never uses its name as an
+// address; each device's address comes from hipGetSymbolAddress with that
+// device current.
+static __device__ __align__(256) unsigned char scratch[TF_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+bool g_scratch_clean[kMaxDevices];
+
+// This device's scratch address (set up on the device's first call: the
+// symbol address, then the whole array zeroed on `s`).  Returns NULL with
+// the error recorded.
+void *device_scratch(hipStream_t s, tf_status *st) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) { *st = hip_fail(e, "hipGetDevice"); return nullptr; }
+    if (dev < 0 || dev >= kMaxDevices) { *st = fail(TF_E_STATE, "device %d out of range", dev); return nullptr; }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) { *st = hip_fail(e, "hipGetSymbolAddress(scratch)"); return nullptr; }
+        g_scratch_ptr[dev] = p;
+        g_scratch_clean[dev] = false;
+    }
+    if (!g_scratch_clean[dev]) {   // first use, or after a call that failed mid-way
+        e = tf_launch_zero(g_scratch_ptr[dev], TF_NOALLOC_SCRATCH_BYTES, s);
+        if (e != hipSuccess) { *st = hip_fail(e, "clearing the scratch"); return nullptr; }
+        g_scratch_clean[dev] = true;
+    }
+    *st = TF_OK;
+    return g_scratch_ptr[dev];
+}
+
+void scratch_dirty() {
+    int dev = -1;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        g_scratch_clean[dev] = false;
+    }
+}
+}  // namespace
+
+extern "C" {
+
+tf_status tf_moe_layer_fwd_noalloc(const tf_moe_layer *L, const uint16_t *x, int32_t T,
+                                   const int32_t *forced_ids, uint16_t *y, float *y32,
+                                   int32_t *ids, float *weights, hipStream_t stream) {
+    if (T < 0 || T > MAX_DECODE_T) return fail(TF_E_ARG, "T must be in [0, %d]", MAX_DECODE_T);
+    if (T == 0) return TF_OK;
+    tf_status st = check_layer(L);
+    if (st) return st;
+    const size_t need = tf_moe_workspace_bytes(L, T);
+    if (need > TF_NOALLOC_SCRATCH_BYTES)
+        return fail(TF_E_NOMEM, "this step needs %zu bytes of scratch, more than the %zu the "
+                    "allocation-free entry point holds (use tf_moe_layer_fwd with a workspace)",
+                    need, (size_t)TF_NOALLOC_SCRATCH_BYTES);
+    void *ws = device_scratch(stream, &st);
+    if (!ws) return st;
+    st = tf_moe_layer_fwd(L, x, T, forced_ids, y, y32, ids, weights, nullptr, 0, stream, stream,
+                          ws, TF_NOALLOC_SCRATCH_BYTES);
+    if (st == TF_E_HIP) scratch_dirty();   // counters may be left set: clear on the next call
+    return st;
 }
 
 }  // extern "C"

@@ -194,6 +194,25 @@ tf_status tf_moe_layer_fwd(const tf_moe_layer *L, const uint16_t *x, int32_t T,
                            int32_t layer, hipStream_t compute, hipStream_t copy,
                            void *ws, size_t ws_bytes);
 
+/* Allocation-free decode step, for callers that cannot allocate device
+ * memory or pass a workspace (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments, kernels and
+ * results as tf_moe_layer_fwd with all experts resident (no slot cache,
+ * compute and copy streams both `stream`), but the workspace is the
+ * library's own static device scratch of TF_NOALLOC_SCRATCH_BYTES per GPU,
+ * held until the process ends.  The call allocates nothing.
+ *   TF_E_NOMEM when tf_moe_workspace_bytes(L, T) exceeds the scratch (at
+ *   d_model 2816, 128 experts, top-8, every T <= 16 fits; 3.9 MB at T = 16).
+ * Every call on a GPU shares that GPU's scratch: calls that overlap on one
+ * GPU (other streams, other host threads) race and give undefined results.
+ * The scratch is zeroed on a device's first call, and again after a call
+ * that returned TF_E_HIP.  The device-side id flags are not reported (no
+ * workspace to read them from). */
+#define TF_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+tf_status tf_moe_layer_fwd_noalloc(const tf_moe_layer *L, const uint16_t *x, int32_t T,
+                                   const int32_t *forced_ids, uint16_t *y, float *y32,
+                                   int32_t *ids, float *weights, hipStream_t stream);
+
 /* Prefill: one chunk of T (1..128) tokens through one layer, all experts
  * resident (shilu.ai README translation, "推理引擎的工作原理": prompt prefill
  * in chunks of at most 128 tokens, so that one fetched expert serves several

@@ -94,12 +94,17 @@ def _traffic_for(name, workload):
 
 def calibration(nbytes=256 << 20, reps=3):
     """Kernels of known traffic for scaling the memory counters (rocprofv3
-    FETCH_SIZE / WRITE_SIZE) of the same run: a read-only reduction and a
-    write-only fill of nbytes each."""
+    FETCH_SIZE / WRITE_SIZE) of the same run: a read-only stream of nbytes
+    with the GEMVs' 16-byte-per-lane whole-line loads (the library's
+    k_stream_read), and a write-only fill of nbytes."""
     import torch
+
+    from bit_routed_expert_tf_amd import _lib
+    lib = _lib.load()
     a = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     for _ in range(reps):
-        a.sum()
+        _lib.check(lib.tf_profile_stream_read(ctypes.c_void_p(a.data_ptr()), nbytes, s))
         a.fill_(2)
     torch.cuda.synchronize()
     del a

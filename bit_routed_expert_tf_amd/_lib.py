@@ -12,7 +12,9 @@ import os
 import threading
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libtf.so")
+# TF_LIBRARY may name another build of the same sources (the host-sanitizer
+# test's); it must exist like the default one -- there is no fallback.
+LIB_PATH = os.environ.get("TF_LIBRARY") or os.path.join(HERE, "libtf.so")
 
 TF_OK, TF_E_ARG, TF_E_SHAPE, TF_E_ALIGN, TF_E_HIP, TF_E_NOMEM, TF_E_STATE = range(7)
 STATUS_NAMES = {0: "TF_OK", 1: "TF_E_ARG", 2: "TF_E_SHAPE", 3: "TF_E_ALIGN", 4: "TF_E_HIP",
@@ -86,6 +88,7 @@ _SIGS = {
     "tf_sample": (c_int32, [c_void_p, c_int32, c_int32, ctypes.c_float, c_int32, ctypes.c_float,
                             c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "tf_profile_kernel": (c_int32, [c_int32, c_void_p, c_void_p]),
+    "tf_profile_stream_read": (c_int32, [c_void_p, c_size_t, c_void_p]),
     "tf_slot_cache_create": (c_int32, [c_int32, c_int32, c_int32, c_int32, c_size_t, c_void_p,
                                        c_void_p, c_int64, ctypes.POINTER(c_void_p)]),
     "tf_slot_cache_destroy": (None, [c_void_p]),

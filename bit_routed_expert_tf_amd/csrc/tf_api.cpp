@@ -281,6 +281,12 @@ tf_status tf_expert_q4_gemv(const uint8_t *pool, size_t blob_stride, int32_t d_m
     return e == hipSuccess ? TF_OK : hip_fail(e, "gemv launch");
 }
 
+tf_status tf_profile_stream_read(const void *p, size_t bytes, hipStream_t s) {
+    if (!p || bytes % 16 || ((uintptr_t)p & 15)) return fail(TF_E_ARG, "16-byte aligned pointer and size");
+    hipError_t e = tf_launch_stream_read(p, bytes, s);
+    return e == hipSuccess ? TF_OK : hip_fail(e, "stream-read kernel");
+}
+
 tf_status tf_profile_kernel(int32_t kernel, hipEvent_t start, hipEvent_t stop) {
     if (kernel != 0 && ((!start || !stop) || (kernel & (kernel - 1)) || kernel > 4096))
         return fail(TF_E_ARG, "one kernel id and two events, or kernel 0 to disarm");

@@ -110,6 +110,16 @@ __device__ __forceinline__ void st_dev(uint4 *p, uint4 v) {
                        __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Data an earlier launch on the stream wrote (expert ids, router weights,
+// item records): plain loads.  The kernel boundary already makes those
+// writes visible, and a plain load can be served by this XCD's L2 -- when
+// every workgroup of a launch reads the same few words, one miss per L2
+// fetches them instead of one device-coherent request per workgroup.
+template <typename T>
+__device__ __forceinline__ T ld_prev(const T *p) {
+    return *p;
+}
+
 // This thread's stores have completed; also a compiler barrier for memory
 // operations.
 __device__ __forceinline__ void stores_done() {

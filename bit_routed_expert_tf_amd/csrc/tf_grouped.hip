@@ -205,9 +205,9 @@ __device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1, KC> &L) {
         const int item = min(max(v - ns, 0) / tiles_r, a.max_items - 1) + z;
         const uint4 *p = reinterpret_cast<const uint4 *>(a.items + ITEM_INTS * item);
         Rec r;
-        r.r0 = ld_dev(p);
-        r.r1 = ld_dev(p + 1);
-        r.r2 = ld_dev(p + 2);
+        r.r0 = ld_prev(p);
+        r.r1 = ld_prev(p + 1);
+        r.r2 = ld_prev(p + 2);
         return r;
     };
     // a loaded record, used here: an ordered empty asm keeps what follows at
@@ -348,7 +348,7 @@ __device__ void grouped(const DecodeArgs &a, GLds<DOWN ? 2 : 1, KC> &L) {
     const Masks km = masks();
     // the first record is read together with the item count
     const Rec rec0 = load_rec(u);
-    const int n_items = (int)ld_dev(a.hdr + HDR_NITEMS);
+    const int n_items = (int)ld_prev(a.hdr + HDR_NITEMS);
     const int n_units = ns + n_items * tiles_r;
     if (u >= n_units) return;
     if (tid < 2 * PARTS) L.zero[tid] = make_uint4(0, 0, 0, 0);

@@ -102,3 +102,4 @@ bool tf_take_profile(int kernel, hipEvent_t *start, hipEvent_t *stop);
             hipLaunchKernelGGL(fn, grid, block, lds, stream, __VA_ARGS__);                 \
     } while (0)
 hipError_t tf_launch_zero(void *p, size_t bytes, hipStream_t s);
+hipError_t tf_launch_stream_read(const void *p, size_t bytes, hipStream_t s);

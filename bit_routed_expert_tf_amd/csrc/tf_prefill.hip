@@ -357,15 +357,15 @@ __device__ int mq_tokens(const DecodeArgs &a, bool routed, bool down, int tile, 
     int e = -1;
     if (tid < 2 * PARTS) L.zero[tid] = make_uint4(0, 0, 0, 0);
     if (routed) {
-        if (tile >= (int)ld_dev(a.hdr + HDR_NITEMS)) return -2;
-        const uint4 it = ld_dev(reinterpret_cast<const uint4 *>(a.items + ITEM_INTS * tile));
+        if (tile >= (int)ld_prev(a.hdr + HDR_NITEMS)) return -2;
+        const uint4 it = ld_prev(reinterpret_cast<const uint4 *>(a.items + ITEM_INTS * tile));
         e = (int)it.x;
         if (tid == 0) L.nt = min((int)it.z, TT);
         if (tid < TT) {
-            const int pr = ld_dev(a.pairs + (int)it.y + min(tid, (int)it.z - 1));
+            const int pr = ld_prev(a.pairs + (int)it.y + min(tid, (int)it.z - 1));
             L.src[tid] = down ? pr : pr / a.k;
             L.dst[tid] = pr;
-            L.coef[tid] = ld_dev(a.weights + pr);
+            L.coef[tid] = ld_prev(a.weights + pr);
         }
     } else {
         const int t0 = tile * TT;

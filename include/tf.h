@@ -325,6 +325,13 @@ enum {
  * timed kernel (measured: 10.3 against 8.5 us for the routed decode kernel).
  * Pass kernel 0 to disarm. */
 tf_status tf_profile_kernel(int32_t kernel, hipEvent_t start, hipEvent_t stop);
+/* Read `bytes` (a multiple of 16; p 16-byte aligned, device memory) once with
+ * the GEMVs' load pattern -- 16 bytes per lane, each wave's load covering
+ * whole 128-byte lines -- and write nothing: the kernel of known traffic
+ * against which memory counters of the GEMV kernels are scaled.  The
+ * kernel's name contains "k_stream_read".  TF_E_ARG on a bad pointer or
+ * size. */
+tf_status tf_profile_stream_read(const void *p, size_t bytes, hipStream_t s);
 
 /* ------------------------------------------------------------ slot cache */
 /* Per-layer LFU expert cache in HBM (shilu.ai README translation,

@@ -3,9 +3,12 @@
 Two counter passes over the same command (``--pmc FETCH_SIZE`` and
 ``--pmc WRITE_SIZE``, both in KiB per dispatch) are scaled by what the same
 counters read, in that run, for kernels of known traffic: ``bench.py
---calibrate`` first runs a read-only reduction over 256 MiB (torch ``sum``,
-16-byte loads per lane, like the GEMVs' code loads) and a write-only fill of
-256 MiB.  The result is in bytes of HBM traffic.  Usage:
+--calibrate`` first runs the library's read-only stream over 256 MiB
+(``k_stream_read``: 16-byte loads per lane covering whole 128-byte lines, the
+GEMVs' code-load pattern) and a write-only fill of 256 MiB.  The calibration
+must share the measured kernel's access pattern: FETCH_SIZE reads the
+whole-line stream at half its bytes but a torch reduction over the same
+buffer at all of them.  The result is in bytes of HBM traffic.  Usage:
 
     python3 profiling.py traffic --fetch F.csv --write W.csv --kernel k_stage_b \\
         --name routed_gateup_shared_down --workload resident-stack-30L-e128k8-uniform
@@ -51,7 +54,7 @@ def _per_dispatch(path, counter, match):
 
 
 def traffic(args):
-    is_read = lambda n: "reduce_kernel" in n   # noqa: E731  torch sum: reads CAL_BYTES
+    is_read = lambda n: "k_stream_read" in n   # noqa: E731  reads CAL_BYTES
     is_fill = lambda n: "FillFunctor" in n     # noqa: E731  torch fill_: writes CAL_BYTES
     is_kern = lambda n: args.kernel in n       # noqa: E731
     kf = _per_dispatch(args.fetch, "FETCH_SIZE", is_kern)
@@ -69,7 +72,7 @@ def traffic(args):
            "fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write),
            "hbm_bytes_per_launch": round(fetch + write), "fetch_scale": round(sf, 4),
            "write_scale": round(sw, 4), "dispatches": [len(kf), len(kw)],
-           "calibration": "read-only torch sum and write-only torch fill_ of 256 MiB, same run"}
+           "calibration": "read-only k_stream_read and write-only torch fill_ of 256 MiB, same run"}
     path = os.path.join(ROOT, "profiles", "traffic.json")
     data = json.load(open(path)) if os.path.exists(path) else {}
     data[args.name] = rec
@@ -77,7 +80,7 @@ def traffic(args):
         json.dump(data, f, indent=1, sort_keys=True)
     print(f"| kernel | dispatches | FETCH_SIZE KiB (avg) | WRITE_SIZE KiB (avg) |\n|---|---|---|---|\n"
           f"| `{args.kernel}` | {len(kf)} / {len(kw)} | {sum(kf) / len(kf):.1f} | {sum(kw) / len(kw):.1f} |\n"
-          f"| 256 MiB read (sum) / write (fill) | {len(cf)} / {len(cw)} | {cfk:.1f} | {cwk:.1f} |\n\n"
+          f"| 256 MiB read (k_stream_read) / write (fill) | {len(cf)} / {len(cw)} | {cfk:.1f} | {cwk:.1f} |\n\n"
           f"Scale factors (known bytes / counter bytes): fetch {sf:.4f}, write {sw:.4f}.\n"
           f"HBM traffic per launch: fetch {fetch / 1e6:.3f} MB + write {write / 1e6:.3f} MB "
           f"= {(fetch + write) / 1e6:.3f} MB.")

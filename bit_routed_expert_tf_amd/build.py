@@ -20,9 +20,17 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, "-c",
+# Host code instrumented by AddressSanitizer and UndefinedBehaviorSanitizer
+# (each flag for the host pass only; the device code is built as usual).  The
+# sanitizer runtime is not linked: the process that loads such a build
+# preloads clang's shared ASan runtime, which also carries UBSan's handlers.
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def _compile(src, build_dir=None, extra=()):
+    obj = os.path.join(build_dir or BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, *extra, "-c",
            os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
@@ -51,6 +59,24 @@ def build(verbose=False):
     if verbose:
         print("built", OUT)
     return OUT
+
+
+def build_host_sanitized(out_dir):
+    """The same library with ASan/UBSan-instrumented host code, as
+    out_dir/libtf_san.so (rebuilt when a source is newer)."""
+    os.makedirs(out_dir, exist_ok=True)
+    out = os.path.join(out_dir, "libtf_san.so")
+    srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
+    deps = [os.path.join(CSRC, f) for f in os.listdir(CSRC)] + [os.path.join(ROOT, "include", "tf.h")]
+    if os.path.exists(out) and os.path.getmtime(out) > max(os.path.getmtime(p) for p in deps):
+        return out
+    with ThreadPoolExecutor(len(srcs)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, out_dir, HOST_SANITIZE), srcs))
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stderr)
+    return out
 
 
 if __name__ == "__main__":

@@ -69,6 +69,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
 _SO = os.path.join(_HERE, "liboracle.so")
+# a separately built copy (the sanitizer test's) when ORACLE_LIBRARY names one
+_SO_OVERRIDE = os.environ.get("ORACLE_LIBRARY")
 _lock = threading.Lock()
 _lib = None
 
@@ -95,8 +97,11 @@ def lib():
     global _lib
     with _lock:
         if _lib is None:
-            build()
-            L = ctypes.CDLL(_SO)
+            if _SO_OVERRIDE:
+                L = ctypes.CDLL(_SO_OVERRIDE)
+            else:
+                build()
+                L = ctypes.CDLL(_SO)
             P = ctypes.c_void_p
             i32, i64 = ctypes.c_int, ctypes.c_int64
             L.orc_half_to_double.restype = ctypes.c_double

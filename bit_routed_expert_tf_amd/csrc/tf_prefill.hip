@@ -94,7 +94,7 @@ __device__ __forceinline__ float hsum2(uint32_t p) {
     return h2f((uint16_t)(p & 0xFFFF)) + h2f((uint16_t)(p >> 16));
 }
 
-template <int PARTS>
+template <int PARTS, int R>
 struct MQLds {
     int src[TT], dst[TT];
     float coef[TT];
@@ -104,16 +104,19 @@ struct MQLds {
     // on different banks
     uint4 xs[TT][KCH * 4 * PARTS * 2 + 1];
     float2 xc[TT][KCH + 1];     // (X, C) per token and group of the chunk
-    float2 sb[KCH][64 + 4];     // (scale, bias) per group and row of the block
+    float2 sb[R][KCH][64 + 4];  // (scale, bias) per row tile, group and row of the block
     uint4 zero[2 * PARTS];      // B operand of the columns a lane block does not feed
 };
 
-// One tile.  DOWN = false: gate/up rows [32 rt, +32) of the expert (F rows,
-// K = d) into hidden rows; DOWN = true: down rows [64 rt, +64) (d rows,
-// K = F) into fp32 output rows.
-template <bool DOWN, int GS>
-__device__ void mq_tile(const DecodeArgs &a, const uint8_t *blob, int F, int rt,
-                        MQLds<DOWN ? 2 : 1> &L, int nt, const uint16_t *x, const uint4 *hsrc,
+// R row tiles rt0 .. rt0 + nrt - 1 (nrt <= R) of one item.  DOWN = false:
+// gate/up rows [32 rt, +32) of the expert (F rows, K = d) into hidden rows;
+// DOWN = true: down rows [64 rt, +64) (d rows, K = F) into fp32 output rows.
+// Each K chunk of the tokens' activations is staged once for all R tiles,
+// and each B operand read from LDS feeds R MFMAs.  Tiles past nrt repeat
+// the last one and store nothing.
+template <bool DOWN, int GS, int R>
+__device__ void mq_tile(const DecodeArgs &a, const uint8_t *blob, int F, int rt0, int nrt,
+                        MQLds<DOWN ? 2 : 1, R> &L, int nt, const uint16_t *x, const uint4 *hsrc,
                         uint4 *hdst, float *ydst) {
     constexpr int PARTS = DOWN ? 2 : 1;
     constexpr int NRND = KCH / GS;   // rounds per chunk
@@ -124,39 +127,46 @@ __device__ void mq_tile(const DecodeArgs &a, const uint8_t *blob, int F, int rt,
     Mat mg, mu, md;
     blob_mats(blob, d, F, mg, mu, md);
     const Mat &mm = DOWN ? md : ((w >> 1) ? mu : mg);
-    const int r0 = DOWN ? 64 * rt + 16 * w : 32 * rt + 16 * (w & 1);   // first row of the wave
-    const uint8_t *qrow = mm.q + (size_t)(r0 + j) * (K >> 1);
+    int rts[R], r0s[R];   // row tile, first row of the wave
+    const uint8_t *qrow[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        rts[i] = rt0 + min(i, nrt - 1);
+        r0s[i] = DOWN ? 64 * rts[i] + 16 * w : 32 * rts[i] + 16 * (w & 1);
+        qrow[i] = mm.q + (size_t)(r0s[i] + j) * (K >> 1);
+    }
 
-    // This lane's code bytes of chunk c, round rho: slot group and words of
-    // lane block b (GS 4: the whole group; 2: half of it; 1: a quarter).
-    uint4 q[4];
-    auto qload = [&](int c, int rho) {
+    // This lane's code bytes of tile i, chunk c, round rho: slot group and
+    // words of lane block b (GS 4: the whole group; 2: half of it; 1: a
+    // quarter).
+    uint4 q[R][4];
+    auto qload = [&](int i, int c, int rho) {
         if (GS == 4) {
             const int g = min(KCH * c + 4 * rho + b, G - 1);
-            q[2 * rho] = *reinterpret_cast<const uint4 *>(qrow + 32 * g);
-            q[2 * rho + 1] = *reinterpret_cast<const uint4 *>(qrow + 32 * g + 16);
+            q[i][2 * rho] = *reinterpret_cast<const uint4 *>(qrow[i] + 32 * g);
+            q[i][2 * rho + 1] = *reinterpret_cast<const uint4 *>(qrow[i] + 32 * g + 16);
         } else if (GS == 2) {
             const int g = min(KCH * c + 2 * rho + (b >> 1), G - 1);
-            q[rho] = *reinterpret_cast<const uint4 *>(qrow + 32 * g + 16 * (b & 1));
+            q[i][rho] = *reinterpret_cast<const uint4 *>(qrow[i] + 32 * g + 16 * (b & 1));
         } else {
             const int g = min(KCH * c + rho, G - 1);
-            const uint2 v = *reinterpret_cast<const uint2 *>(qrow + 32 * g + 8 * b);
-            if (rho & 1) { q[rho >> 1].z = v.x; q[rho >> 1].w = v.y; }
-            else { q[rho >> 1].x = v.x; q[rho >> 1].y = v.y; }
+            const uint2 v = *reinterpret_cast<const uint2 *>(qrow[i] + 32 * g + 8 * b);
+            if (rho & 1) { q[i][rho >> 1].z = v.x; q[i][rho >> 1].w = v.y; }
+            else { q[i][rho >> 1].x = v.x; q[i][rho >> 1].y = v.y; }
         }
     };
-    // words (w0, w1) of step sg of round rho
-    auto words = [&](int rho, int sg, uint32_t &w0, uint32_t &w1) {
+    // words (w0, w1) of step sg of round rho of tile i
+    auto words = [&](int i, int rho, int sg, uint32_t &w0, uint32_t &w1) {
         if (GS == 4) {
-            const uint4 v = q[2 * rho + (sg >> 1)];
+            const uint4 v = q[i][2 * rho + (sg >> 1)];
             w0 = (sg & 1) ? v.z : v.x;
             w1 = (sg & 1) ? v.w : v.y;
         } else if (GS == 2) {
-            const uint4 v = q[rho];
+            const uint4 v = q[i][rho];
             w0 = sg ? v.z : v.x;
             w1 = sg ? v.w : v.y;
         } else {
-            const uint4 v = q[rho >> 1];
+            const uint4 v = q[i][rho >> 1];
             w0 = (rho & 1) ? v.z : v.x;
             w1 = (rho & 1) ? v.w : v.y;
         }
@@ -171,7 +181,7 @@ __device__ void mq_tile(const DecodeArgs &a, const uint8_t *blob, int F, int rt,
     struct Pre {
         uint4 v[DOWN ? 8 : 4];
         float2 xc;
-        uint32_t sbw[2];
+        uint32_t sbw[R][2];
     };
     // (every lane loads, non-stagers a valid row they then ignore: the loads
     // take no branch, so each wait counts only the loads it needs)
@@ -187,11 +197,15 @@ __device__ void mq_tile(const DecodeArgs &a, const uint8_t *blob, int F, int rt,
             P.xc = reinterpret_cast<const float2 *>(hr + HU)[min(16 * c + sub, F / 32 - 1)];
         }
 #pragma unroll
-        for (int qq = 0; qq < 2; ++qq) {
-            const int e = tid + 256 * qq, rr = e >> 3, g = min(KCH * c + (e & 7), G - 1);
-            const Mat &ms = DOWN ? md : (rr < 32 ? mg : mu);
-            const int row = DOWN ? 64 * rt + rr : 32 * rt + (rr & 31);
-            P.sbw[qq] = (uint32_t)ms.s[(size_t)row * G + g] | ((uint32_t)ms.b[(size_t)row * G + g] << 16);
+        for (int i = 0; i < R; ++i) {
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq) {
+                const int e = tid + 256 * qq, rr = e >> 3, g = min(KCH * c + (e & 7), G - 1);
+                const Mat &ms = DOWN ? md : (rr < 32 ? mg : mu);
+                const int row = DOWN ? 64 * rts[i] + rr : 32 * rts[i] + (rr & 31);
+                P.sbw[i][qq] =
+                    (uint32_t)ms.s[(size_t)row * G + g] | ((uint32_t)ms.b[(size_t)row * G + g] << 16);
+            }
         }
     };
     auto store = [&](const Pre &P, int c) {
@@ -227,10 +241,13 @@ __device__ void mq_tile(const DecodeArgs &a, const uint8_t *blob, int F, int rt,
         const float X2 = X + __shfl_xor(X, 1), C2 = C + __shfl_xor(C, 1);
         if (stager && !(sub & 1)) L.xc[tj][sub >> 1] = make_float2(X2, C2);
 #pragma unroll
-        for (int qq = 0; qq < 2; ++qq) {
-            const int e = tid + 256 * qq, rr = e >> 3, gl = e & 7;
-            const uint32_t v = KCH * c + gl < G ? P.sbw[qq] : 0u;
-            L.sb[gl][rr] = make_float2(h2f((uint16_t)(v & 0xFFFF)), h2f((uint16_t)(v >> 16)));
+        for (int i = 0; i < R; ++i) {
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq) {
+                const int e = tid + 256 * qq, rr = e >> 3, gl = e & 7;
+                const uint32_t v = KCH * c + gl < G ? P.sbw[i][qq] : 0u;
+                L.sb[i][gl][rr] = make_float2(h2f((uint16_t)(v & 0xFFFF)), h2f((uint16_t)(v >> 16)));
+            }
         }
     };
 
@@ -240,11 +257,15 @@ __device__ void mq_tile(const DecodeArgs &a, const uint8_t *blob, int F, int rt,
     const bool col_ok = tc < nt;
     const bool feeds = col_ok && (GS == 1 || sc == b / BPS);
 #pragma unroll
-    for (int rho = 0; rho < NRND; ++rho) qload(0, rho);
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int rho = 0; rho < NRND; ++rho) qload(i, 0, rho);
     Pre P;
     fetch(P, 0);
     store(P, 0);
-    f32x4 y = {0.f, 0.f, 0.f, 0.f};
+    f32x4 y[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) y[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int nch = (G + KCH - 1) / KCH;
     const uint4 *xrow = &L.xs[tc][0];
     const Masks km = masks();
@@ -258,101 +279,122 @@ __device__ void mq_tile(const DecodeArgs &a, const uint8_t *blob, int F, int rt,
         for (int rho = 0; rho < NRND; ++rho) {
             const int gc = GS * rho + sc;   // the column's group in the chunk
             const float2 xc = L.xc[tc][gc];
-            f32x4 D = {-xc.y, -xc.y, -xc.y, -xc.y};
+            f32x4 D[R];
+#pragma unroll
+            for (int i = 0; i < R; ++i) D[i] = f32x4{-xc.y, -xc.y, -xc.y, -xc.y};
 #pragma unroll
             for (int sg = 0; sg < GS; ++sg) {
-                uint32_t w0, w1;
-                words(rho, sg, w0, w1);
-                const half8 al = codes_lo(km, w0, w1), ah = codes_hi(km, w0, w1);
                 // the word pair lane block b feeds in this step
                 const int m = GS == 4 ? 4 * (4 * rho + b) + sg
                             : GS == 2 ? 4 * (2 * rho + (b >> 1)) + 2 * (b & 1) + sg
                                       : 4 * rho + b;
                 const uint4 *bp = feeds ? xrow + m * 2 * PARTS : L.zero;
+                uint4 bv[2 * PARTS];
 #pragma unroll
-                for (int p = 0; p < PARTS; ++p) {
-                    D = mfma(al, as_half8(bp[2 * p]), D);
-                    D = mfma(ah, as_half8(bp[2 * p + 1]), D);
+                for (int p = 0; p < 2 * PARTS; ++p) bv[p] = bp[p];
+#pragma unroll
+                for (int i = 0; i < R; ++i) {
+                    uint32_t w0, w1;
+                    words(i, rho, sg, w0, w1);
+                    const half8 al = codes_lo(km, w0, w1), ah = codes_hi(km, w0, w1);
+#pragma unroll
+                    for (int p = 0; p < PARTS; ++p) {
+                        D[i] = mfma(al, as_half8(bv[2 * p]), D[i]);
+                        D[i] = mfma(ah, as_half8(bv[2 * p + 1]), D[i]);
+                    }
                 }
             }
-            qload(cn, rho);
-            const float4 s01 = *reinterpret_cast<const float4 *>(&L.sb[gc][16 * w + 4 * b]);
-            const float4 s23 = *reinterpret_cast<const float4 *>(&L.sb[gc][16 * w + 4 * b + 2]);
-            y[0] = fmaf(s01.x, D[0], fmaf(s01.y, xc.x, y[0]));
-            y[1] = fmaf(s01.z, D[1], fmaf(s01.w, xc.x, y[1]));
-            y[2] = fmaf(s23.x, D[2], fmaf(s23.y, xc.x, y[2]));
-            y[3] = fmaf(s23.z, D[3], fmaf(s23.w, xc.x, y[3]));
-            // the round's epilogue completes here (an ordered empty asm reading
-            // y), so no round's D stays live to the end of the chunk
-            asm volatile("" : "+v"(y[0]), "+v"(y[1]), "+v"(y[2]), "+v"(y[3]));
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                qload(i, cn, rho);
+                const float4 s01 = *reinterpret_cast<const float4 *>(&L.sb[i][gc][16 * w + 4 * b]);
+                const float4 s23 = *reinterpret_cast<const float4 *>(&L.sb[i][gc][16 * w + 4 * b + 2]);
+                y[i][0] = fmaf(s01.x, D[i][0], fmaf(s01.y, xc.x, y[i][0]));
+                y[i][1] = fmaf(s01.z, D[i][1], fmaf(s01.w, xc.x, y[i][1]));
+                y[i][2] = fmaf(s23.x, D[i][2], fmaf(s23.y, xc.x, y[i][2]));
+                y[i][3] = fmaf(s23.z, D[i][3], fmaf(s23.w, xc.x, y[i][3]));
+                // the round's epilogue completes here (an ordered empty asm
+                // reading y), so no round's D stays live to the end of the chunk
+                asm volatile("" : "+v"(y[i][0]), "+v"(y[i][1]), "+v"(y[i][2]), "+v"(y[i][3]));
+            }
         }
         lds_barrier();   // everyone is done reading chunk c
         store(P, cn);
     }
     // a token's slot columns are neighbouring lanes: sum them
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        if (GS >= 2) y[r] += dpp_f<DPP_XOR1>(y[r]);
-        if (GS == 4) y[r] += dpp_f<DPP_XOR2>(y[r]);
-    }
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if (GS >= 2) y[i][r] += dpp_f<DPP_XOR1>(y[i][r]);
+            if (GS == 4) y[i][r] += dpp_f<DPP_XOR2>(y[i][r]);
+        }
     const bool owner = col_ok && sc == 0;
     if (DOWN) {   // rows r0 + 4b .. +3 of token tc
-        if (owner)
-            *reinterpret_cast<float4 *>(ydst + (size_t)L.dst[tc] * d + r0 + 4 * b) =
-                make_float4(y[0], y[1], y[2], y[3]);
+        if (owner) {
+#pragma unroll
+            for (int i = 0; i < R; ++i)
+                if (i < nrt)
+                    *reinterpret_cast<float4 *>(ydst + (size_t)L.dst[tc] * d + r0s[i] + 4 * b) =
+                        make_float4(y[i][0], y[i][1], y[i][2], y[i][3]);
+        }
         return;
     }
     // gate and up sums, in the activation area once every wave is done with it
     float(*out)[32][TT + 1] = reinterpret_cast<float(*)[32][TT + 1]>(&L.xs[0][0]);
-    lds_barrier();
-    if (owner) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) out[w >> 1][16 * (w & 1) + 4 * b + r][tc] = y[r];
-    }
-    lds_barrier();
-    if (tid < 64) {   // thread (token, 8-row block): h = coef * gelu(g) * u
-        const int t = tid >> 2, s4 = tid & 3;
-        const bool ok = t < nt;
-        float hh[8], hl[8], X = 0.f, C = 0.f;
+    for (int i = 0; i < R; ++i) {
+        if (i >= nrt) break;   // uniform
+        lds_barrier();
+        if (owner) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float e = ok ? L.coef[t] * (gelu_f(out[0][8 * s4 + i][t], a.act) *
-                                              out[1][8 * s4 + i][t])
-                               : 0.f;
-            hh[i] = (float)(_Float16)e;
-            hl[i] = (float)(_Float16)(e - hh[i]);
-            X += e;
+            for (int r = 0; r < 4; ++r) out[w >> 1][16 * (w & 1) + 4 * b + r][tc] = y[i][r];
         }
-        // even elements as they are, odd ones divided by 16, in the pair
-        // order (e0,e4)(e2,e6) | (e1,e5)(e3,e7)
-        const uint2 he = make_uint2(pack_h2(hh[0], hh[4]), pack_h2(hh[2], hh[6]));
-        const uint2 ho = make_uint2(div16(pack_h2(hh[1], hh[5])), div16(pack_h2(hh[3], hh[7])));
-        const uint2 le = make_uint2(pack_h2(hl[0], hl[4]), pack_h2(hl[2], hl[6]));
-        const uint2 lo = make_uint2(div16(pack_h2(hl[1], hl[5])), div16(pack_h2(hl[3], hl[7])));
-        C = ((hsum2(he.x) + hsum2(he.y)) + (hsum2(ho.x) + hsum2(ho.y))) +
-            ((hsum2(le.x) + hsum2(le.y)) + (hsum2(lo.x) + hsum2(lo.y)));
-        C *= 1024.f;
-        X += __shfl_xor(X, 1);
-        X += __shfl_xor(X, 2);
-        C += __shfl_xor(C, 1);
-        C += __shfl_xor(C, 2);
-        if (ok) {
-            const int wg = 4 * rt + s4;   // word of the hidden row
-            uint4 *row = hdst + (size_t)L.dst[t] * mq_row_u4(F);
-            uint2 *u2 = reinterpret_cast<uint2 *>(row) + 8 * (wg >> 1) + (wg & 1);
-            u2[0] = he;
-            u2[2] = ho;
-            u2[4] = le;
-            u2[6] = lo;
-            if (s4 == 0) reinterpret_cast<float2 *>(row + F / 4)[rt] = make_float2(X, C);
+        lds_barrier();
+        if (tid < 64) {   // thread (token, 8-row block): h = coef * gelu(g) * u
+            const int t = tid >> 2, s4 = tid & 3;
+            const bool ok = t < nt;
+            float hh[8], hl[8], X = 0.f, C = 0.f;
+#pragma unroll
+            for (int e8 = 0; e8 < 8; ++e8) {
+                const float e = ok ? L.coef[t] * (gelu_f(out[0][8 * s4 + e8][t], a.act) *
+                                                  out[1][8 * s4 + e8][t])
+                                   : 0.f;
+                hh[e8] = (float)(_Float16)e;
+                hl[e8] = (float)(_Float16)(e - hh[e8]);
+                X += e;
+            }
+            // even elements as they are, odd ones divided by 16, in the pair
+            // order (e0,e4)(e2,e6) | (e1,e5)(e3,e7)
+            const uint2 he = make_uint2(pack_h2(hh[0], hh[4]), pack_h2(hh[2], hh[6]));
+            const uint2 ho = make_uint2(div16(pack_h2(hh[1], hh[5])), div16(pack_h2(hh[3], hh[7])));
+            const uint2 le = make_uint2(pack_h2(hl[0], hl[4]), pack_h2(hl[2], hl[6]));
+            const uint2 lo = make_uint2(div16(pack_h2(hl[1], hl[5])), div16(pack_h2(hl[3], hl[7])));
+            C = ((hsum2(he.x) + hsum2(he.y)) + (hsum2(ho.x) + hsum2(ho.y))) +
+                ((hsum2(le.x) + hsum2(le.y)) + (hsum2(lo.x) + hsum2(lo.y)));
+            C *= 1024.f;
+            X += __shfl_xor(X, 1);
+            X += __shfl_xor(X, 2);
+            C += __shfl_xor(C, 1);
+            C += __shfl_xor(C, 2);
+            if (ok) {
+                const int wg = 4 * rts[i] + s4;   // word of the hidden row
+                uint4 *row = hdst + (size_t)L.dst[t] * mq_row_u4(F);
+                uint2 *u2 = reinterpret_cast<uint2 *>(row) + 8 * (wg >> 1) + (wg & 1);
+                u2[0] = he;
+                u2[2] = ho;
+                u2[4] = le;
+                u2[6] = lo;
+                if (s4 == 0) reinterpret_cast<float2 *>(row + F / 4)[rts[i]] = make_float2(X, C);
+            }
         }
     }
 }
 
 // Token list of a tile: routed item (expert, up to 16 pairs) or 16 shared
 // tokens.  Returns the expert (-1: the shared expert, -2: nothing to do).
-template <int PARTS>
-__device__ int mq_tokens(const DecodeArgs &a, bool routed, bool down, int tile, MQLds<PARTS> &L) {
+template <int PARTS, int R>
+__device__ int mq_tokens(const DecodeArgs &a, bool routed, bool down, int tile, MQLds<PARTS, R> &L) {
     const int tid = threadIdx.x;
     int e = -1;
     if (tid < 2 * PARTS) L.zero[tid] = make_uint4(0, 0, 0, 0);
@@ -379,40 +421,49 @@ __device__ int mq_tokens(const DecodeArgs &a, bool routed, bool down, int tile, 
     return e;
 }
 
+// Row tiles per workgroup (each staged activation chunk serves them all) and
+// the residency that leaves room for their registers.
+constexpr int RT_GU = 1, RT_DN = 4;
+constexpr int occ(int r) { return r == 1 ? 4 : r == 2 ? 3 : 2; }
+
 // Gate/up of the shared expert (blocks [0, a_shared_blocks)) and of the
-// routed expert items (the rest).
-__global__ __launch_bounds__(256, 4) void k_mq_gateup(DecodeArgs a) {
-    __shared__ MQLds<1> L;
+// routed expert items (the rest); a workgroup takes RT_GU row tiles of one
+// item.
+__global__ __launch_bounds__(256, occ(RT_GU)) void k_mq_gateup(DecodeArgs a) {
+    __shared__ MQLds<1, RT_GU> L;
     int b = blockIdx.x;
     const bool routed = b >= a.a_shared_blocks;
     if (routed) b -= a.a_shared_blocks;
-    const int F = routed ? a.f : a.fs, tiles = F / 32;
-    const int e = mq_tokens(a, routed, false, b / tiles, L);
+    const int F = routed ? a.f : a.fs, tiles = F / 32, wpi = (tiles + RT_GU - 1) / RT_GU;
+    const int e = mq_tokens(a, routed, false, b / wpi, L);
     if (e == -2) return;
     const int nt = uniform(L.nt);
+    const int rt0 = (b % wpi) * RT_GU, nrt = min(RT_GU, tiles - rt0);
     const uint8_t *blob = routed ? expert_blob(a, e) : a.shared_blob;
     uint4 *dst = routed ? a.h_r : a.h_s;
-    if (nt <= 4) mq_tile<false, 4>(a, blob, F, b % tiles, L, nt, a.x, nullptr, dst, nullptr);
-    else if (nt <= 8) mq_tile<false, 2>(a, blob, F, b % tiles, L, nt, a.x, nullptr, dst, nullptr);
-    else mq_tile<false, 1>(a, blob, F, b % tiles, L, nt, a.x, nullptr, dst, nullptr);
+    if (nt <= 4) mq_tile<false, 4, RT_GU>(a, blob, F, rt0, nrt, L, nt, a.x, nullptr, dst, nullptr);
+    else if (nt <= 8) mq_tile<false, 2, RT_GU>(a, blob, F, rt0, nrt, L, nt, a.x, nullptr, dst, nullptr);
+    else mq_tile<false, 1, RT_GU>(a, blob, F, rt0, nrt, L, nt, a.x, nullptr, dst, nullptr);
 }
 
-// Down of the shared expert (-> y_s) and of the routed expert items (-> y_e).
-__global__ __launch_bounds__(256, 4) void k_mq_down(DecodeArgs a) {
-    __shared__ MQLds<2> L;
+// Down of the shared expert (-> y_s) and of the routed expert items (-> y_e);
+// a workgroup takes RT_DN row tiles of one item.
+__global__ __launch_bounds__(256, occ(RT_DN)) void k_mq_down(DecodeArgs a) {
+    __shared__ MQLds<2, RT_DN> L;
     int b = blockIdx.x;
     const bool routed = b >= a.b_shared_blocks;
     if (routed) b -= a.b_shared_blocks;
-    const int F = routed ? a.f : a.fs, tiles = a.d / 64;
-    const int e = mq_tokens(a, routed, true, b / tiles, L);
+    const int F = routed ? a.f : a.fs, tiles = a.d / 64, wpi = (tiles + RT_DN - 1) / RT_DN;
+    const int e = mq_tokens(a, routed, true, b / wpi, L);
     if (e == -2) return;
     const int nt = uniform(L.nt);
+    const int rt0 = (b % wpi) * RT_DN, nrt = min(RT_DN, tiles - rt0);
     const uint8_t *blob = routed ? expert_blob(a, e) : a.shared_blob;
     const uint4 *src = routed ? a.h_r : a.h_s;
     float *dst = routed ? a.y_e : a.y_s;
-    if (nt <= 4) mq_tile<true, 4>(a, blob, F, b % tiles, L, nt, nullptr, src, nullptr, dst);
-    else if (nt <= 8) mq_tile<true, 2>(a, blob, F, b % tiles, L, nt, nullptr, src, nullptr, dst);
-    else mq_tile<true, 1>(a, blob, F, b % tiles, L, nt, nullptr, src, nullptr, dst);
+    if (nt <= 4) mq_tile<true, 4, RT_DN>(a, blob, F, rt0, nrt, L, nt, nullptr, src, nullptr, dst);
+    else if (nt <= 8) mq_tile<true, 2, RT_DN>(a, blob, F, rt0, nrt, L, nt, nullptr, src, nullptr, dst);
+    else mq_tile<true, 1, RT_DN>(a, blob, F, rt0, nrt, L, nt, nullptr, src, nullptr, dst);
 }
 
 }  // namespace
@@ -422,13 +473,15 @@ __global__ __launch_bounds__(256, 4) void k_mq_down(DecodeArgs a) {
 hipError_t tf_launch_prefill_tiles(const DecodeArgs &a0, int max_items, hipStream_t s) {
     DecodeArgs a = a0;
     const int ttiles = (a.T + TT - 1) / TT;
-    a.a_shared_blocks = ttiles * (a.fs / 32);
-    const int n_gu = a.a_shared_blocks + max_items * (a.f / 32);
+    const int wpi_s = (a.fs / 32 + RT_GU - 1) / RT_GU, wpi_r = (a.f / 32 + RT_GU - 1) / RT_GU;
+    a.a_shared_blocks = ttiles * wpi_s;
+    const int n_gu = a.a_shared_blocks + max_items * wpi_r;
     TF_LAUNCH(TF_KERNEL_PREFILL_GATEUP, k_mq_gateup, dim3(n_gu), dim3(WG), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    a.b_shared_blocks = ttiles * (a.d / 64);
-    const int n_dn = a.b_shared_blocks + max_items * (a.d / 64);
+    const int wpi_d = (a.d / 64 + RT_DN - 1) / RT_DN;
+    a.b_shared_blocks = ttiles * wpi_d;
+    const int n_dn = a.b_shared_blocks + max_items * wpi_d;
     TF_LAUNCH(TF_KERNEL_PREFILL_DOWN, k_mq_down, dim3(n_dn), dim3(WG), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

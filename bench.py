@@ -255,7 +255,8 @@ def run_stack_batch(args, wl, layers, B, lib, dev, roofline):
                  _lib.TF_KERNEL_DOWN_COMBINE: "k_stage_c1"}
         gemv = {"k_stage_b": stage_b_bytes(d, f, fs, k)}
     else:
-        names = {_lib.TF_KERNEL_ROUTER_SHARED_GATEUP: "k_stage_a",
+        names = {_lib.TF_KERNEL_ROUTER_SHARED_GATEUP: "k_router_mm",
+                 _lib.TF_KERNEL_ROUTER_TOPK: "k_router_topk",
                  _lib.TF_KERNEL_PREFILL_GATEUP: "k_gu",
                  _lib.TF_KERNEL_PREFILL_DOWN: "k_dn",
                  _lib.TF_KERNEL_PREFILL_COMBINE: "k_pf_combine"}
@@ -464,10 +465,11 @@ def run_prefill(args):
     blob = 2 * qb(f, d) + qb(d, f)
     chunk_bytes = qb(E, d, 8) + 2 * qb(fs, d) + qb(d, fs) + distinct * blob + 4 * C * d
     kern = _profile(lib, _hip(), {
-        _lib.TF_KERNEL_ROUTER_SHARED_GATEUP: "router_topk_group",
-        _lib.TF_KERNEL_PREFILL_GATEUP: "gateup_mfma",
-        _lib.TF_KERNEL_PREFILL_DOWN: "down_mfma",
-        _lib.TF_KERNEL_PREFILL_COMBINE: "combine"}, step, range(min(args.prof_steps, 64)), stream)
+        _lib.TF_KERNEL_ROUTER_SHARED_GATEUP: "k_router_mm",
+        _lib.TF_KERNEL_ROUTER_TOPK: "k_router_topk",
+        _lib.TF_KERNEL_PREFILL_GATEUP: "k_mq_gateup",
+        _lib.TF_KERNEL_PREFILL_DOWN: "k_mq_down",
+        _lib.TF_KERNEL_PREFILL_COMBINE: "k_pf_combine"}, step, range(min(args.prof_steps, 64)), stream)
     us = ms * 1e3 / steps
     return {"metric": "prefill tokens/s (128-token chunks, one layer)",
             "value": round(C * steps / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,

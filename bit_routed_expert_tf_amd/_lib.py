@@ -26,6 +26,7 @@ TF_KERNEL_PREFILL_DOWN, TF_KERNEL_PREFILL_COMBINE = 8, 16
 TF_KERNEL_PREFILL_GATEUP, TF_KERNEL_GROUP = 32, 64
 TF_KERNEL_SAMPLE_PART, TF_KERNEL_SAMPLE_FINAL = 128, 256
 TF_KERNEL_ATTN_CHUNK, TF_KERNEL_ATTN_COMBINE = 512, 1024
+TF_KERNEL_ROUTER_TOPK = 2048
 TF_SLOT_LFU, TF_SLOT_LRU = 0, 1
 TF_SLOT_COPY_DMA, TF_SLOT_COPY_KERNEL = 0, 1
 

@@ -76,7 +76,7 @@ constexpr size_t kCtkBytes = (size_t)128 * (4096 / 32);   // one token's down ti
 
 // Decode workspace layout (offsets in bytes).
 struct WsLayout {
-    size_t hdr, logits, items, pairs, hs, ys, hr, xb, ye, ctk, total;
+    size_t hdr, logits, part, items, pairs, hs, ys, hr, xb, ye, ctk, total;
 };
 
 WsLayout decode_layout(int d, int f, int fs, int E, int k, int T) {
@@ -85,6 +85,7 @@ WsLayout decode_layout(int d, int f, int fs, int E, int k, int T) {
     w.hdr = o; o += kHdrBytes;
     w.ctk = o; o += kCtkBytes;             // decode down tile tickets (one token)
     w.logits = o; o += up256((size_t)8 * T * E);
+    w.part = o; o += T >= 2 ? up256((size_t)8 * tf_router_nkr(T, E) * T * E) : 0;   // grouped steps
     w.items = o; o += up256((size_t)4 * ITEM_INTS * T * k);
     w.pairs = o; o += up256((size_t)4 * T * k);
     w.hs = o; o += up256(h_row_bytes(fs) * T);
@@ -151,8 +152,9 @@ hipError_t grouped_step(const tf_moe_layer *L, const uint16_t *x, int T, const i
     const int P = T * a.k;
     const int max_items = P < a.E + P / a.tbi ? P : a.E + P / a.tbi;
     a.max_items = max_items;
-    a.a_router_blocks = router_blocks(a.E, T);
-    hipError_t e = tf_launch_decode(a, STAGE_A, s);
+    a.part = at<double>(ws, w.part);
+    a.nkr = tf_router_nkr(T, a.E);
+    hipError_t e = tf_launch_router_grouped(a, s);
     if (e == hipSuccess)
         e = tiles ? tf_launch_prefill_tiles(a, max_items, s) : tf_launch_grouped(a, max_items, s);
     return e;

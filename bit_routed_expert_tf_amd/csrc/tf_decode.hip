@@ -322,7 +322,13 @@ __device__ void topk_block(const DecodeArgs &a, int t, int tid, unsigned char *l
     if (tid < 16) { sel[tid] = 0; hits[tid] = 0; }
     if (tid == 0) *tie = 0;
     for (int i = tid; i < E; i += WG) {
-        double v = ld_dev(a.logits + (size_t)t * E + i);
+        double v;
+        if (a.part) {   // partial logits of an earlier launch, added in K-range order
+            v = 0.0;
+            for (int r = 0; r < a.nkr; ++r) v += ld_prev(a.part + ((size_t)r * a.T + t) * E + i);
+        } else {
+            v = ld_dev(a.logits + (size_t)t * E + i);
+        }
         if (v != v) v = -__builtin_inf();   // NaN ranks last
         l[i] = v;
         key[i] = order_key(v);
@@ -505,7 +511,116 @@ __device__ void group_block(const DecodeArgs &a, int tid, unsigned char *lds) {
     for (int i = tid; i < P; i += WG) st_dev(a.pairs + i, (int32_t)pl[i]);
 }
 
+// x of token t in the grouped kernels' B-operand form (whole WG; d <= 4096:
+// one word pair per thread).
+__device__ void xb_row(const DecodeArgs &a, int t, int tid) {
+    const int d = a.d, NC = d >> 4;
+    const uint4 *xrow = reinterpret_cast<const uint4 *>(a.x + (size_t)t * d);
+    uint4 xv0 = make_uint4(0, 0, 0, 0), xv1 = xv0;
+    if (tid < NC) {
+        xv0 = xrow[2 * tid];
+        xv1 = xrow[2 * tid + 1];
+    }
+    uint4 *row = a.xb + (size_t)t * xb_row_u4(d);
+    float X = 0.f, C = 0.f;
+    if (tid < NC) xb_produce(xv0, xv1, row, tid, X, C);
+    // a group is four word pairs: lanes 4g .. 4g+3
+    X += dpp_f<DPP_XOR1>(X);
+    C += dpp_f<DPP_XOR1>(C);
+    X += dpp_f<DPP_XOR2>(X);
+    C += dpp_f<DPP_XOR2>(C);
+    if (tid < NC && !(tid & 3)) reinterpret_cast<float2 *>(row + d / 8)[tid >> 2] = make_float2(X, C);
+}
+
+// After a token's top-k in a grouped step: the step's ticket; the last
+// token's workgroup groups the pairs by expert.
+__device__ void group_after_topk(const DecodeArgs &a, int tid, unsigned char *lds) {
+    stores_done();
+    lds_barrier();
+    if (tid == 0) {
+        const uint32_t old = atomicAdd(a.hdr + hdr_ticket(a.T), 1u);
+        reinterpret_cast<int *>(lds)[0] = old == (uint32_t)(a.T - 1);
+    }
+    lds_barrier();
+    if (!reinterpret_cast<int *>(lds)[0]) return;
+    if (tid == 0) st_dev(a.hdr + hdr_ticket(a.T), 0u);
+    group_block(a, tid, lds);
+}
+
+// ----------------------------------------------------- grouped router
+// Router logits of a grouped step on the matrix cores, in fp64:
+// l[t][e] = sum_k w[e][k] x[t][k] with w = s q + b dequantised exactly in fp64
+// (s q has at most 19 significant bits and every term is a multiple of
+// 2^-24 below 2^24, so the sum is exact) and x exact; every product is
+// exact, only the fp64 sums round.  v_mfma_f64_16x16x4_f64 takes A[e][k]
+// from lane l as A[l % 16][l / 16] and B[k][t] as B[l / 16][l % 16], and
+// leaves D[l / 16 + 4 r][l % 16] in slot r of lane l (rows interleaved, unlike
+// the fp32 16x16 layout).  Workgroup: a tile
+// of 16 experts x 16 tokens over one of nkr K ranges, the range split in
+// four between the waves; the wave sums are added in wave order and the
+// ranges' partial logits part[kr][t][e] in range order by the top-k.
+typedef double v4d __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void k_router_mm(DecodeArgs a) {
+    __shared__ v4d red[3][64];
+    const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
+    const int ebn = (a.E + 15) >> 4;
+    int b = blockIdx.x;
+    const int kr = b % a.nkr;
+    b /= a.nkr;
+    const int eb = b % ebn, tb = b / ebn;
+    const int d = a.d, NC = d >> 4, G = d >> 6;   // 16-column chunks, groups
+    const int pidx = 4 * kr + w, parts = 4 * a.nkr;
+    const int c0 = (int)((long)NC * pidx / parts), c1 = (int)((long)NC * (pidx + 1) / parts);
+    const int i = lane & 15, kq = lane >> 4;
+    const int e = min(16 * eb + i, a.E - 1), t = min(16 * tb + i, a.T - 1);   // clamped: not stored
+    const uint8_t *qrow = a.rq + (size_t)e * d;
+    const uint16_t *srow = a.rs + (size_t)e * G, *brow = a.rb + (size_t)e * G;
+    const uint16_t *xrow = a.x + (size_t)t * d;
+    v4d acc = {0.0, 0.0, 0.0, 0.0};
+    for (int c = c0; c < c1; ++c) {
+        const uint4 qv = *reinterpret_cast<const uint4 *>(qrow + 16 * c);
+        const uint4 x0 = *reinterpret_cast<const uint4 *>(xrow + 16 * c);
+        const uint4 x1 = *reinterpret_cast<const uint4 *>(xrow + 16 * c + 8);
+        const double sc = (double)h2f(srow[c >> 2]), bi = (double)h2f(brow[c >> 2]);
+        const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+        const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+            // this lane's column k = 16 c + 4 s4 + kq
+            const int kk = 4 * s4 + kq;
+            const uint32_t code = (qw[kk >> 2] >> (8 * (kk & 3))) & 0xFFu;
+            const uint16_t xh = (uint16_t)(xw[kk >> 1] >> (16 * (kk & 1)));
+            const double wv = fma(sc, (double)code, bi);
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64(wv, (double)h2f(xh), acc, 0, 0, 0);
+        }
+    }
+    if (w > 0) red[w - 1][lane] = acc;
+    lds_barrier();
+    if (w == 0) {
+        const v4d s = ((acc + red[0][lane]) + red[1][lane]) + red[2][lane];
+        const int tt = 16 * tb + i;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int ee = 16 * eb + kq + 4 * r;
+            if (tt < a.T && ee < a.E) a.part[((size_t)kr * a.T + tt) * a.E + ee] = s[r];
+        }
+    }
+}
+
+// One workgroup per token of a grouped step: x in B-operand form (decode
+// steps), top-k and softmax from the partial logits, then the grouping by
+// the last token's workgroup.
+__global__ __launch_bounds__(256) void k_router_topk(DecodeArgs a) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int t = blockIdx.x, tid = threadIdx.x;
+    if (a.xb) xb_row(a, t, tid);
+    topk_block(a, t, tid, lds);
+    if (a.do_group) group_after_topk(a, tid, lds);
+}
+
 // ------------------------------------------------------------- router
+// ROUTER_ROWS router rows per workgroup// ------------------------------------------------------------- router
 // ROUTER_ROWS router rows per workgroup, two waves per row: lane r of a row
 // (0..127) takes the 16-element chunks r and r + 128, reading its codes and
 // its x straight into registers.  Logit of expert e: sum over chunks of
@@ -535,22 +650,7 @@ __device__ void router_block(const DecodeArgs &a, int b, int tid, unsigned char 
     }
     double *part = reinterpret_cast<double *>(lds);   // [4] wave sums
     int *flag = reinterpret_cast<int *>(part + 4);
-    if (a.xb && b == t * nrb) {   // the token's first router workgroup: x in B-operand form
-        uint4 xv0 = make_uint4(0, 0, 0, 0), xv1 = xv0;
-        if (tid < NC) {
-            xv0 = xrow[2 * tid];
-            xv1 = xrow[2 * tid + 1];
-        }
-        uint4 *row = a.xb + (size_t)t * xb_row_u4(d);
-        float X = 0.f, C = 0.f;
-        if (tid < NC) xb_produce(xv0, xv1, row, tid, X, C);
-        // a group is four word pairs: lanes 4g .. 4g+3
-        X += dpp_f<DPP_XOR1>(X);
-        C += dpp_f<DPP_XOR1>(C);
-        X += dpp_f<DPP_XOR2>(X);
-        C += dpp_f<DPP_XOR2>(C);
-        if (tid < NC && !(tid & 3)) reinterpret_cast<float2 *>(row + d / 8)[tid >> 2] = make_float2(X, C);
-    }
+    if (a.xb && b == t * nrb) xb_row(a, t, tid);   // the token's first router workgroup
     double acc = 0.0;
 #pragma unroll
     for (int j = 0; j < JR; ++j) {
@@ -584,17 +684,7 @@ __device__ void router_block(const DecodeArgs &a, int b, int tid, unsigned char 
     if (!*flag) return;
     if (tid == 0) st_dev(a.hdr + hdr_ticket(t), 0u);
     topk_block(a, t, tid, lds);
-    if (!a.do_group || a.T == 1) return;
-    stores_done();
-    lds_barrier();
-    if (tid == 0) {
-        const uint32_t old = atomicAdd(a.hdr + hdr_ticket(a.T), 1u);
-        reinterpret_cast<int *>(lds)[0] = old == (uint32_t)(a.T - 1);
-    }
-    lds_barrier();
-    if (!reinterpret_cast<int *>(lds)[0]) return;
-    if (tid == 0) st_dev(a.hdr + hdr_ticket(a.T), 0u);
-    group_block(a, tid, lds);
+    if (a.do_group && a.T > 1) group_after_topk(a, tid, lds);
 }
 
 // ------------------------------------------------------- gate/up block
@@ -1107,6 +1197,23 @@ hipError_t tf_launch_decode(const DecodeArgs &a, int which, hipStream_t s) {
 #undef TF_CALL_C
     }
     return e;
+}
+
+int tf_router_nkr(int T, int E) {
+    // enough K ranges for about 256 workgroups, at most 16
+    const int tiles = ((E + 15) / 16) * ((T + 15) / 16);
+    int n = (256 + tiles - 1) / tiles;
+    return n < 1 ? 1 : n > 16 ? 16 : n;
+}
+
+hipError_t tf_launch_router_grouped(const DecodeArgs &a, hipStream_t s) {
+    const int tiles = ((a.E + 15) / 16) * ((a.T + 15) / 16);
+    TF_LAUNCH(TF_KERNEL_ROUTER_SHARED_GATEUP, k_router_mm, dim3(tiles * a.nkr), dim3(WG), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int lds = max(topk_lds_bytes(a.E), a.do_group ? group_lds_bytes(a.E, a.T) : 0);
+    TF_LAUNCH(TF_KERNEL_ROUTER_TOPK, k_router_topk, dim3(a.T), dim3(WG), lds, s, a);
+    return hipGetLastError();
 }
 
 hipError_t tf_launch_group(const DecodeArgs &a, hipStream_t s) {

@@ -41,6 +41,8 @@ struct DecodeArgs {
     int32_t *ids;
     float *weights;
     double *logits;
+    double *part;                // grouped steps: partial logits [nkr][T][E] (NULL otherwise)
+    int nkr;                     // their number of K ranges
     uint16_t *y;
     float *y32;
     uint32_t *hdr;
@@ -74,6 +76,12 @@ struct DecodeArgs {
 hipError_t tf_launch_decode(const DecodeArgs &a, int which, hipStream_t s);
 // Grouping alone (one workgroup): pairs, item records, counts and offsets.
 hipError_t tf_launch_group(const DecodeArgs &a, hipStream_t s);
+// Router of a grouped step (T >= 2) on the matrix cores: partial fp64 logits
+// over nkr K ranges, then one workgroup per token (top-k, softmax, x in
+// B-operand form for decode steps) and the grouping by the last of them.
+hipError_t tf_launch_router_grouped(const DecodeArgs &a, hipStream_t s);
+// K ranges of the grouped router for a step of T tokens over E experts.
+int tf_router_nkr(int T, int E);
 // Prefill combine: y = y_s + sum over ranks of y_e -> fp16.
 hipError_t tf_launch_prefill_combine(const DecodeArgs &a, hipStream_t s);
 // Grouped steps (prefill, decode of more than one token) on the matrix cores

@@ -304,7 +304,8 @@ tf_status tf_sample(const float *logits, int32_t V, int32_t T, float temperature
 /* ------------------------------------------------------------ profiling */
 /* Kernel ids of the hot path (for tf_profile_kernel). */
 enum {
-    TF_KERNEL_ROUTER_SHARED_GATEUP = 1,      /* decode A: router + top-k + shared gate/up */
+    TF_KERNEL_ROUTER_SHARED_GATEUP = 1,      /* decode A: router + top-k + shared gate/up;
+                                                grouped steps: the router GEMM            */
     TF_KERNEL_ROUTED_GATEUP_SHARED_DOWN = 2, /* decode B: routed gate/up + shared down    */
     TF_KERNEL_DOWN_COMBINE = 4,              /* decode C: routed down + combine -> y      */
     TF_KERNEL_PREFILL_DOWN = 8,              /* prefill: shared and per-item down (MFMA)  */
@@ -314,7 +315,8 @@ enum {
     TF_KERNEL_SAMPLE_PART = 128,             /* tf_sample: per-slice 64 largest keys      */
     TF_KERNEL_SAMPLE_FINAL = 256,            /* tf_sample: row merge, softmax, draw       */
     TF_KERNEL_ATTN_CHUNK = 512,              /* tf_attn_decode: per-chunk partials        */
-    TF_KERNEL_ATTN_COMBINE = 1024            /* tf_attn_decode: merge per query head      */
+    TF_KERNEL_ATTN_COMBINE = 1024,           /* tf_attn_decode: merge per query head      */
+    TF_KERNEL_ROUTER_TOPK = 2048             /* grouped steps: per-token top-k + grouping  */
 };
 /* Arm a one-shot timer: the next launch, by this host thread, of the named
  * kernel goes through hipExtLaunchKernel with `start` recorded when the

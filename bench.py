@@ -124,13 +124,16 @@ def _profile(lib, h, kernels, step, steps, stream):
                 _lib.check(lib.tf_profile_kernel(kid, a, b))
                 step(i)
         torch.cuda.synchronize()
+        _lib.check(lib.tf_profile_kernel(0, None, None))   # disarm
         durs = []
         for a, b in evs:
             v = ctypes.c_float()
-            assert h.hipEventElapsedTime(ctypes.byref(v), a, b) == 0
-            durs.append(v.value * 1e3)
+            if h.hipEventElapsedTime(ctypes.byref(v), a, b) == 0:
+                durs.append(v.value * 1e3)
             h.hipEventDestroy(a)
             h.hipEventDestroy(b)
+        if not durs:
+            raise RuntimeError(f"kernel {name} did not run in the profiled steps")
         durs.sort()
         out[name] = {"avg_us": round(sum(durs) / len(durs), 3),
                      "median_us": round(durs[len(durs) // 2], 3), "min_us": round(durs[0], 3),
@@ -255,8 +258,7 @@ def run_stack_batch(args, wl, layers, B, lib, dev, roofline):
                  _lib.TF_KERNEL_DOWN_COMBINE: "k_stage_c1"}
         gemv = {"k_stage_b": stage_b_bytes(d, f, fs, k)}
     else:
-        names = {_lib.TF_KERNEL_ROUTER_SHARED_GATEUP: "k_router_mm",
-                 _lib.TF_KERNEL_ROUTER_TOPK: "k_router_topk",
+        names = {_lib.TF_KERNEL_ROUTER_SHARED_GATEUP: "k_stage_a",
                  _lib.TF_KERNEL_PREFILL_GATEUP: "k_gu",
                  _lib.TF_KERNEL_PREFILL_DOWN: "k_dn",
                  _lib.TF_KERNEL_PREFILL_COMBINE: "k_pf_combine"}

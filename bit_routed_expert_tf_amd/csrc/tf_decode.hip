@@ -560,6 +560,7 @@ __device__ void group_after_topk(const DecodeArgs &a, int tid, unsigned char *ld
 // four between the waves; the wave sums are added in wave order and the
 // ranges' partial logits part[kr][t][e] in range order by the top-k.
 typedef double v4d __attribute__((ext_vector_type(4)));
+constexpr int RMM_CHUNKS = 4;   // 16-column chunks per wave at most
 
 __global__ __launch_bounds__(256) void k_router_mm(DecodeArgs a) {
     __shared__ v4d red[3][64];
@@ -578,13 +579,25 @@ __global__ __launch_bounds__(256) void k_router_mm(DecodeArgs a) {
     const uint16_t *srow = a.rs + (size_t)e * G, *brow = a.rb + (size_t)e * G;
     const uint16_t *xrow = a.x + (size_t)t * d;
     v4d acc = {0.0, 0.0, 0.0, 0.0};
-    for (int c = c0; c < c1; ++c) {
-        const uint4 qv = *reinterpret_cast<const uint4 *>(qrow + 16 * c);
-        const uint4 x0 = *reinterpret_cast<const uint4 *>(xrow + 16 * c);
-        const uint4 x1 = *reinterpret_cast<const uint4 *>(xrow + 16 * c + 8);
-        const double sc = (double)h2f(srow[c >> 2]), bi = (double)h2f(brow[c >> 2]);
-        const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
-        const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    // a wave's chunks (at most RMM_CHUNKS, see tf_router_nkr): every load in
+    // flight before the first MFMA
+    uint4 qv[RMM_CHUNKS], x0[RMM_CHUNKS], x1[RMM_CHUNKS];
+    uint16_t sh[RMM_CHUNKS], bh[RMM_CHUNKS];
+#pragma unroll
+    for (int u = 0; u < RMM_CHUNKS; ++u) {
+        const int c = min(c0 + u, NC - 1);
+        qv[u] = *reinterpret_cast<const uint4 *>(qrow + 16 * c);
+        x0[u] = *reinterpret_cast<const uint4 *>(xrow + 16 * c);
+        x1[u] = *reinterpret_cast<const uint4 *>(xrow + 16 * c + 8);
+        sh[u] = srow[c >> 2];
+        bh[u] = brow[c >> 2];
+    }
+#pragma unroll
+    for (int u = 0; u < RMM_CHUNKS; ++u) {
+        if (c0 + u >= c1) break;   // uniform
+        const double sc = (double)h2f(sh[u]), bi = (double)h2f(bh[u]);
+        const uint32_t qw[4] = {qv[u].x, qv[u].y, qv[u].z, qv[u].w};
+        const uint32_t xw[8] = {x0[u].x, x0[u].y, x0[u].z, x0[u].w, x1[u].x, x1[u].y, x1[u].z, x1[u].w};
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
             // this lane's column k = 16 c + 4 s4 + kq
@@ -1199,11 +1212,9 @@ hipError_t tf_launch_decode(const DecodeArgs &a, int which, hipStream_t s) {
     return e;
 }
 
-int tf_router_nkr(int T, int E) {
-    // enough K ranges for about 256 workgroups, at most 16
-    const int tiles = ((E + 15) / 16) * ((T + 15) / 16);
-    int n = (256 + tiles - 1) / tiles;
-    return n < 1 ? 1 : n > 16 ? 16 : n;
+int tf_router_nkr(int d) {
+    // K ranges of four waves each, every wave at most RMM_CHUNKS 16-column chunks
+    return (d / 16 + 4 * RMM_CHUNKS - 1) / (4 * RMM_CHUNKS);
 }
 
 hipError_t tf_launch_router_grouped(const DecodeArgs &a, hipStream_t s) {

@@ -80,8 +80,8 @@ hipError_t tf_launch_group(const DecodeArgs &a, hipStream_t s);
 // over nkr K ranges, then one workgroup per token (top-k, softmax, x in
 // B-operand form for decode steps) and the grouping by the last of them.
 hipError_t tf_launch_router_grouped(const DecodeArgs &a, hipStream_t s);
-// K ranges of the grouped router for a step of T tokens over E experts.
-int tf_router_nkr(int T, int E);
+// K ranges of the grouped router for d_model d.
+int tf_router_nkr(int d);
 // Prefill combine: y = y_s + sum over ranks of y_e -> fp16.
 hipError_t tf_launch_prefill_combine(const DecodeArgs &a, hipStream_t s);
 // Grouped steps (prefill, decode of more than one token) on the matrix cores

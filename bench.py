@@ -578,17 +578,21 @@ def run_slot(args):
                       "fill_h2d_bytes": filled})
         return r
 
-    base = one(S, "lfu")
+    base = one(S, "lfu", engine=args.slot_engine)
     out = {"metric": "slot-cache stack decode tokens/s (30 layers, 16 slots, PCIe misses)",
            "workload": wl.name, "tokens": ntok, "value": base["value"], "unit": "tokens/s",
+           "copy_engine": args.slot_engine,
            "hit_rate": base["hit_rate"], "h2d_bytes": base["h2d_bytes"],
            "h2d_GBps": base["h2d_GBps"], "pinned_h2d_peak_GBps": round(peak, 2),
            "setup_s": round(setup, 1), "wall_s": base["wall_s"]}
     if args.prefetch:     # speculative fill of the next layer's predicted experts
         out["prefetch"] = [one(S, "lfu", "exact"), one(S, "lfu", "noisy"),
                            one(S, "lfu", None, "dma"), one(S, "lfu", "exact", "dma")]
+    if args.slot_engines:   # the other copy engines on the same stream
+        out["engines"] = [one(S, "lfu", None, e) for e in ("device", "kernel", "dma")
+                          if e != args.slot_engine]
     if args.slot_sweep:   # slot counts x policies (the LFU reading and the LRU gloss)
-        out["sweep"] = [one(n, pol) for n in (8, 16, 32) for pol in ("lfu", "lru")
+        out["sweep"] = [one(n, pol, None, args.slot_engine) for n in (8, 16, 32) for pol in ("lfu", "lru")
                         if not (n == S and pol == "lfu")] + [dict(base)]
     return out
 
@@ -724,6 +728,11 @@ def main():
     ap.add_argument("--prefetch", action="store_true",
                     help="slot-cache workload: also run with the next layer's experts "
                          "prefetched (exact predictions, and half of them wrong)")
+    ap.add_argument("--slot-engine", choices=["device", "kernel", "dma"], default="device",
+                    help="copy engine of the slot-cache fills (device: the fill kernel reads "
+                         "the miss list on the GPU)")
+    ap.add_argument("--slot-engines", action="store_true",
+                    help="slot-cache workload: also run the other copy engines")
     ap.add_argument("--slot-sweep", action="store_true",
                     help="slot-cache workload: also run 8, 16 and 32 slots under LFU and LRU")
     ap.add_argument("--workload", choices=list(DEFAULT_STEPS), default="stack",

@@ -28,7 +28,7 @@ TF_KERNEL_SAMPLE_PART, TF_KERNEL_SAMPLE_FINAL = 128, 256
 TF_KERNEL_ATTN_CHUNK, TF_KERNEL_ATTN_COMBINE = 512, 1024
 TF_KERNEL_ROUTER_TOPK = 2048
 TF_SLOT_LFU, TF_SLOT_LRU = 0, 1
-TF_SLOT_COPY_DMA, TF_SLOT_COPY_KERNEL = 0, 1
+TF_SLOT_COPY_DMA, TF_SLOT_COPY_KERNEL, TF_SLOT_COPY_DEVICE = 0, 1, 2
 
 c_void_p, c_int32, c_int64, c_size_t = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 

@@ -325,8 +325,10 @@ class SlotCache:
 
     def set_copy_engine(self, engine):
         """"kernel" (one launch per fill or prefetch reading the mapped host
-        pool, the default) or "dma" (one hipMemcpyAsync per blob)."""
-        code = {"dma": _lib.TF_SLOT_COPY_DMA, "kernel": _lib.TF_SLOT_COPY_KERNEL}[engine]
+        pool, the default), "dma" (one hipMemcpyAsync per blob) or "device"
+        (the fill kernel reads the miss list on the GPU: no host wait)."""
+        code = {"dma": _lib.TF_SLOT_COPY_DMA, "kernel": _lib.TF_SLOT_COPY_KERNEL,
+                "device": _lib.TF_SLOT_COPY_DEVICE}[engine]
         check(load().tf_slot_cache_set_copy_engine(self.handle, code))
 
     def set_prefetch(self, buffers, n_buffers):

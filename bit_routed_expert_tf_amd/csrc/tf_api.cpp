@@ -370,6 +370,36 @@ tf_status tf_moe_layer_fwd(const tf_moe_layer *L, const uint16_t *x, int32_t T,
         return e == hipSuccess ? TF_OK : hip_fail(e, "decode launch");
     }
 
+    if (tf_slot_device_engine(cache)) {
+        // Planned and filled on the GPU, all on `compute`: router + top-k +
+        // lookup | miss copies beside the shared gate/up | routed gate/up +
+        // shared down | routed down + combine.
+        SlotFused sf;
+        st = tf_slot_fused_begin(cache, layer, compute, &sf);
+        if (st) return st;
+        a.sc = sf.d;
+        a.sc_layer = layer;
+        a.sc_host = sf.host_layer;
+        a.sc_slots = sf.slot_layer;
+        a.a_router_blocks = n_router;
+        e = tf_launch_decode(a, STAGE_A, compute);
+        if (e != hipSuccess) return hip_fail(e, "router launch");
+        a.a_router_blocks = 0;
+        a.a_shared_blocks = n_shared_a;
+        a.copy_per = SLOT_COPY_WGS_PER_BLOB;
+        a.a_copy_blocks = a.k * a.copy_per;
+        e = tf_launch_decode(a, STAGE_A, compute);
+        if (e != hipSuccess) return hip_fail(e, "copy + shared-branch launch");
+        a.a_shared_blocks = 0;
+        a.a_copy_blocks = 0;
+        a.slot_map = tf_slot_map(cache, layer);
+        a.pool = tf_slot_pool(cache, layer);
+        a.b_routed_blocks = n_routed_b;
+        a.b_shared_blocks = n_shared_b;
+        e = tf_launch_decode(a, STAGE_B | STAGE_C, compute);
+        return e == hipSuccess ? TF_OK : hip_fail(e, "routed launch");
+    }
+
     // Slot-cache path: router -> lookup -> shared branch (runs while the host
     // waits for the miss list and the copies run) -> routed experts.
     a.a_router_blocks = n_router;

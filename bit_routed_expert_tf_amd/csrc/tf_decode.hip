@@ -698,6 +698,10 @@ __device__ void router_block(const DecodeArgs &a, int b, int tid, unsigned char 
     if (tid == 0) st_dev(a.hdr + hdr_ticket(t), 0u);
     topk_block(a, t, tid, lds);
     if (a.do_group && a.T > 1) group_after_topk(a, tid, lds);
+    if (a.sc.slot_of && tid < WAVE) {   // one token: the slot lookup of its ids (rank order)
+        const int *sel = reinterpret_cast<const int *>(lds + 16 * (size_t)a.E);
+        slotk::lookup_wave(a.sc, a.sc_layer, sel, a.k, nullptr, false, tid);
+    }
 }
 
 // ------------------------------------------------------- gate/up block
@@ -872,7 +876,15 @@ __device__ void shared_down_block(const DecodeArgs &a, int b, int tid, unsigned 
 template <int LPR, int J>
 __global__ __launch_bounds__(256, 4) void k_stage_a(DecodeArgs a) {
     extern __shared__ __align__(16) unsigned char lds[];
-    const int b = blockIdx.x, tid = threadIdx.x;
+    const int tid = threadIdx.x;
+    int b = blockIdx.x;
+    if (b < a.a_copy_blocks) {   // the slot-cache miss copies, first so that they start first
+        const int r = b / a.copy_per;
+        slotk::copy_missed(a.sc.miss_gpu + (size_t)a.sc_layer * (1 + 2 * a.k), a.sc_host, a.sc_slots,
+                           a.stride, a.E, a.sc.S, a.sc.nfill, r, b - r * a.copy_per, a.copy_per, tid);
+        return;
+    }
+    b -= a.a_copy_blocks;
     if (b < a.a_router_blocks)
         router_block(a, b, tid, lds);
     else
@@ -1120,7 +1132,7 @@ int lds_c1(const DecodeArgs &a) { return 4 * 4 * 8 * (a.f >> 6) + hst_bytes(a.f)
 template <int LPR, int J>
 hipError_t launch_ab(const DecodeArgs &a, int which, hipStream_t s) {
     if (which & STAGE_A) {
-        const int n = a.a_router_blocks + a.a_shared_blocks;
+        const int n = a.a_copy_blocks + a.a_router_blocks + a.a_shared_blocks;
         if (n)
             TF_LAUNCH(TF_KERNEL_ROUTER_SHARED_GATEUP, (k_stage_a<LPR, J>), dim3(n), dim3(WG),
                       lds_a(a, LPR), s, a);

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "../../include/tf.h"
+#include "tf_slot_dev.h"
 
 // Workspace header words (uint32): device-side flags, the number of expert
 // work items of the current step, then one ticket per token and one for the
@@ -26,6 +27,7 @@ __host__ __device__ constexpr size_t h_row_bytes(int K) { return (size_t)160 * (
 constexpr int MAX_DECODE_T = 16;  // tokens per decode step
 constexpr int MAX_PREFILL_T = 128;  // tokens per prefill chunk
 constexpr int MAX_TB = 4;         // tokens staged per pass of a gate/up block
+constexpr int SLOT_COPY_WGS_PER_BLOB = 16;   // miss copies over PCIe inside a decode step
 constexpr int ITEM_INTS = 16;     // ints per expert item record (see group_block)
 
 struct DecodeArgs {
@@ -71,6 +73,14 @@ struct DecodeArgs {
     const int32_t *gemv_slot, *gemv_token;
     const float *gemv_coef;
     int P;
+    // slot-cache step planned on the GPU (sc.slot_of != NULL, one token): the
+    // router's top-k workgroup also looks the ids up in layer sc_layer of the
+    // cache; stage A's first a_copy_blocks workgroups (copy_per per rank of
+    // the miss list) copy the missed blobs from sc_host into sc_slots
+    SlotDev sc;
+    int sc_layer, a_copy_blocks, copy_per;
+    const uint8_t *sc_host;
+    uint8_t *sc_slots;
 };
 
 hipError_t tf_launch_decode(const DecodeArgs &a, int which, hipStream_t s);

@@ -14,7 +14,10 @@
 // experts it predicts for a layer into per-layer buffers ahead of that
 // layer's lookup (speculative fill, after the pages' read-ahead); the fill
 // then takes each predicted miss from its buffer.  Predictions never change
-// the hit/miss sequence.
+// the hit/miss sequence.  With the device copy engine the host is out of the
+// loop: the lookup also leaves the miss list in device memory, and a copy
+// kernel queued behind the lookup on the copy stream reads it and moves the
+// missed blobs.
 //
 // Policy (reading of "LFU"): a slot's count is 1 on fill and +1 per hit; the
 // token's own ids are pinned; misses are taken in rank order; the victim is
@@ -31,21 +34,7 @@
 #include <vector>
 
 #include "tf_slot.h"
-
-// Plain device view of the tables (passed to the lookup kernel by value).
-struct SlotDev {
-    int L, E, S, k;
-    int policy;                // TF_SLOT_LFU or TF_SLOT_LRU
-    int64_t trace_cap;
-    int32_t *slot_of;          // [L][E]  -1 = not cached
-    int16_t *expert_of;        // [L][S]  -1 = empty
-    uint32_t *count;           // [L][S]
-    uint32_t *last;            // [L][S]  last-use token
-    uint32_t *tok;             // [L]     tokens seen
-    int8_t *trace_hit;         // [L][cap*k]
-    int16_t *trace_slot;       // [L][cap*k]
-    int32_t *miss_dev;         // [L][1+2k] device alias of the mapped pinned miss list
-};
+#include "tf_slot_dev.h"
 
 struct tf_slot_cache {
     SlotDev d;
@@ -68,6 +57,9 @@ struct tf_slot_cache {
     int64_t pf_bytes = 0, pf_used = 0, pf_wasted = 0;
     const uint8_t *host_dev = nullptr;   // device mapping of host_pool (NULL: DMA only)
     int engine = TF_SLOT_COPY_KERNEL;   // DMA when the host pool has no mapping
+    std::vector<hipEvent_t> ev_dfill;    // [L] after the layer's latest device-initiated fill
+    std::vector<char> dfill_pending;     // [L] that fill may still run
+    bool dfill_any = false;              // some fill ran with TF_SLOT_COPY_DEVICE
 };
 
 namespace {
@@ -92,9 +84,7 @@ struct BlobCopies {
     const uint4 *src[MAX_COPIES];
     uint4 *dst[MAX_COPIES];
 };
-__global__ __launch_bounds__(256) void k_copy_blobs(BlobCopies c, size_t n16) {
-    const uint4 *src = c.src[blockIdx.y];
-    uint4 *dst = c.dst[blockIdx.y];
+__device__ __forceinline__ void copy_blob(const uint4 *src, uint4 *dst, size_t n16) {
     const size_t step = (size_t)gridDim.x * 256;
     for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += 4 * step) {
         uint4 v[4];
@@ -106,80 +96,25 @@ __global__ __launch_bounds__(256) void k_copy_blobs(BlobCopies c, size_t n16) {
             if (i + j * step < n16) dst[i + j * step] = v[j];
     }
 }
+__global__ __launch_bounds__(256) void k_copy_blobs(BlobCopies c, size_t n16) {
+    copy_blob(c.src[blockIdx.y], c.dst[blockIdx.y], n16);
+}
 
-// One token's lookup for one layer; a single lane walks the policy so that
-// the order of every decision is exactly the policy's order.
-__global__ __launch_bounds__(64) void k_lookup(SlotDev c, int layer, const int32_t *ids,
-                                               int n, int32_t *slots_out, uint32_t *flags) {
-    if (threadIdx.x != 0) return;
-    const int S = c.S, E = c.E;
-    int32_t *slot_of = c.slot_of + (size_t)layer * E;
-    int16_t *expert_of = c.expert_of + (size_t)layer * S;
-    uint32_t *count = c.count + (size_t)layer * S;
-    uint32_t *last = c.last + (size_t)layer * S;
-    int32_t *miss = c.miss_dev + (size_t)layer * (1 + 2 * c.k);
-    const uint32_t t = c.tok[layer];
-    int e_r[16], s_r[16];
-    bool hit[16];
-    uint32_t pinned = 0, fl = 0;
-    for (int r = 0; r < n; ++r) {
-        int e = ids[r];
-        if (e < 0 || e >= E) { fl |= TF_FLAG_ID_RANGE; e = e < 0 ? 0 : E - 1; }
-        for (int q = 0; q < r; ++q)
-            if (e_r[q] == e) fl |= TF_FLAG_ID_REPEAT;
-        e_r[r] = e;
-        const int s = slot_of[e];
-        hit[r] = s >= 0;
-        s_r[r] = s;
-        if (s >= 0) {               // hits first: they are pinned for this token
-            bool seen = (pinned >> s) & 1u;
-            if (!seen) { count[s] += 1; last[s] = t; }
-            pinned |= 1u << s;
-        }
-    }
-    int nm = 0;
-    for (int r = 0; r < n; ++r) {
-        if (hit[r]) continue;
-        const int e = e_r[r];
-        if (slot_of[e] >= 0) {      // repeated id already filled for this token
-            s_r[r] = slot_of[e];
-            continue;
-        }
-        int v = -1;
-        for (int s = 0; s < S; ++s)
-            if (expert_of[s] < 0) { v = s; break; }
-        if (v < 0) {
-            for (int s = 0; s < S; ++s) {
-                if ((pinned >> s) & 1u) continue;
-                if (v < 0) { v = s; continue; }   // the first unpinned slot
-                const bool lt = c.policy == TF_SLOT_LRU
-                                    ? last[s] < last[v]
-                                    : count[s] < count[v] || (count[s] == count[v] && last[s] < last[v]);
-                if (lt) v = s;
-            }
-            slot_of[expert_of[v]] = -1;
-        }
-        expert_of[v] = (int16_t)e;
-        slot_of[e] = v;
-        count[v] = 1;
-        last[v] = t;
-        pinned |= 1u << v;
-        s_r[r] = v;
-        miss[1 + 2 * nm] = e;
-        miss[2 + 2 * nm] = v;
-        ++nm;
-    }
-    miss[0] = nm;
-    if ((int64_t)t < c.trace_cap) {
-        int8_t *th = c.trace_hit + ((size_t)layer * c.trace_cap + t) * c.k;
-        int16_t *ts = c.trace_slot + ((size_t)layer * c.trace_cap + t) * c.k;
-        for (int r = 0; r < n; ++r) { th[r] = hit[r] ? 1 : 0; ts[r] = (int16_t)s_r[r]; }
-    }
-    if (slots_out)
-        for (int r = 0; r < n; ++r) slots_out[r] = s_r[r];
-    if (fl && flags) atomicOr(flags, fl);
-    c.tok[layer] = t + 1;
-    __threadfence_system();
+// Fill of one layer planned on the GPU: the miss list the lookup left in
+// device memory says which blobs to move, so the copy starts as soon as the
+// lookup ends, with no host round trip.  Miss blockIdx.y of the list.
+__global__ __launch_bounds__(256) void k_fill_listed(const int32_t *miss, const uint8_t *host_layer,
+                                                     uint8_t *slot_layer, size_t stride, int E, int S,
+                                                     unsigned long long *nfill) {
+    slotk::copy_missed(miss, host_layer, slot_layer, stride, E, S, nfill, blockIdx.y, blockIdx.x,
+                       gridDim.x, threadIdx.x);
+}
+
+// One token's lookup for one layer (one wave), the miss list also in the
+// mapped host memory for the host-driven fills.
+__global__ __launch_bounds__(64) void k_lookup(SlotDev c, int layer, const int32_t *ids, int n,
+                                               int32_t *slots_out) {
+    slotk::lookup_wave(c, layer, ids, n, slots_out, true, threadIdx.x);
 }
 
 }  // namespace
@@ -207,6 +142,21 @@ tf_status tf_slot_check_layer(const tf_slot_cache *c, const tf_moe_layer *L, int
 }
 
 hipEvent_t tf_slot_fill_event(tf_slot_cache *c) { return c->ev_fill; }
+bool tf_slot_device_engine(const tf_slot_cache *c) { return c->engine == TF_SLOT_COPY_DEVICE; }
+
+tf_status tf_slot_fused_begin(tf_slot_cache *c, int32_t layer, hipStream_t compute, SlotFused *out) {
+    if (c->pending[layer]) return fail(TF_E_STATE, "layer %d: previous lookup not filled", layer);
+    if (c->dfill_pending[layer]) {   // a standalone fill may still read the layer's miss list
+        const hipError_t e = hipStreamWaitEvent(compute, c->ev_dfill[layer], 0);
+        if (e != hipSuccess) return fail(TF_E_HIP, "slot step: %s", hipGetErrorString(e));
+        c->dfill_pending[layer] = 0;
+    }
+    out->d = c->d;
+    out->host_layer = c->host_dev + (size_t)layer * c->d.E * c->stride;
+    out->slot_layer = c->slot_pool + (size_t)layer * c->d.S * c->stride;
+    c->dfill_any = true;
+    return TF_OK;
+}
 const int32_t *tf_slot_map(const tf_slot_cache *c, int32_t layer) {
     return c->d.slot_of + (size_t)layer * c->d.E;
 }
@@ -220,7 +170,8 @@ static tf_status reset_tables(tf_slot_cache *c) {
     hipLaunchKernelGGL(k_fill16, dim3(256), dim3(256), 0, 0,
                        reinterpret_cast<int16_t *>(c->d.slot_of), n16, (int16_t)-1);
     hipError_t e = hipGetLastError();
-    const size_t zbytes = (size_t)c->d.L * c->d.S * 8 + (size_t)c->d.L * 4;   // count, last, tok
+    // count, last, tok, the device miss lists and the fill counter
+    const size_t zbytes = reinterpret_cast<char *>(c->d.nfill + 1) - reinterpret_cast<char *>(c->d.count);
     if (e == hipSuccess) e = tf_launch_zero(c->d.count, (zbytes + 3) & ~size_t(3), 0);
     if (e == hipSuccess && c->d.trace_cap) {
         const size_t tb = (size_t)c->d.L * c->d.trace_cap * c->d.k;
@@ -234,6 +185,8 @@ static tf_status reset_tables(tf_slot_cache *c) {
     c->mirror.assign((size_t)c->d.L * c->d.S, -1);
     c->pf.assign((size_t)c->d.L * c->P, -1);
     c->pf_bytes = c->pf_used = c->pf_wasted = 0;
+    c->dfill_any = false;
+    for (auto &p : c->dfill_pending) p = 0;
     return TF_OK;
 }
 
@@ -290,7 +243,9 @@ tf_status tf_slot_cache_create(int32_t n_layers, int32_t n_experts, int32_t n_sl
     const size_t o_count = up256(o_expert_of + 2 * (size_t)n_layers * n_slots);
     const size_t o_last = o_count + 4 * (size_t)n_layers * n_slots;
     const size_t o_tok = o_last + 4 * (size_t)n_layers * n_slots;
-    const size_t o_th = up256(o_tok + 4 * (size_t)n_layers);
+    const size_t o_miss = o_tok + 4 * (size_t)n_layers;
+    const size_t o_nfill = (o_miss + 4 * (size_t)n_layers * (1 + 2 * top_k) + 7) & ~size_t(7);
+    const size_t o_th = up256(o_nfill + 8);
     const size_t tb = (size_t)n_layers * trace_cap * top_k;
     const size_t o_ts = o_th + up256(tb);
     const size_t total = o_ts + up256(2 * tb) + 256;
@@ -302,6 +257,8 @@ tf_status tf_slot_cache_create(int32_t n_layers, int32_t n_experts, int32_t n_sl
     c->d.count = reinterpret_cast<uint32_t *>(b + o_count);
     c->d.last = reinterpret_cast<uint32_t *>(b + o_last);
     c->d.tok = reinterpret_cast<uint32_t *>(b + o_tok);
+    c->d.miss_gpu = reinterpret_cast<int32_t *>(b + o_miss);
+    c->d.nfill = reinterpret_cast<unsigned long long *>(b + o_nfill);
     c->d.trace_hit = reinterpret_cast<int8_t *>(b + o_th);
     c->d.trace_slot = reinterpret_cast<int16_t *>(b + o_ts);
     e = hipHostMalloc(reinterpret_cast<void **>(&c->miss_host),
@@ -345,6 +302,8 @@ void tf_slot_cache_destroy(tf_slot_cache *c) {
         if (ev) (void)hipEventDestroy(ev);
     for (auto ev : c->ev_done)
         if (ev) (void)hipEventDestroy(ev);
+    for (auto ev : c->ev_dfill)
+        if (ev) (void)hipEventDestroy(ev);
     if (c->ev_fill) (void)hipEventDestroy(c->ev_fill);
 
     if (c->miss_host) (void)hipHostFree(c->miss_host);
@@ -358,8 +317,12 @@ tf_status tf_slot_cache_lookup(tf_slot_cache *c, int32_t layer, const int32_t *i
     if (layer < 0 || layer >= c->d.L) return fail(TF_E_ARG, "layer %d out of range", layer);
     if (n != c->d.k) return fail(TF_E_ARG, "n must equal top_k (%d)", c->d.k);
     if (c->pending[layer]) return fail(TF_E_STATE, "layer %d: previous lookup not filled", layer);
-    hipLaunchKernelGGL(k_lookup, dim3(1), dim3(64), 0, compute, c->d, layer, ids, n, slots,
-                       static_cast<uint32_t *>(nullptr));
+    if (c->dfill_pending.size() && c->dfill_pending[layer]) {   // its miss list is still being read
+        const hipError_t w = hipStreamWaitEvent(compute, c->ev_dfill[layer], 0);
+        if (w != hipSuccess) return fail(TF_E_HIP, "lookup: %s", hipGetErrorString(w));
+        c->dfill_pending[layer] = 0;
+    }
+    hipLaunchKernelGGL(k_lookup, dim3(1), dim3(64), 0, compute, c->d, layer, ids, n, slots);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess) e = hipEventRecord(c->ev_lookup[layer], compute);
     if (e != hipSuccess) return fail(TF_E_HIP, "lookup: %s", hipGetErrorString(e));
@@ -372,6 +335,25 @@ tf_status tf_slot_cache_fill(tf_slot_cache *c, int32_t layer, hipStream_t copy, 
     if (!c) return fail(TF_E_ARG, "NULL cache");
     if (layer < 0 || layer >= c->d.L) return fail(TF_E_ARG, "layer %d out of range", layer);
     if (!c->pending[layer]) return fail(TF_E_STATE, "layer %d: fill without a lookup", layer);
+    if (c->engine == TF_SLOT_COPY_DEVICE) {
+        // the copy stream waits for the lookup on the GPU; the kernel reads the list itself
+        hipError_t e = hipStreamWaitEvent(copy, c->ev_lookup[layer], 0);
+        const size_t lay = (size_t)layer;
+        if (e == hipSuccess) {
+            hipLaunchKernelGGL(k_fill_listed, dim3(HOST_WGS_PER_BLOB, c->d.k), dim3(256), 0, copy,
+                               c->d.miss_gpu + lay * (1 + 2 * c->d.k), c->host_dev + lay * c->d.E * c->stride,
+                               c->slot_pool + lay * c->d.S * c->stride, c->stride, c->d.E, c->d.S, c->d.nfill);
+            e = hipGetLastError();
+        }
+        if (e == hipSuccess) e = hipEventRecord(c->ev_dfill[layer], copy);
+        if (e == hipSuccess && filled) e = hipEventRecord(filled, copy);
+        if (e != hipSuccess) return fail(TF_E_HIP, "device fill: %s", hipGetErrorString(e));
+        c->pending[layer] = 0;
+        c->dfill_pending[layer] = 1;
+        c->dfill_any = true;
+        if (n_miss_host) *n_miss_host = -1;
+        return TF_OK;
+    }
     hipError_t e = hipEventSynchronize(c->ev_lookup[layer]);
     if (e != hipSuccess) return fail(TF_E_HIP, "waiting for lookup: %s", hipGetErrorString(e));
     c->pending[layer] = 0;
@@ -433,6 +415,8 @@ tf_status tf_slot_cache_fill(tf_slot_cache *c, int32_t layer, hipStream_t copy, 
 tf_status tf_slot_cache_set_prefetch(tf_slot_cache *c, uint8_t *buffers, int32_t n_buffers) {
     if (!c) return fail(TF_E_ARG, "NULL cache");
     if (n_buffers < 0 || n_buffers > 16) return fail(TF_E_ARG, "n_buffers must be in [0, 16]");
+    if (n_buffers && c->engine == TF_SLOT_COPY_DEVICE)
+        return fail(TF_E_STATE, "prefetch needs a host-driven copy engine");
     if (n_buffers && !buffers) return fail(TF_E_ARG, "NULL buffers");
     if ((uintptr_t)buffers & 255) return fail(TF_E_ALIGN, "buffers 256-byte aligned");
     hipError_t e = hipSuccess;
@@ -500,10 +484,22 @@ tf_status tf_slot_cache_prefetch(tf_slot_cache *c, int32_t layer, const int32_t 
 
 tf_status tf_slot_cache_set_copy_engine(tf_slot_cache *c, int32_t engine) {
     if (!c) return fail(TF_E_ARG, "NULL cache");
-    if (engine != TF_SLOT_COPY_DMA && engine != TF_SLOT_COPY_KERNEL)
+    if (engine != TF_SLOT_COPY_DMA && engine != TF_SLOT_COPY_KERNEL && engine != TF_SLOT_COPY_DEVICE)
         return fail(TF_E_ARG, "unknown copy engine %d", engine);
-    if (engine == TF_SLOT_COPY_KERNEL && !c->host_dev)
+    if (engine != TF_SLOT_COPY_DMA && !c->host_dev)
         return fail(TF_E_STATE, "the host pool has no device mapping");
+    if (engine == TF_SLOT_COPY_DEVICE && c->P)
+        return fail(TF_E_STATE, "the device copy engine does not take prefetch buffers");
+    for (int l = 0; l < c->d.L; ++l)
+        if (c->pending[l]) return fail(TF_E_STATE, "layer %d: lookup not yet filled", l);
+    if (engine == TF_SLOT_COPY_DEVICE && c->ev_dfill.empty()) {
+        hipError_t e = hipSuccess;
+        c->ev_dfill.assign(c->d.L, nullptr);
+        for (int l = 0; l < c->d.L && e == hipSuccess; ++l)
+            e = hipEventCreateWithFlags(&c->ev_dfill[l], hipEventDisableTiming);
+        if (e != hipSuccess) return fail(TF_E_HIP, "fill events: %s", hipGetErrorString(e));
+        c->dfill_pending.assign(c->d.L, 0);
+    }
     c->engine = engine;
     return TF_OK;
 }
@@ -543,7 +539,15 @@ tf_status tf_slot_cache_reset(tf_slot_cache *c) {
     return reset_tables(c);
 }
 
-int64_t tf_slot_cache_bytes_filled(const tf_slot_cache *c) { return c ? c->bytes_filled : -1; }
+int64_t tf_slot_cache_bytes_filled(const tf_slot_cache *c) {
+    if (!c) return -1;
+    if (!c->dfill_any) return c->bytes_filled;
+    unsigned long long n = 0;   // device-initiated fills count their blobs on the GPU
+    if (hipDeviceSynchronize() != hipSuccess ||
+        hipMemcpy(&n, c->d.nfill, sizeof n, hipMemcpyDeviceToHost) != hipSuccess)
+        return -1;
+    return c->bytes_filled + (int64_t)n * (int64_t)c->stride;
+}
 
 tf_status tf_slot_cache_set_policy(tf_slot_cache *c, int32_t policy) {
     if (!c) return fail(TF_E_ARG, "NULL cache");

@@ -185,7 +185,12 @@ size_t tf_moe_workspace_bytes(const tf_moe_layer *L, int32_t T);
  *   cache non-NULL (T must be 1): the layer's routed experts are looked up in
  *     the slot cache; misses are copied from the pinned host pool on `copy`
  *     while the shared branch runs on `compute`.  [SYNC: waits once for the
- *     lookup result to issue the copies.]
+ *     lookup result to issue the copies.]  With the cache's copy engine set
+ *     to TF_SLOT_COPY_DEVICE the whole step runs on `compute` with no host
+ *     wait (`copy` is not used): the router's top-k workgroup does the
+ *     lookup, and the next launch copies the missed blobs (16 workgroups per
+ *     rank of the miss list, over the host pool's device mapping) beside the
+ *     shared gate/up.
  * Kernels: router+shared gate/up | (lookup) | routed gate/up + shared down |
  * routed down + combine. */
 tf_status tf_moe_layer_fwd(const tf_moe_layer *L, const uint16_t *x, int32_t T,
@@ -361,7 +366,10 @@ tf_status tf_slot_cache_lookup(tf_slot_cache *c, int32_t layer, const int32_t *i
 /* [SYNC] Wait for the last lookup of `layer`, copy each missed blob from the
  * host pool (or a prefetch buffer) into its slot on `copy` (see the copy
  * engine below), then record `filled` (may be NULL) on `copy`.
- * *n_miss_host receives the count. */
+ * *n_miss_host receives the count.  With TF_SLOT_COPY_DEVICE the call does
+ * not wait: `copy` waits for the lookup on the GPU, one kernel reads the
+ * miss list from device memory and moves the blobs, and *n_miss_host
+ * receives -1 (the count stays on the GPU; tf_slot_cache_trace has it). */
 tf_status tf_slot_cache_fill(tf_slot_cache *c, int32_t layer, hipStream_t copy,
                              hipEvent_t filled, int32_t *n_miss_host);
 /* [SYNC] Copy `layer`'s trace (hit flag, slot per token and rank) to the host.
@@ -371,7 +379,9 @@ tf_status tf_slot_cache_trace(tf_slot_cache *c, int32_t layer, int8_t *hit_host,
 /* [SYNC] Empty every layer and clear the traces. */
 tf_status tf_slot_cache_reset(tf_slot_cache *c);
 /* Total bytes copied host->device by fills since create/reset (misses served
- * from a prefetch buffer are device copies and do not count). */
+ * from a prefetch buffer are device copies and do not count).  [SYNC once a
+ * TF_SLOT_COPY_DEVICE fill has run: those fills count on the GPU.]  -1 on a
+ * NULL cache or a failed read. */
 int64_t tf_slot_cache_bytes_filled(const tf_slot_cache *c);
 
 /* Speculative fill (shengyayun.com AI newsletter of 2026-07-30, "事件与背景"
@@ -404,10 +414,20 @@ tf_status tf_slot_cache_prefetch_stats(const tf_slot_cache *c, int64_t *h2d_byte
  * host pool): one kernel launch per fill or prefetch reads every blob of the
  * call over PCIe through the mapping (16 workgroups per blob).
  * TF_SLOT_COPY_DMA (the default otherwise): one hipMemcpyAsync per blob.
+ * TF_SLOT_COPY_DEVICE: the fill is planned on the GPU too, with no host
+ * round trip.  tf_slot_cache_fill: the copy stream waits for the lookup, and
+ * one kernel of k x 16 workgroups reads the layer's miss list from device
+ * memory and copies the missed blobs over the mapping; the next lookup of
+ * the layer waits on the GPU for that fill.  tf_moe_layer_fwd: the lookup
+ * and the copies join the step's own launches (see there).  No prefetch
+ * with it (it keeps no host view of the slots).
  * Device copies out of prefetch buffers always run as a kernel.  TF_E_STATE
- * asks for the kernel engine on an unmapped pool; TF_E_ARG for an unknown
- * engine. */
-typedef enum { TF_SLOT_COPY_DMA = 0, TF_SLOT_COPY_KERNEL = 1 } tf_slot_copy_engine;
+ * asks for a kernel engine on an unmapped pool, for the device engine with
+ * prefetch buffers set, or for any change between a lookup and its fill;
+ * TF_E_ARG for an unknown engine. */
+typedef enum {
+    TF_SLOT_COPY_DMA = 0, TF_SLOT_COPY_KERNEL = 1, TF_SLOT_COPY_DEVICE = 2
+} tf_slot_copy_engine;
 tf_status tf_slot_cache_set_copy_engine(tf_slot_cache *c, int32_t engine);
 
 /* Eviction rule of later lookups (every layer).  TF_SLOT_LFU (the default,

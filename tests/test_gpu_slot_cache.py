@@ -139,10 +139,11 @@ def test_slot_cache_ragged_shapes(tfa):
     _run(tfa, 5, L=2, d=320, E=12, k=3, f=192, fs=320, S=5, T=40, check_tokens=[0, 39])
 
 
-@pytest.mark.parametrize("engine", ["dma", "kernel"])
+@pytest.mark.parametrize("engine", ["dma", "kernel", "device"])
 def test_slot_cache_full_width(tfa, engine):
     # the slot-cache workload's shapes (d=2816, 128 experts, top-8, 16 slots)
-    # on two layers and 48 tokens, blobs moved by the copy kernel or by DMA
+    # on two layers and 48 tokens, blobs moved by the copy kernel, by DMA or
+    # by the kernel that reads the miss list on the GPU
     print(f"slot cache: {engine} d=2816 E=128 k=8 f=704 fs=2816 S=16 L=2 T=48", flush=True)
     miss = _run(tfa, 2, L=2, d=2816, E=128, k=8, f=704, fs=2816, S=16, T=48,
                 check_tokens=[0, 47], engine=engine)
@@ -160,6 +161,54 @@ def test_slot_cache_policies_and_sizes(tfa, S, policy, E):
     miss = _run(tfa, 5, L=2, d=256, E=E, k=4, f=128, fs=256, S=S, T=96, check_tokens=[0, 95],
                 policy=policy)
     assert 0.0 < miss < 1.0
+
+
+@pytest.mark.parametrize("S,policy,E,L", [(8, "lfu", 32, 3), (32, "lru", 96, 2), (5, "lfu", 12, 2)])
+def test_slot_cache_device_engine(tfa, S, policy, E, L):
+    """Fills planned on the GPU (no host wait between lookup and copy): the
+    same hit/slot sequences, outputs and byte count as the host-driven fills."""
+    print(f"slot cache: device engine {policy} S={S} d=256 E={E} k=4 L={L} T=80", flush=True)
+    miss = _run(tfa, 8, L=L, d=256, E=E, k=4, f=128, fs=256, S=S, T=80, check_tokens=[0, 79],
+                policy=policy, engine="device")
+    assert 0.0 < miss < 1.0
+
+
+def test_slot_cache_engine_state(tfa):
+    """The device engine refuses prefetch buffers (and the reverse), and no
+    engine change is taken between a lookup and its fill."""
+    from bit_routed_expert_tf_amd import _lib
+    L, E, S, k, stride = 2, 16, 8, 4, 4096
+    host = tfa.pinned_host(L * E * stride)
+    host.copy_((torch.arange(host.numel()) % 251).to(torch.uint8))
+    pool = torch.zeros(L * S * stride, dtype=torch.uint8, device="cuda")
+    buf = torch.zeros(L * k * stride, dtype=torch.uint8, device="cuda")
+    cache = tfa.SlotCache(L, E, S, k, stride, pool, host, trace_cap=4)
+    cache.set_copy_engine("device")
+    with pytest.raises(_lib.TFError, match="host-driven"):
+        cache.set_prefetch(buf, k)
+    cache.set_copy_engine("kernel")
+    cache.set_prefetch(buf, k)
+    with pytest.raises(_lib.TFError, match="prefetch"):
+        cache.set_copy_engine("device")
+    cache.set_prefetch(buf, 0)
+    cache.set_copy_engine("device")
+    ids = torch.tensor([3, 1, 4, 9], dtype=torch.int32, device="cuda")
+    cache.lookup(0, ids)
+    with pytest.raises(_lib.TFError, match="not yet filled"):
+        cache.set_copy_engine("kernel")
+    assert cache.fill(0) == -1          # the count stays on the GPU
+    torch.cuda.synchronize()
+    assert cache.bytes_filled() == 4 * stride
+    cache.lookup(0, ids)                 # all four resident now
+    cache.fill(0)
+    torch.cuda.synchronize()
+    assert cache.bytes_filled() == 4 * stride
+    hit, slot = cache.trace(0, 2 * k)
+    assert hit.tolist() == [False] * 4 + [True] * 4 and slot.tolist() == [0, 1, 2, 3] * 2
+    assert torch.equal(pool[:4 * stride].cpu(),
+                       host[torch.cat([torch.arange(e * stride, (e + 1) * stride) for e in (3, 1, 4, 9)])])
+    assert _lib.TF_SLOT_COPY_DEVICE == 2
+    cache.close()
 
 
 @pytest.mark.parametrize("mode,engine,policy", [("exact", "kernel", "lfu"), ("noisy", "kernel", "lfu"),

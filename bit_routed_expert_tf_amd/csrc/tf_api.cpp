@@ -143,11 +143,11 @@ hipError_t grouped_step(const tf_moe_layer *L, const uint16_t *x, int T, const i
     a.h_r = at<uint4>(ws, w.hr);
     a.y_e = at<float>(ws, w.total);
     a.do_group = 1;
-    // decode steps (T <= 16): persistent units of up to four tokens, x staged
-    // in B-operand form by the router launch; prefill chunks: tiles of up to
-    // 16 tokens
+    // decode steps (T <= 16): persistent units of up to four tokens; prefill
+    // chunks: tiles of up to 16 tokens; both read x in B-operand form, staged
+    // by the router launch
     const bool tiles = T > MAX_DECODE_T;
-    a.xb = tiles ? nullptr : at<uint4>(ws, w.xb);
+    a.xb = at<uint4>(ws, w.xb);
     a.tbi = tiles ? 16 : 4;
     const int P = T * a.k;
     const int max_items = P < a.E + P / a.tbi ? P : a.E + P / a.tbi;

@@ -633,7 +633,7 @@ __global__ __launch_bounds__(256) void k_router_topk(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------- router
-// ROUTER_ROWS router rows per workgroup// ------------------------------------------------------------- router
+// ------------------------------------------------------------- router
 // ROUTER_ROWS router rows per workgroup, two waves per row: lane r of a row
 // (0..127) takes the 16-element chunks r and r + 128, reading its codes and
 // its x straight into registers.  Logit of expert e: sum over chunks of

@@ -99,7 +99,7 @@ hipError_t tf_launch_prefill_combine(const DecodeArgs &a, hipStream_t s);
 // the combine.
 hipError_t tf_launch_grouped(const DecodeArgs &a, int max_items, hipStream_t s);
 // The same for prefill chunks of more than 16 tokens: one workgroup per tile
-// of an item of at most 16 tokens (x read directly).
+// of an item of at most 16 tokens (x in B-operand form from the router launch).
 hipError_t tf_launch_prefill_tiles(const DecodeArgs &a, int max_items, hipStream_t s);
 // Lanes per weight row used by stages A and B for these shapes (8 or 16).
 int tf_decode_lpr(const DecodeArgs &a);

@@ -34,7 +34,7 @@
 // summed (DPP), in a fixed order.
 //
 // Work.  A workgroup owns 32 rows of gate and of up (waves 0/1 gate, 2/3 up)
-// or 64 rows of down, for one tile.  K goes through LDS in chunks of 8 groups
+// or 64 rows of down, for one tile.  K goes through LDS in chunks of KC_GU / KC_DN groups
 // (activations and scale/bias as fp32), loaded into registers one chunk
 // ahead; each lane's codes (64 bytes per chunk) are reloaded for the next
 // chunk as soon as a round has used them.
@@ -51,7 +51,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int TT = 16;    // tokens per tile (the MFMA's N)
-constexpr int KCH = 8;    // groups per staged K chunk (512 columns)
+constexpr int KC_GU = 8;  // groups per staged K chunk: gate/up (512 columns of d)
+constexpr int KC_DN = 4;  // down (256 columns of d_ff; 704 = 11 groups)
 
 // Hidden rows between the grouped gate/up and down launches, F values:
 // word pairs (16 values) of 64 bytes [part hi: even | odd/16][part lo:
@@ -94,7 +95,7 @@ __device__ __forceinline__ float hsum2(uint32_t p) {
     return h2f((uint16_t)(p & 0xFFFF)) + h2f((uint16_t)(p >> 16));
 }
 
-template <int PARTS, int R>
+template <int PARTS, int R, int KC>
 struct MQLds {
     int src[TT], dst[TT];
     float coef[TT];
@@ -102,9 +103,9 @@ struct MQLds {
     // the chunk's activations: [token][word pair][part][even | odd/16], one
     // 16-byte entry each; rows padded so that the 16 tokens of a B read fall
     // on different banks
-    uint4 xs[TT][KCH * 4 * PARTS * 2 + 1];
-    float2 xc[TT][KCH + 1];     // (X, C) per token and group of the chunk
-    float2 sb[R][KCH][64 + 4];  // (scale, bias) per row tile, group and row of the block
+    uint4 xs[TT][KC * 4 * PARTS * 2 + 1];
+    float2 xc[TT][KC + 1];      // (X, C) per token and group of the chunk
+    float2 sb[R][KC][64 + 4];   // (scale, bias) per row tile, group and row of the block
     uint4 zero[2 * PARTS];      // B operand of the columns a lane block does not feed
 };
 
@@ -113,13 +114,18 @@ struct MQLds {
 // DOWN = true: down rows [64 rt, +64) (d rows, K = F) into fp32 output rows.
 // Each K chunk of the tokens' activations is staged once for all R tiles,
 // and each B operand read from LDS feeds R MFMAs.  Tiles past nrt repeat
-// the last one and store nothing.
-template <bool DOWN, int GS, int R>
+// the last one and store nothing.  hsrc: the activation rows, already in
+// B-operand form (gate/up: x rows as the router launch left them,
+// xb_row_u4(d) uint4 each; down: hidden rows, mq_row_u4(F) uint4 each).
+template <bool DOWN, int GS, int R, int KC>
 __device__ void mq_tile(const DecodeArgs &a, const uint8_t *blob, int F, int rt0, int nrt,
-                        MQLds<DOWN ? 2 : 1, R> &L, int nt, const uint16_t *x, const uint4 *hsrc,
-                        uint4 *hdst, float *ydst) {
+                        MQLds<DOWN ? 2 : 1, R, KC> &L, int nt, const uint4 *hsrc, uint4 *hdst,
+                        float *ydst) {
     constexpr int PARTS = DOWN ? 2 : 1;
-    constexpr int NRND = KCH / GS;   // rounds per chunk
+    constexpr int NRND = KC / GS;    // rounds per chunk
+    constexpr int XU = DOWN ? KC : KC / 2;   // staged uint4 per thread per chunk
+    constexpr int SBQ = KC / 4;      // scale/bias entries per thread per chunk and tile
+    static_assert(KC % 4 == 0 && KC <= 8, "rounds of four groups; 16 threads per token row");
     constexpr int BPS = 4 / GS;      // lane blocks per slot
     const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
     const int j = lane & 15, b = lane >> 4;
@@ -142,14 +148,14 @@ __device__ void mq_tile(const DecodeArgs &a, const uint8_t *blob, int F, int rt0
     uint4 q[R][4];
     auto qload = [&](int i, int c, int rho) {
         if (GS == 4) {
-            const int g = min(KCH * c + 4 * rho + b, G - 1);
+            const int g = min(KC * c + 4 * rho + b, G - 1);
             q[i][2 * rho] = *reinterpret_cast<const uint4 *>(qrow[i] + 32 * g);
             q[i][2 * rho + 1] = *reinterpret_cast<const uint4 *>(qrow[i] + 32 * g + 16);
         } else if (GS == 2) {
-            const int g = min(KCH * c + 2 * rho + (b >> 1), G - 1);
+            const int g = min(KC * c + 2 * rho + (b >> 1), G - 1);
             q[i][rho] = *reinterpret_cast<const uint4 *>(qrow[i] + 32 * g + 16 * (b & 1));
         } else {
-            const int g = min(KCH * c + rho, G - 1);
+            const int g = min(KC * c + rho, G - 1);
             const uint2 v = *reinterpret_cast<const uint2 *>(qrow[i] + 32 * g + 8 * b);
             if (rho & 1) { q[i][rho >> 1].z = v.x; q[i][rho >> 1].w = v.y; }
             else { q[i][rho >> 1].x = v.x; q[i][rho >> 1].y = v.y; }
@@ -172,35 +178,38 @@ __device__ void mq_tile(const DecodeArgs &a, const uint8_t *blob, int F, int rt0
         }
     };
 
-    // Staging: thread (token tj, sub) moves 64 values of the chunk; loads
-    // into registers one chunk ahead (fetch), LDS stores after the compute.
+    // Staging: thread (token tj, sub) copies uint4 sub + 16 i of the chunk's
+    // row (4 for gate/up, 8 for down; neighbouring lanes, neighbouring LDS
+    // entries); loads into registers one chunk ahead (fetch), LDS stores after
+    // the compute.
     const int tj = tid >> 4, sub = tid & 15;
     const bool stager = tj < nt;
     const int srow = L.src[min(tj, nt - 1)];
     const int HU = F / 4;   // word-pair uint4 of a hidden row (DOWN)
     struct Pre {
-        uint4 v[DOWN ? 8 : 4];
+        uint4 v[XU];
         float2 xc;
-        uint32_t sbw[R][2];
+        uint32_t sbw[R][SBQ];
     };
     // (every lane loads, non-stagers a valid row they then ignore: the loads
     // take no branch, so each wait counts only the loads it needs)
     auto fetch = [&](Pre &P, int c) {
-        if (!DOWN) {
-            const uint4 *xr = reinterpret_cast<const uint4 *>(x + (size_t)srow * d);
+        if (!DOWN) {   // uint4 sub + 16 i of the chunk's x row in B-operand form; (X, C) of group sub / 2
+            const uint4 *xr = hsrc + (size_t)srow * xb_row_u4(d);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) P.v[i] = xr[min(64 * c + 4 * sub + i, d / 8 - 1)];
+            for (int i = 0; i < XU; ++i) P.v[i] = xr[min(8 * KC * c + sub + 16 * i, d / 8 - 1)];
+            P.xc = reinterpret_cast<const float2 *>(xr + d / 8)[min(KC * c + (sub >> 1), G - 1)];
         } else {
             const uint4 *hr = hsrc + (size_t)srow * mq_row_u4(F);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) P.v[i] = hr[min(128 * c + 8 * sub + i, HU - 1)];
-            P.xc = reinterpret_cast<const float2 *>(hr + HU)[min(16 * c + sub, F / 32 - 1)];
+            for (int i = 0; i < XU; ++i) P.v[i] = hr[min(16 * KC * c + sub + 16 * i, HU - 1)];
+            P.xc = reinterpret_cast<const float2 *>(hr + HU)[min(2 * KC * c + sub, F / 32 - 1)];
         }
 #pragma unroll
         for (int i = 0; i < R; ++i) {
 #pragma unroll
-            for (int qq = 0; qq < 2; ++qq) {
-                const int e = tid + 256 * qq, rr = e >> 3, g = min(KCH * c + (e & 7), G - 1);
+            for (int qq = 0; qq < SBQ; ++qq) {
+                const int e = tid + 256 * qq, rr = e / KC, g = min(KC * c + e % KC, G - 1);
                 const Mat &ms = DOWN ? md : (rr < 32 ? mg : mu);
                 const int row = DOWN ? 64 * rts[i] + rr : 32 * rts[i] + (rr & 31);
                 P.sbw[i][qq] =
@@ -209,43 +218,34 @@ __device__ void mq_tile(const DecodeArgs &a, const uint8_t *blob, int F, int rt0
         }
     };
     auto store = [&](const Pre &P, int c) {
-        float X = 0.f, C = 0.f;
-        if (stager) {
-            if (!DOWN) {
+        if (!DOWN) {   // copies: the router launch staged x in this form
+            if (stager) {
 #pragma unroll
-                for (int pp = 0; pp < 2; ++pp) {   // word pairs 2 sub + pp
-                    uint32_t ev[4], od[4];
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const int i = 2 * pp + h;
-                        const bool ok = 64 * c + 4 * sub + i < d / 8;
-                        const uint4 pv = pair_halves(ok ? P.v[i] : make_uint4(0, 0, 0, 0));
-                        ev[2 * h] = pv.x; ev[2 * h + 1] = pv.z;
-                        od[2 * h] = div16(pv.y); od[2 * h + 1] = div16(pv.w);
-                        X += (hsum2(pv.x) + hsum2(pv.z)) + (hsum2(pv.y) + hsum2(pv.w));
-                        C += (hsum2(pv.x) + hsum2(pv.z)) + (hsum2(od[2 * h]) + hsum2(od[2 * h + 1]));
-                    }
-                    L.xs[tj][2 * (2 * sub + pp)] = make_uint4(ev[0], ev[1], ev[2], ev[3]);
-                    L.xs[tj][2 * (2 * sub + pp) + 1] = make_uint4(od[0], od[1], od[2], od[3]);
-                }
-                C *= 1024.f;
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    L.xs[tj][8 * sub + i] =
-                        128 * c + 8 * sub + i < HU ? P.v[i] : make_uint4(0, 0, 0, 0);
-                if (16 * c + sub < F / 32) { X = P.xc.x; C = P.xc.y; }
+                for (int i = 0; i < XU; ++i)
+                    L.xs[tj][sub + 16 * i] =
+                        8 * KC * c + sub + 16 * i < d / 8 ? P.v[i] : make_uint4(0, 0, 0, 0);
+                if (!(sub & 1) && (sub >> 1) < KC)
+                    L.xc[tj][sub >> 1] = KC * c + (sub >> 1) < G ? P.xc : make_float2(0.f, 0.f);
             }
+        } else {
+            float X = 0.f, C = 0.f;
+            if (stager) {
+#pragma unroll
+                for (int i = 0; i < XU; ++i)
+                    L.xs[tj][sub + 16 * i] =
+                        16 * KC * c + sub + 16 * i < HU ? P.v[i] : make_uint4(0, 0, 0, 0);
+                if (sub < 2 * KC && 2 * KC * c + sub < F / 32) { X = P.xc.x; C = P.xc.y; }
+            }
+            // the two halves of a group: lanes sub and sub ^ 1 (whole wave active)
+            const float X2 = X + __shfl_xor(X, 1), C2 = C + __shfl_xor(C, 1);
+            if (stager && !(sub & 1) && (sub >> 1) < KC) L.xc[tj][sub >> 1] = make_float2(X2, C2);
         }
-        // the two halves of a group: lanes sub and sub ^ 1 (whole wave active)
-        const float X2 = X + __shfl_xor(X, 1), C2 = C + __shfl_xor(C, 1);
-        if (stager && !(sub & 1)) L.xc[tj][sub >> 1] = make_float2(X2, C2);
 #pragma unroll
         for (int i = 0; i < R; ++i) {
 #pragma unroll
-            for (int qq = 0; qq < 2; ++qq) {
-                const int e = tid + 256 * qq, rr = e >> 3, gl = e & 7;
-                const uint32_t v = KCH * c + gl < G ? P.sbw[i][qq] : 0u;
+            for (int qq = 0; qq < SBQ; ++qq) {
+                const int e = tid + 256 * qq, rr = e / KC, gl = e % KC;
+                const uint32_t v = KC * c + gl < G ? P.sbw[i][qq] : 0u;
                 L.sb[i][gl][rr] = make_float2(h2f((uint16_t)(v & 0xFFFF)), h2f((uint16_t)(v >> 16)));
             }
         }
@@ -266,7 +266,7 @@ __device__ void mq_tile(const DecodeArgs &a, const uint8_t *blob, int F, int rt0
     f32x4 y[R];
 #pragma unroll
     for (int i = 0; i < R; ++i) y[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int nch = (G + KCH - 1) / KCH;
+    const int nch = (G + KC - 1) / KC;
     const uint4 *xrow = &L.xs[tc][0];
     const Masks km = masks();
     for (int c = 0; c < nch; ++c) {
@@ -393,8 +393,9 @@ __device__ void mq_tile(const DecodeArgs &a, const uint8_t *blob, int F, int rt0
 
 // Token list of a tile: routed item (expert, up to 16 pairs) or 16 shared
 // tokens.  Returns the expert (-1: the shared expert, -2: nothing to do).
-template <int PARTS, int R>
-__device__ int mq_tokens(const DecodeArgs &a, bool routed, bool down, int tile, MQLds<PARTS, R> &L) {
+template <int PARTS, int R, int KC>
+__device__ int mq_tokens(const DecodeArgs &a, bool routed, bool down, int tile,
+                          MQLds<PARTS, R, KC> &L) {
     const int tid = threadIdx.x;
     int e = -1;
     if (tid < 2 * PARTS) L.zero[tid] = make_uint4(0, 0, 0, 0);
@@ -422,15 +423,16 @@ __device__ int mq_tokens(const DecodeArgs &a, bool routed, bool down, int tile, 
 }
 
 // Row tiles per workgroup (each staged activation chunk serves them all) and
-// the residency that leaves room for their registers.
-constexpr int RT_GU = 1, RT_DN = 4;
+// the residency that leaves room for their registers.  At 128 tokens: gate/up
+// 115 us at one tile, 124 at two; down 64.5 at two, 66.5 at four.
+constexpr int RT_GU = 1, RT_DN = 2;
 constexpr int occ(int r) { return r == 1 ? 4 : r == 2 ? 3 : 2; }
 
 // Gate/up of the shared expert (blocks [0, a_shared_blocks)) and of the
 // routed expert items (the rest); a workgroup takes RT_GU row tiles of one
 // item.
 __global__ __launch_bounds__(256, occ(RT_GU)) void k_mq_gateup(DecodeArgs a) {
-    __shared__ MQLds<1, RT_GU> L;
+    __shared__ MQLds<1, RT_GU, KC_GU> L;
     int b = blockIdx.x;
     const bool routed = b >= a.a_shared_blocks;
     if (routed) b -= a.a_shared_blocks;
@@ -441,15 +443,15 @@ __global__ __launch_bounds__(256, occ(RT_GU)) void k_mq_gateup(DecodeArgs a) {
     const int rt0 = (b % wpi) * RT_GU, nrt = min(RT_GU, tiles - rt0);
     const uint8_t *blob = routed ? expert_blob(a, e) : a.shared_blob;
     uint4 *dst = routed ? a.h_r : a.h_s;
-    if (nt <= 4) mq_tile<false, 4, RT_GU>(a, blob, F, rt0, nrt, L, nt, a.x, nullptr, dst, nullptr);
-    else if (nt <= 8) mq_tile<false, 2, RT_GU>(a, blob, F, rt0, nrt, L, nt, a.x, nullptr, dst, nullptr);
-    else mq_tile<false, 1, RT_GU>(a, blob, F, rt0, nrt, L, nt, a.x, nullptr, dst, nullptr);
+    if (nt <= 4) mq_tile<false, 4, RT_GU, KC_GU>(a, blob, F, rt0, nrt, L, nt, a.xb, dst, nullptr);
+    else if (nt <= 8) mq_tile<false, 2, RT_GU, KC_GU>(a, blob, F, rt0, nrt, L, nt, a.xb, dst, nullptr);
+    else mq_tile<false, 1, RT_GU, KC_GU>(a, blob, F, rt0, nrt, L, nt, a.xb, dst, nullptr);
 }
 
 // Down of the shared expert (-> y_s) and of the routed expert items (-> y_e);
 // a workgroup takes RT_DN row tiles of one item.
 __global__ __launch_bounds__(256, occ(RT_DN)) void k_mq_down(DecodeArgs a) {
-    __shared__ MQLds<2, RT_DN> L;
+    __shared__ MQLds<2, RT_DN, KC_DN> L;
     int b = blockIdx.x;
     const bool routed = b >= a.b_shared_blocks;
     if (routed) b -= a.b_shared_blocks;
@@ -461,9 +463,9 @@ __global__ __launch_bounds__(256, occ(RT_DN)) void k_mq_down(DecodeArgs a) {
     const uint8_t *blob = routed ? expert_blob(a, e) : a.shared_blob;
     const uint4 *src = routed ? a.h_r : a.h_s;
     float *dst = routed ? a.y_e : a.y_s;
-    if (nt <= 4) mq_tile<true, 4, RT_DN>(a, blob, F, rt0, nrt, L, nt, nullptr, src, nullptr, dst);
-    else if (nt <= 8) mq_tile<true, 2, RT_DN>(a, blob, F, rt0, nrt, L, nt, nullptr, src, nullptr, dst);
-    else mq_tile<true, 1, RT_DN>(a, blob, F, rt0, nrt, L, nt, nullptr, src, nullptr, dst);
+    if (nt <= 4) mq_tile<true, 4, RT_DN, KC_DN>(a, blob, F, rt0, nrt, L, nt, src, nullptr, dst);
+    else if (nt <= 8) mq_tile<true, 2, RT_DN, KC_DN>(a, blob, F, rt0, nrt, L, nt, src, nullptr, dst);
+    else mq_tile<true, 1, RT_DN, KC_DN>(a, blob, F, rt0, nrt, L, nt, src, nullptr, dst);
 }
 
 }  // namespace

@@ -29,9 +29,9 @@ CSRC = os.path.join(ROOT, "bit_routed_expert_tf_amd", "csrc")
 CAL_BYTES = 256 << 20
 # device sources each measured kernel is built from
 SOURCES = {
-    "k_stage": ["tf_decode.hip", "tf_device.h", "tf_layer.h", "tf_internal.h"],
-    "k_gu": ["tf_grouped.hip", "tf_device.h", "tf_layer.h", "tf_internal.h"],
-    "k_dn": ["tf_grouped.hip", "tf_device.h", "tf_layer.h", "tf_internal.h"],
+    "k_stage": ["tf_decode.hip", "tf_device.h", "tf_layer.h", "tf_internal.h", "tf_slot_dev.h"],
+    "k_gu": ["tf_grouped.hip", "tf_device.h", "tf_layer.h", "tf_internal.h", "tf_slot_dev.h"],
+    "k_dn": ["tf_grouped.hip", "tf_device.h", "tf_layer.h", "tf_internal.h", "tf_slot_dev.h"],
 }
 
 

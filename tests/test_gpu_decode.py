@@ -163,6 +163,20 @@ def test_ragged_shapes(tfa, T):
     _check_layer(L, tfa, x)
 
 
+# ------------------------------------------- one token, wider d_ff
+WIDE = dict(seed=78, d=256, E=16, k=4, f=1024, fs=256)
+
+
+def test_one_token_wide_ff(tfa):
+    """A one-token step with d_ff = 1024 (four 16-byte chunks per lane in the
+    routed down, where the full-width layer has three): the same parity bar
+    as every other shape."""
+    L = oracle_layer(WIDE["seed"], 0, WIDE["d"], WIDE["E"], WIDE["k"], WIDE["f"], WIDE["fs"])
+    x = gen.tokens(WIDE["seed"], 4, WIDE["d"])
+    for t in range(4):
+        _check_layer(L, tfa, x[t:t + 1])
+
+
 def test_t_zero_is_a_no_op(tfa, tiny):
     D = device_layer(tiny)
     x = torch.zeros((0, TINY.d_model), dtype=torch.int16, device="cuda")
@@ -249,6 +263,24 @@ def test_workspace_reused_across_token_counts(tfa, full):
             assert torch.equal(u.view(torch.int16) if u.dtype == torch.float16 else u,
                                v.view(torch.int16) if v.dtype == torch.float16 else v), T
         r0 += T
+
+
+def test_one_token_counters_return_to_zero(tfa, full):
+    """After one-token steps every counter and ticket of a fresh workspace
+    (the router's ticket, the down launch's per-tile tickets) is zero again
+    and no flag is set."""
+    L, D, X = full
+    ws = tfa.workspace(tfa.tf_moe_workspace_bytes(D, 1))
+    xt = torch.from_numpy(X[500:506].view(np.int16)).cuda()
+    for t in range(6):
+        y, ids, w, y32 = tfa.tf_moe_layer_fwd(D, xt[t:t + 1], ws=ws, want_y32=True)
+        ref = oracle.moe_token(L, X[500 + t])
+        torch.cuda.synchronize()
+        assert np.array_equal(ids.cpu().numpy()[0], ref["ids"])
+        check_token(y.cpu().numpy().view(np.float16)[0], ref["y"])
+    head = ws[:33024].cpu().numpy()       # header (16,640 B) and the down tickets (16,384 B)
+    assert not head.any(), np.nonzero(head)[0][:8]
+    assert tfa.tf_workspace_flags(ws) == 0
 
 
 def test_router_topk_logits_fp64(tfa, full):

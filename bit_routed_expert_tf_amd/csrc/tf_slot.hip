@@ -500,6 +500,8 @@ tf_status tf_slot_cache_set_copy_engine(tf_slot_cache *c, int32_t engine) {
         if (e != hipSuccess) return fail(TF_E_HIP, "fill events: %s", hipGetErrorString(e));
         c->dfill_pending.assign(c->d.L, 0);
     }
+    if (c->engine == TF_SLOT_COPY_DEVICE && engine != TF_SLOT_COPY_DEVICE && c->dfill_any)
+        c->mirror.assign(c->mirror.size(), -1);   // device fills kept no host view: assume nothing resident
     c->engine = engine;
     return TF_OK;
 }

@@ -311,7 +311,38 @@ __device__ __forceinline__ int count_above(const uint64_t *key, int j0, int j1, 
     return r;
 }
 
-__device__ void topk_block(const DecodeArgs &a, int t, int tid, unsigned char *lds) {
+// x of token t in the grouped kernels' B-operand form (whole WG; d <= 4096:
+// one word pair per thread).
+__device__ void xb_load(const DecodeArgs &a, int t, int tid, uint4 &xv0, uint4 &xv1) {
+    const uint4 *xrow = reinterpret_cast<const uint4 *>(a.x + (size_t)t * a.d);
+    if (tid < (a.d >> 4)) {
+        xv0 = xrow[2 * tid];
+        xv1 = xrow[2 * tid + 1];
+    }
+}
+__device__ void xb_store(const DecodeArgs &a, int t, int tid, uint4 xv0, uint4 xv1) {
+    const int d = a.d, NC = d >> 4;
+    uint4 *row = a.xb + (size_t)t * xb_row_u4(d);
+    float X = 0.f, C = 0.f;
+    if (tid < NC) xb_produce(xv0, xv1, row, tid, X, C);
+    // a group is four word pairs: lanes 4g .. 4g+3
+    X += dpp_f<DPP_XOR1>(X);
+    C += dpp_f<DPP_XOR1>(C);
+    X += dpp_f<DPP_XOR2>(X);
+    C += dpp_f<DPP_XOR2>(C);
+    if (tid < NC && !(tid & 3)) reinterpret_cast<float2 *>(row + d / 8)[tid >> 2] = make_float2(X, C);
+}
+__device__ void xb_row(const DecodeArgs &a, int t, int tid) {
+    uint4 xv0 = make_uint4(0, 0, 0, 0), xv1 = xv0;
+    xb_load(a, t, tid, xv0, xv1);
+    xb_store(a, t, tid, xv0, xv1);
+}
+
+// PART: the logits are the partial sums of an earlier launch (a.part), else
+// single values written in this launch (a.logits).
+template <bool PART>
+__device__ void topk_block(const DecodeArgs &a, int t, int tid, unsigned char *lds, bool xb = false,
+                           uint4 xv0 = {}, uint4 xv1 = {}) {
     const int E = a.E;
     uint64_t *key = reinterpret_cast<uint64_t *>(lds);        // [E] (16-byte aligned)
     double *l = reinterpret_cast<double *>(key + E);          // [E] logits
@@ -323,9 +354,15 @@ __device__ void topk_block(const DecodeArgs &a, int t, int tid, unsigned char *l
     if (tid == 0) *tie = 0;
     for (int i = tid; i < E; i += WG) {
         double v;
-        if (a.part) {   // partial logits of an earlier launch, added in K-range order
+        if (PART) {   // partial logits of an earlier launch, added in K-range order
+            double pv[RMM_MAX_KR];   // all in flight at once
+#pragma unroll
+            for (int r = 0; r < RMM_MAX_KR; ++r)
+                pv[r] = ld_prev(a.part + ((size_t)min(r, a.nkr - 1) * a.T + t) * E + i);
             v = 0.0;
-            for (int r = 0; r < a.nkr; ++r) v += ld_prev(a.part + ((size_t)r * a.T + t) * E + i);
+#pragma unroll
+            for (int r = 0; r < RMM_MAX_KR; ++r)
+                if (r < a.nkr) v += pv[r];
         } else {
             v = ld_dev(a.logits + (size_t)t * E + i);
         }
@@ -333,6 +370,7 @@ __device__ void topk_block(const DecodeArgs &a, int t, int tid, unsigned char *l
         l[i] = v;
         key[i] = order_key(v);
     }
+    if (xb) xb_store(a, t, tid, xv0, xv1);   // x has arrived with the logits
     lds_barrier();
     if (a.forced) {
         uint32_t fl = 0;
@@ -411,22 +449,24 @@ __device__ void topk_block(const DecodeArgs &a, int t, int tid, unsigned char *l
 // and their router weights, so a gate/up block learns everything it needs
 // in one load.  Token t's pair with expert e lands at
 // offs[e] + #{t' < t that selected e}, counted on a per-expert bit mask over
-// the tokens (T <= 128), so the order never depends on thread timing.
+// the tokens (T <= 128) and the exclusive prefix of its words' counts, so the
+// order never depends on thread timing.
 // The ids and weights are read once (one round trip); the sorted order is
 // built in LDS, where positions start out holding their own index, so
 // repeated ids (flagged by the top-k) can never leave an out-of-range pair
 // behind, and is written out at the end.  Whole WG.
 constexpr int GROUP_PPT = (MAX_PREFILL_T * 16 + WG - 1) / WG;   // pairs per thread, at most
+constexpr int GROUP_MAX_NW = (MAX_PREFILL_T + 31) / 32;          // mask words per expert, at most
 __host__ __device__ constexpr int group_lds_bytes(int E, int T) {
-    return 4 * E * ((T + 31) >> 5) + 12 * E + 8 * 4 + 4 * T * 16;
+    return 8 * E * ((T + 31) >> 5) + 12 * E + 8 * 4 + 4 * T * 16;
 }
-__host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 __device__ void group_block(const DecodeArgs &a, int tid, unsigned char *lds) {
     const int P = a.T * a.k, E = a.E, NW = (a.T + 31) >> 5;
     const int lane = tid & 63, w = tid >> 6;
     uint32_t *mask = reinterpret_cast<uint32_t *>(lds);       // [E][NW]
-    int *cnt = reinterpret_cast<int *>(mask + E * NW);        // [E]
+    int *pref = reinterpret_cast<int *>(mask + E * NW);       // [E][NW] pairs in earlier words
+    int *cnt = pref + E * NW;                                 // [E]
     int *offs = cnt + E;                                      // [E]
     int *iidx = offs + E;                                     // [E] item index
     int *wsum = iidx + E;                                     // [4][2]
@@ -442,28 +482,38 @@ __device__ void group_block(const DecodeArgs &a, int tid, unsigned char *lds) {
         ev[j] = (int)ld_dev(a.ids + pc);
         pw[j] = a.weights ? ld_dev(a.weights + pc) : 0.f;
     }
+    int pt[GROUP_PPT];   // the pairs' tokens
 #pragma unroll
-    for (int j = 0; j < GROUP_PPT; ++j) pe[j] = min(max(ev[j], 0), E - 1);
+    for (int j = 0; j < GROUP_PPT; ++j) {
+        pe[j] = min(max(ev[j], 0), E - 1);
+        pt[j] = WG * j < P ? (tid + WG * j) / a.k : 0;   // (rounds beyond P: uniform skips)
+    }
+    const int tsh = __builtin_ctz(a.tbi);   // a power of two
     lds_barrier();
     for (int i = tid; i < E * NW; i += WG) mask[i] = 0;
     for (int i = tid; i < P; i += WG) pl[i] = i;
     lds_barrier();
 #pragma unroll
-    for (int j = 0; j < GROUP_PPT; ++j) {
-        const int p = tid + WG * j, t = p / a.k;
-        if (p < P) atomicOr(&mask[pe[j] * NW + (t >> 5)], 1u << (t & 31));
-    }
+    for (int j = 0; j < GROUP_PPT; ++j)
+        if (tid + WG * j < P) atomicOr(&mask[pe[j] * NW + (pt[j] >> 5)], 1u << (pt[j] & 31));
     lds_barrier();
     // counts, and exclusive scans of the counts and of the item counts;
     // thread tid owns experts [tid*per, tid*per + per)
     const int per = (E + WG - 1) / WG, e0 = tid * per, e1 = min(E, e0 + per);
     int sc = 0, sn = 0;
     for (int e = e0; e < e1; ++e) {
+        uint32_t m[GROUP_MAX_NW];
+#pragma unroll
+        for (int q = 0; q < GROUP_MAX_NW; ++q) m[q] = q < NW ? mask[e * NW + q] : 0u;
         int c = 0;
-        for (int q = 0; q < NW; ++q) c += __popc(mask[e * NW + q]);
+#pragma unroll
+        for (int q = 0; q < GROUP_MAX_NW; ++q) {
+            if (q < NW) pref[e * NW + q] = c;
+            c += __popc(m[q]);
+        }
         cnt[e] = c;
         sc += c;
-        sn += ceil_div(c, a.tbi);
+        sn += (c + a.tbi - 1) >> tsh;
     }
     const int ic = wave_scan_incl(sc), in = wave_scan_incl(sn);
     if (lane == WAVE - 1) { wsum[2 * w] = ic; wsum[2 * w + 1] = in; }
@@ -474,7 +524,7 @@ __device__ void group_block(const DecodeArgs &a, int tid, unsigned char *lds) {
         offs[e] = oc;
         iidx[e] = on;
         oc += cnt[e];
-        on += ceil_div(cnt[e], a.tbi);
+        on += (cnt[e] + a.tbi - 1) >> tsh;
     }
     if (tid == WG - 1) st_dev(a.hdr + HDR_NITEMS, (uint32_t)on);
     if (a.g_counts) {
@@ -485,23 +535,34 @@ __device__ void group_block(const DecodeArgs &a, int tid, unsigned char *lds) {
         if (tid == WG - 1) st_dev(a.g_offsets + E, (int32_t)oc);   // the total
     }
     lds_barrier();
-    for (int e = tid; e < E; e += WG)
-        for (int q = 0; q < cnt[e]; q += a.tbi)
-            st_dev(reinterpret_cast<uint4 *>(a.items + ITEM_INTS * (iidx[e] + q / a.tbi)),
-                   make_uint4((uint32_t)e, (uint32_t)(offs[e] + q),
-                              (uint32_t)min(a.tbi, cnt[e] - q), 0u));
+    for (int e = tid; e < E; e += WG) {
+        const int c = cnt[e], o = offs[e], ii = iidx[e];
+        for (int q = 0; q < c; q += a.tbi)
+            st_dev(reinterpret_cast<uint4 *>(a.items + ITEM_INTS * (ii + (q >> tsh))),
+                   make_uint4((uint32_t)e, (uint32_t)(o + q), (uint32_t)min(a.tbi, c - q), 0u));
+    }
+    // a pair's rank within its expert: earlier words' pairs + the bits below
+    // its token; every LDS read of the thread's pairs before the first use
+    int rk[GROUP_PPT], po[GROUP_PPT], pi[GROUP_PPT];
 #pragma unroll
     for (int j = 0; j < GROUP_PPT; ++j) {
-        const int p = tid + WG * j;
+        rk[j] = po[j] = pi[j] = 0;
+        if (WG * j < P) {
+            const int e = pe[j], t = pt[j], wq = e * NW + min(t >> 5, NW - 1);
+            rk[j] = pref[wq] + __popc(mask[wq] & ((1u << (t & 31)) - 1u));
+            po[j] = offs[e];
+            pi[j] = iidx[e];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < GROUP_PPT; ++j) {
+        const int p = tid + WG * j, r = rk[j];
         if (p < P) {
-            const int e = pe[j], t = p / a.k;
-            int r = __popc(mask[e * NW + (t >> 5)] & ((1u << (t & 31)) - 1u));
-            for (int q = 0; q < (t >> 5); ++q) r += __popc(mask[e * NW + q]);
-            const int pos = offs[e] + r;
+            const int pos = po[j] + r;
             if (pos < P) pl[pos] = p;
-            const int slot = r % a.tbi;
+            const int slot = r & (a.tbi - 1);
             if (slot < MAX_TB) {
-                int32_t *rec = a.items + ITEM_INTS * (iidx[e] + r / a.tbi);
+                int32_t *rec = a.items + ITEM_INTS * (pi[j] + (r >> tsh));
                 st_dev(rec + 4 + slot, (int32_t)p);
                 st_dev(reinterpret_cast<float *>(rec) + 8 + slot, pw[j]);
             }
@@ -511,36 +572,19 @@ __device__ void group_block(const DecodeArgs &a, int tid, unsigned char *lds) {
     for (int i = tid; i < P; i += WG) st_dev(a.pairs + i, (int32_t)pl[i]);
 }
 
-// x of token t in the grouped kernels' B-operand form (whole WG; d <= 4096:
-// one word pair per thread).
-__device__ void xb_row(const DecodeArgs &a, int t, int tid) {
-    const int d = a.d, NC = d >> 4;
-    const uint4 *xrow = reinterpret_cast<const uint4 *>(a.x + (size_t)t * d);
-    uint4 xv0 = make_uint4(0, 0, 0, 0), xv1 = xv0;
-    if (tid < NC) {
-        xv0 = xrow[2 * tid];
-        xv1 = xrow[2 * tid + 1];
-    }
-    uint4 *row = a.xb + (size_t)t * xb_row_u4(d);
-    float X = 0.f, C = 0.f;
-    if (tid < NC) xb_produce(xv0, xv1, row, tid, X, C);
-    // a group is four word pairs: lanes 4g .. 4g+3
-    X += dpp_f<DPP_XOR1>(X);
-    C += dpp_f<DPP_XOR1>(C);
-    X += dpp_f<DPP_XOR2>(X);
-    C += dpp_f<DPP_XOR2>(C);
-    if (tid < NC && !(tid & 3)) reinterpret_cast<float2 *>(row + d / 8)[tid >> 2] = make_float2(X, C);
-}
-
 // After a token's top-k in a grouped step: the step's ticket; the last
-// token's workgroup groups the pairs by expert.
-__device__ void group_after_topk(const DecodeArgs &a, int tid, unsigned char *lds) {
+// token's workgroup groups the pairs by expert.  With xb, the token's x in
+// B-operand form is stored while the ticket is out (the grouping does not
+// read it, so the ticket need not wait for those stores).
+__device__ void group_after_topk(const DecodeArgs &a, int t, int tid, unsigned char *lds,
+                                 bool xb = false, uint4 xv0 = {}, uint4 xv1 = {}) {
     stores_done();
     lds_barrier();
     if (tid == 0) {
         const uint32_t old = atomicAdd(a.hdr + hdr_ticket(a.T), 1u);
         reinterpret_cast<int *>(lds)[0] = old == (uint32_t)(a.T - 1);
     }
+    if (xb) xb_store(a, t, tid, xv0, xv1);
     lds_barrier();
     if (!reinterpret_cast<int *>(lds)[0]) return;
     if (tid == 0) st_dev(a.hdr + hdr_ticket(a.T), 0u);
@@ -555,40 +599,45 @@ __device__ void group_after_topk(const DecodeArgs &a, int tid, unsigned char *ld
 // exact, only the fp64 sums round.  v_mfma_f64_16x16x4_f64 takes A[e][k]
 // from lane l as A[l % 16][l / 16] and B[k][t] as B[l / 16][l % 16], and
 // leaves D[l / 16 + 4 r][l % 16] in slot r of lane l (rows interleaved, unlike
-// the fp32 16x16 layout).  Workgroup: a tile
-// of 16 experts x 16 tokens over one of nkr K ranges, the range split in
-// four between the waves; the wave sums are added in wave order and the
-// ranges' partial logits part[kr][t][e] in range order by the top-k.
+// the fp32 16x16 layout).  The k index of a step is free: lane (i, kq) feeds
+// columns 16 c + 4 kq + s of chunk c in step s, so it reads just its own four
+// consecutive codes (one word) and x values (two words) of each chunk.
+// Workgroup: a tile of 16 experts x 16 tokens over one of nkr K ranges, the
+// range split in four between the waves; the wave sums are added in wave
+// order and the ranges' partial logits part[kr][t][e] in range order by the
+// top-k.
 typedef double v4d __attribute__((ext_vector_type(4)));
-constexpr int RMM_CHUNKS = 4;   // 16-column chunks per wave at most
 
 __global__ __launch_bounds__(256) void k_router_mm(DecodeArgs a) {
     __shared__ v4d red[3][64];
     const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
-    const int ebn = (a.E + 15) >> 4;
+    // token tile fastest: workgroup b runs on XCD b mod 8, so with eight
+    // token tiles every tile's partial logits stay in one XCD's L2, the one
+    // its tokens' top-k workgroups run on
+    const int ebn = (a.E + 15) >> 4, ntb = (a.T + 15) >> 4;
     int b = blockIdx.x;
-    const int kr = b % a.nkr;
-    b /= a.nkr;
-    const int eb = b % ebn, tb = b / ebn;
+    const int tb = b % ntb;
+    b /= ntb;
+    const int eb = b % ebn, kr = b / ebn;
     const int d = a.d, NC = d >> 4, G = d >> 6;   // 16-column chunks, groups
     const int pidx = 4 * kr + w, parts = 4 * a.nkr;
     const int c0 = (int)((long)NC * pidx / parts), c1 = (int)((long)NC * (pidx + 1) / parts);
     const int i = lane & 15, kq = lane >> 4;
     const int e = min(16 * eb + i, a.E - 1), t = min(16 * tb + i, a.T - 1);   // clamped: not stored
-    const uint8_t *qrow = a.rq + (size_t)e * d;
+    const uint8_t *qrow = a.rq + (size_t)e * d + 4 * kq;
     const uint16_t *srow = a.rs + (size_t)e * G, *brow = a.rb + (size_t)e * G;
-    const uint16_t *xrow = a.x + (size_t)t * d;
+    const uint16_t *xrow = a.x + (size_t)t * d + 4 * kq;
     v4d acc = {0.0, 0.0, 0.0, 0.0};
     // a wave's chunks (at most RMM_CHUNKS, see tf_router_nkr): every load in
     // flight before the first MFMA
-    uint4 qv[RMM_CHUNKS], x0[RMM_CHUNKS], x1[RMM_CHUNKS];
+    uint32_t qv[RMM_CHUNKS];
+    uint2 xv[RMM_CHUNKS];
     uint16_t sh[RMM_CHUNKS], bh[RMM_CHUNKS];
 #pragma unroll
     for (int u = 0; u < RMM_CHUNKS; ++u) {
         const int c = min(c0 + u, NC - 1);
-        qv[u] = *reinterpret_cast<const uint4 *>(qrow + 16 * c);
-        x0[u] = *reinterpret_cast<const uint4 *>(xrow + 16 * c);
-        x1[u] = *reinterpret_cast<const uint4 *>(xrow + 16 * c + 8);
+        qv[u] = *reinterpret_cast<const uint32_t *>(qrow + 16 * c);
+        xv[u] = *reinterpret_cast<const uint2 *>(xrow + 16 * c);
         sh[u] = srow[c >> 2];
         bh[u] = brow[c >> 2];
     }
@@ -596,14 +645,10 @@ __global__ __launch_bounds__(256) void k_router_mm(DecodeArgs a) {
     for (int u = 0; u < RMM_CHUNKS; ++u) {
         if (c0 + u >= c1) break;   // uniform
         const double sc = (double)h2f(sh[u]), bi = (double)h2f(bh[u]);
-        const uint32_t qw[4] = {qv[u].x, qv[u].y, qv[u].z, qv[u].w};
-        const uint32_t xw[8] = {x0[u].x, x0[u].y, x0[u].z, x0[u].w, x1[u].x, x1[u].y, x1[u].z, x1[u].w};
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
-            // this lane's column k = 16 c + 4 s4 + kq
-            const int kk = 4 * s4 + kq;
-            const uint32_t code = (qw[kk >> 2] >> (8 * (kk & 3))) & 0xFFu;
-            const uint16_t xh = (uint16_t)(xw[kk >> 1] >> (16 * (kk & 1)));
+            const uint32_t code = (qv[u] >> (8 * s4)) & 0xFFu;
+            const uint16_t xh = (uint16_t)((s4 < 2 ? xv[u].x : xv[u].y) >> (16 * (s4 & 1)));
             const double wv = fma(sc, (double)code, bi);
             acc = __builtin_amdgcn_mfma_f64_16x16x4f64(wv, (double)h2f(xh), acc, 0, 0, 0);
         }
@@ -626,10 +671,15 @@ __global__ __launch_bounds__(256) void k_router_mm(DecodeArgs a) {
 // the last token's workgroup.
 __global__ __launch_bounds__(256) void k_router_topk(DecodeArgs a) {
     extern __shared__ __align__(16) unsigned char lds[];
-    const int t = blockIdx.x, tid = threadIdx.x;
-    if (a.xb) xb_row(a, t, tid);
-    topk_block(a, t, tid, lds);
-    if (a.do_group) group_after_topk(a, tid, lds);
+    // token t of tile t / 16 on that tile's XCD (see k_router_mm) when the
+    // tiles are full
+    const int ntb = a.T >> 4, b = blockIdx.x, tid = threadIdx.x;
+    const int t = (a.T & 15) ? b : (b % ntb) * 16 + b / ntb;
+    // the x loads go out with the top-k's logit loads
+    uint4 xv0 = make_uint4(0, 0, 0, 0), xv1 = xv0;
+    if (a.xb) xb_load(a, t, tid, xv0, xv1);
+    topk_block<true>(a, t, tid, lds, a.xb && !a.do_group, xv0, xv1);
+    if (a.do_group) group_after_topk(a, t, tid, lds, a.xb != nullptr, xv0, xv1);
 }
 
 // ------------------------------------------------------------- router
@@ -696,8 +746,8 @@ __device__ void router_block(const DecodeArgs &a, int b, int tid, unsigned char 
     lds_barrier();
     if (!*flag) return;
     if (tid == 0) st_dev(a.hdr + hdr_ticket(t), 0u);
-    topk_block(a, t, tid, lds);
-    if (a.do_group && a.T > 1) group_after_topk(a, tid, lds);
+    topk_block<false>(a, t, tid, lds);
+    if (a.do_group && a.T > 1) group_after_topk(a, t, tid, lds);
     if (a.sc.slot_of && tid < WAVE) {   // one token: the slot lookup of its ids (rank order)
         const int *sel = reinterpret_cast<const int *>(lds + 16 * (size_t)a.E);
         slotk::lookup_wave(a.sc, a.sc_layer, sel, a.k, nullptr, false, tid);

@@ -19,6 +19,8 @@ __host__ __device__ constexpr size_t hdr_bytes(int T) { return (size_t)4 * hdr_t
 enum { STAGE_A = 1, STAGE_B = 2, STAGE_C = 4 };
 constexpr int KC_BATCH = 8;       // pairs staged per pass in the down/combine kernel
 constexpr int ROUTER_ROWS = 2;    // router rows per workgroup (two waves per row)
+constexpr int RMM_CHUNKS = 6;     // 16-column chunks per wave of the matrix-core router, at most
+constexpr int RMM_MAX_KR = (4096 / 16 + 4 * RMM_CHUNKS - 1) / (4 * RMM_CHUNKS);   // its K ranges at d = 4096
 // Router workgroups of a step of T tokens over E experts.
 __host__ __device__ constexpr int router_blocks(int E, int T) { return ((E + ROUTER_ROWS - 1) / ROUTER_ROWS) * T; }
 

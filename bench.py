@@ -258,7 +258,7 @@ def run_stack_batch(args, wl, layers, B, lib, dev, roofline):
                  _lib.TF_KERNEL_DOWN_COMBINE: "k_stage_c1"}
         gemv = {"k_stage_b": stage_b_bytes(d, f, fs, k)}
     else:
-        names = {_lib.TF_KERNEL_ROUTER_SHARED_GATEUP: "k_stage_a",
+        names = {_lib.TF_KERNEL_ROUTER_SHARED_GATEUP: "k_router_rows",
                  _lib.TF_KERNEL_PREFILL_GATEUP: "k_gu",
                  _lib.TF_KERNEL_PREFILL_DOWN: "k_dn",
                  _lib.TF_KERNEL_PREFILL_COMBINE: "k_pf_combine"}

@@ -941,6 +941,15 @@ __global__ __launch_bounds__(256, 4) void k_stage_a(DecodeArgs a) {
         gateup_block<LPR, J, false>(a, b - a.a_router_blocks, tid, lds);
 }
 
+// A router launch with no other roles (grouped steps, the router alone):
+// router rows, and the top-k and grouping that their last workgroups run, at
+// a fraction of k_stage_a's registers, so that every workgroup is resident
+// at once.
+__global__ __launch_bounds__(256) void k_router_rows(DecodeArgs a) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    router_block(a, blockIdx.x, threadIdx.x, lds);
+}
+
 template <int LPR, int J>
 __global__ __launch_bounds__(256, 4) void k_stage_b(DecodeArgs a) {
     extern __shared__ __align__(16) unsigned char lds[];
@@ -1183,7 +1192,9 @@ template <int LPR, int J>
 hipError_t launch_ab(const DecodeArgs &a, int which, hipStream_t s) {
     if (which & STAGE_A) {
         const int n = a.a_copy_blocks + a.a_router_blocks + a.a_shared_blocks;
-        if (n)
+        if (n && n == a.a_router_blocks)
+            TF_LAUNCH(TF_KERNEL_ROUTER_SHARED_GATEUP, k_router_rows, dim3(n), dim3(WG), lds_a(a, LPR), s, a);
+        else if (n)
             TF_LAUNCH(TF_KERNEL_ROUTER_SHARED_GATEUP, (k_stage_a<LPR, J>), dim3(n), dim3(WG),
                       lds_a(a, LPR), s, a);
     }

@@ -165,13 +165,14 @@ __device__ __forceinline__ void copy_missed(const int32_t *miss, const uint8_t *
     uint4 *dst = reinterpret_cast<uint4 *>(slot_layer + (size_t)sl * stride);
     const size_t n16 = stride / 16, step = (size_t)per * 256;
     for (size_t i = (size_t)part * 256 + tid; i < n16; i += 4 * step) {
-        uint4 v[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (i + j * step < n16) v[j] = src[i + j * step];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (i + j * step < n16) dst[i + j * step] = v[j];
+        // four loads in flight, unconditional (clamped) and in named
+        // registers: a conditionally filled array is kept in scratch memory
+        const uint4 v0 = src[i], v1 = src[min(i + step, n16 - 1)];
+        const uint4 v2 = src[min(i + 2 * step, n16 - 1)], v3 = src[min(i + 3 * step, n16 - 1)];
+        dst[i] = v0;
+        if (i + step < n16) dst[i + step] = v1;
+        if (i + 2 * step < n16) dst[i + 2 * step] = v2;
+        if (i + 3 * step < n16) dst[i + 3 * step] = v3;
     }
 }
 

@@ -310,7 +310,9 @@ tf_status tf_sample(const float *logits, int32_t V, int32_t T, float temperature
 /* Kernel ids of the hot path (for tf_profile_kernel). */
 enum {
     TF_KERNEL_ROUTER_SHARED_GATEUP = 1,      /* decode A: router + top-k + shared gate/up;
-                                                grouped steps: the router GEMM            */
+                                                decode steps of 2-16 tokens and the router
+                                                alone: router rows + top-k (+ grouping);
+                                                prefill chunks: the router GEMM           */
     TF_KERNEL_ROUTED_GATEUP_SHARED_DOWN = 2, /* decode B: routed gate/up + shared down    */
     TF_KERNEL_DOWN_COMBINE = 4,              /* decode C: routed down + combine -> y      */
     TF_KERNEL_PREFILL_DOWN = 8,              /* prefill: shared and per-item down (MFMA)  */

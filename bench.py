@@ -141,17 +141,28 @@ def _profile(lib, h, kernels, step, steps, stream):
     return out
 
 
-def _graphs(step, first, n, chunk, stream):
+def _graphs(step, first, n, chunk, stream, sides=()):
     """HIP graphs of at most `chunk` consecutive steps each, covering steps
-    first .. first + n - 1 in order."""
+    first .. first + n - 1 in order.  With side streams, every graph forks
+    them from `stream` at its start and joins them back at its end (the step
+    function picks each step's stream)."""
     import torch
     graphs = []
     for j in range(first, first + n, chunk):
         g = torch.cuda.CUDAGraph()
         m = min(first + n, j + chunk) - j
         with torch.cuda.graph(g, stream=stream):
+            if sides:
+                fork = torch.cuda.Event()
+                fork.record(stream)
+                for s in sides:
+                    s.wait_event(fork)
             for i in range(j, j + m):
                 step(i)
+            for s in sides:
+                join = torch.cuda.Event()
+                join.record(s)
+                stream.wait_event(join)
         graphs.append((g, m))
     torch.cuda.synchronize()
     return graphs
@@ -165,12 +176,12 @@ def _replay_all(graphs, stream):
     return sum(m for _, m in graphs)
 
 
-def _timed(step, warmup, steps, chunk, stream):
+def _timed(step, warmup, steps, chunk, stream, sides=()):
     """Warm-up steps 0 .. warmup-1, then steps warmup .. warmup+steps-1 timed
     with events on the stream; every step exactly once.  Returns (steps, ms)."""
     import torch
-    wg = _graphs(step, 0, warmup, chunk, stream) if warmup else []
-    tg = _graphs(step, warmup, steps, chunk, stream)
+    wg = _graphs(step, 0, warmup, chunk, stream, sides) if warmup else []
+    tg = _graphs(step, warmup, steps, chunk, stream, sides)
     _replay_all(wg, stream)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -428,7 +439,10 @@ def cpu_baseline_stack(args, wl, host_layers):
 
 
 def run_prefill(args):
-    """128-token chunks through one full-width layer (natural routing)."""
+    """128-token chunks through one full-width layer (natural routing).  The
+    chunks of a layer are independent, so the line keeps two in flight:
+    consecutive chunks alternate between two streams, each with a workspace of
+    its own.  One chunk at a time on one stream is timed as well."""
     import numpy as np
     import torch
 
@@ -446,21 +460,32 @@ def run_prefill(args):
     Y = torch.empty((wl.n_tokens, d), dtype=torch.int16, device=dev)
     IDS = torch.empty((wl.n_tokens, k), dtype=torch.int32, device=dev)
     W = torch.empty((wl.n_tokens, k), dtype=torch.float32, device=dev)
-    ws = api.workspace(api.tf_prefill_workspace_bytes(D, C), dev)
-    stream = torch.cuda.Stream(device=dev)
-    sh = ctypes.c_void_p(stream.cuda_stream)
+    wss = [api.workspace(api.tf_prefill_workspace_bytes(D, C), dev) for _ in range(2)]
+    streams = [torch.cuda.Stream(device=dev) for _ in range(2)]
+    stream = streams[0]
     Lp = ctypes.byref(D.struct)
+    # chunk j always runs on stream j % 2 (64 chunks: its rows of Y, IDS and W
+    # are written by one stream only)
+    assert nch % 2 == 0
 
-    def step(i):
+    def launch(i, q):
         j = i % nch
         _lib.check(lib.tf_moe_prefill_chunk(
             Lp, ctypes.c_void_p(X.data_ptr() + 2 * d * C * j), C,
             ctypes.c_void_p(Y.data_ptr() + 2 * d * C * j), None,
             ctypes.c_void_p(IDS.data_ptr() + 4 * k * C * j),
-            ctypes.c_void_p(W.data_ptr() + 4 * k * C * j), sh, ctypes.c_void_p(ws.data_ptr()),
-            ws.numel()))
+            ctypes.c_void_p(W.data_ptr() + 4 * k * C * j),
+            ctypes.c_void_p(streams[q].cuda_stream), ctypes.c_void_p(wss[q].data_ptr()),
+            wss[q].numel()))
 
-    steps, ms = _timed(step, args.warmup, args.steps, args.graph_chunk, stream)
+    def step(i):    # one chunk at a time
+        launch(i, 0)
+
+    def step2(i):   # two chunks in flight
+        launch(i, i % 2)
+
+    steps1, ms1 = _timed(step, args.warmup, args.steps, args.graph_chunk, stream)
+    steps, ms = _timed(step2, args.warmup, args.steps, args.graph_chunk, stream, streams[1:])
     ids = IDS.cpu().numpy().reshape(nch, C * k)
     distinct = float(np.mean([len(np.unique(r)) for r in ids]))
     qb = lambda n, kk, bits=4: n * kk * bits // 8 + 4 * n * (kk // 64)   # noqa: E731
@@ -472,13 +497,17 @@ def run_prefill(args):
         _lib.TF_KERNEL_PREFILL_GATEUP: "k_mq_gateup",
         _lib.TF_KERNEL_PREFILL_DOWN: "k_mq_down",
         _lib.TF_KERNEL_PREFILL_COMBINE: "k_pf_combine"}, step, range(min(args.prof_steps, 64)), stream)
-    us = ms * 1e3 / steps
+    us, us1 = ms * 1e3 / steps, ms1 * 1e3 / steps1
     return {"metric": "prefill tokens/s (128-token chunks, one layer)",
             "value": round(C * steps / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
             "steps": steps, "us_per_chunk": round(us, 2), "higher_is_better": True,
+            "one_chunk_at_a_time": {"tokens_per_s": round(C * steps1 / (ms1 / 1e3), 1),
+                                    "us_per_chunk": round(us1, 2)},
             "data": "synthetic (seeded)", "dtype": "fp32",
             "config": {"workload": wl.name, "chunk": C, "chunks": nch,
-                       "distinct_experts_per_chunk": distinct},
+                       "distinct_experts_per_chunk": distinct,
+                       "chunks_in_flight": 2, "schedule": "consecutive chunks alternate between "
+                       "two streams, one workspace each; graphs fork and join the streams"},
             "chunk_bytes": int(chunk_bytes),
             "GBps": round(chunk_bytes / (us * 1e-6) / 1e9, 1),
             "frac_of_hbm_peak": round(chunk_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),

@@ -95,3 +95,34 @@ def test_prefill_full_width_chunk(tfa):
     # repeat: bitwise identical
     y2, ids2, _, _ = _prefill(tfa, D, x)
     assert np.array_equal(ids, ids2) and np.array_equal(y.view(np.int16), y2.view(np.int16))
+
+
+def test_prefill_two_chunks_in_flight(tfa):
+    # the prefill line's schedule: consecutive chunks alternate between two
+    # streams with a workspace each, so two chunks run at once; every output
+    # must be bitwise the one-at-a-time result
+    print("prefill two streams: 6 chunks of 128, full width", flush=True)
+    wl = gen.WORKLOADS[3]
+    L = oracle_layer(wl.seed, 0, wl.d_model, wl.n_experts, wl.top_k, wl.d_ff, wl.d_ff_shared)
+    D = device_layer(L)
+    C, n = 128, 6
+    x = torch.from_numpy(gen.tokens(wl.seed, C * n, wl.d_model).view(np.int16)).cuda()
+    ws = [tfa.workspace(tfa.tf_prefill_workspace_bytes(D, C), x.device) for _ in range(2)]
+    streams = [torch.cuda.Stream() for _ in range(2)]
+
+    def run(two):
+        y = torch.empty((C * n, wl.d_model), dtype=torch.int16, device=x.device)
+        ids = torch.empty((C * n, wl.top_k), dtype=torch.int32, device=x.device)
+        w = torch.empty((C * n, wl.top_k), dtype=torch.float32, device=x.device)
+        torch.cuda.synchronize()
+        for j in range(n):
+            q = j % 2 if two else 0
+            tfa.tf_moe_prefill_chunk(D, x[C * j:C * (j + 1)], y=y[C * j:C * (j + 1)],
+                                     ids=ids[C * j:C * (j + 1)], weights=w[C * j:C * (j + 1)],
+                                     ws=ws[q], stream=streams[q])
+        torch.cuda.synchronize()
+        return y.cpu(), ids.cpu(), w.cpu()
+
+    one, two = run(False), run(True)
+    for a, b in zip(one, two):
+        assert torch.equal(a, b)

@@ -228,7 +228,10 @@ tf_status tf_moe_layer_fwd_noalloc(const tf_moe_layer *L, const uint16_t *x, int
  * before first use.  TF_E_ARG for T outside [0, 128] or a NULL pointer,
  * TF_E_ALIGN, TF_E_NOMEM for a short workspace, TF_E_SHAPE as in
  * tf_moe_layer_fwd; T == 0 enqueues nothing.  Same outputs as T single-token calls (ids bitwise,
- * y within fp32 rounding). */
+ * y within fp32 rounding).  The chunks of one layer are independent: calls
+ * on different streams, each with a workspace of its own, may run at once
+ * (two chunks in flight overlap one chunk's short router and combine
+ * launches with the other's GEMMs) and give bitwise the same results. */
 size_t tf_prefill_workspace_bytes(const tf_moe_layer *L, int32_t T);
 tf_status tf_moe_prefill_chunk(const tf_moe_layer *L, const uint16_t *x, int32_t T,
                                uint16_t *y, float *y32, int32_t *ids, float *weights,

@@ -110,6 +110,40 @@ def calibration(nbytes=256 << 20, reps=3):
     del a
 
 
+def same_size_stream(lib, nbytes, dev, n_buf=24, reps=10):
+    """What one launch of a plain read-only stream (the library's
+    k_stream_read: 16 bytes per lane, loads only) of `nbytes` reaches on this
+    GPU: graph-replayed back to back, every launch over a buffer of its own.
+    Context for a kernel's roofline fraction at the same launch size."""
+    import torch
+
+    from bit_routed_expert_tf_amd import _lib
+    n = nbytes // 16 * 16
+    bufs = [torch.ones(n // 4, dtype=torch.int32, device=dev) for _ in range(n_buf)]
+    stream = torch.cuda.Stream(device=dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for b in bufs:
+            _lib.check(lib.tf_profile_stream_read(ctypes.c_void_p(b.data_ptr()), n, sh))
+    with torch.cuda.stream(stream):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (n_buf * reps)
+    del g, bufs
+    return {"bytes": n, "us_per_launch": round(us, 3), "GBps": round(n / us / 1e3, 1),
+            "frac_of_peak": round(n / us / 1e3 / HBM_PEAK_GBPS, 4),
+            "kernel": "k_stream_read: read-only, 16 B per lane, graph-replayed, "
+                      f"{n_buf} buffers of its size in turn"}
+
+
 def _profile(lib, h, kernels, step, steps, stream):
     """Average durations of the named kernels over eager calls step(i) for i
     in `steps`: start/stop events attached to the launch (fence-free)."""
@@ -331,6 +365,10 @@ def run_stack(args):
         "device": torch.cuda.get_device_name(dev), "setup_s": round(setup, 1),
     }
     if not args.headline_only:
+        # context: a plain stream of the dominant kernel's bytes in one launch
+        st = same_size_stream(lib, out["roofline"]["algorithmic_bytes_per_launch"], dev)
+        st["kernel_over_stream"] = round(out["roofline"]["achieved"] / st["GBps"], 4)
+        out["roofline"]["same_size_stream"] = st
         out["batch16"] = run_stack_batch(args, wl, layers, 16, lib, dev, "k_gu")
         print(f"stack batch 16: {out['batch16']['tokens_per_s']} tokens/s", file=sys.stderr,
               flush=True)

@@ -49,7 +49,9 @@ def _decode_each(api, D, x16):
             torch.cat(ids).cpu().numpy())
 
 
-@pytest.mark.parametrize("T", [1, 2, 7, 33, 128])
+# 48 and 128: whole 16-token tiles, which the top-k launch walks in the
+# router launch's XCD order; 33: a ragged last tile (plain order)
+@pytest.mark.parametrize("T", [1, 2, 7, 33, 48, 128])
 def test_prefill_tiny_layer_matches_oracle(tfa, T):
     print(f"prefill tiny layer T={T}", flush=True)
     L = oracle_layer(0, 0, 256, 8, 2, 128, 256)
